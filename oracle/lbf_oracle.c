@@ -1,0 +1,375 @@
+/*
+ * lbf_oracle.c — CPU oracle for lossless byte-split BF16 weight coding.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The GPU library never
+ * links, calls or includes anything from this directory, and this file shares
+ * no code, header or table with it.  Everything here is plain, scalar,
+ * single-threaded C99 written to be checked against the method by eye.
+ *
+ * What the method computes (sources are the pages this project follows):
+ *  - "Lossless LLM Weight Compression vs 8-bit GGUF" (wavect.io, English),
+ *    section "What does 'lossless' mean for LLM weights?": the coded form must
+ *    rebuild every bit of the source BF16 tensor; decoding is a round trip.
+ *  - same page, section "What did the GLM-5.2 experiment actually prove?":
+ *    a BF16 weight splits into sign (1 bit), exponent (8) and mantissa (7);
+ *    since trained tensors concentrate on few exponent values, the frequent
+ *    ones are given fixed-width short codes and the infrequent ones are stored
+ *    verbatim in a separate escape stream.
+ *  - same page, opening section ("The short answer"): the byte-split
+ *    representation, rebuilt bit-for-bit; "K15" names a 15-symbol alphabet.
+ *  - "你的 bf16 模型,有 5 個 bit 是廢的" (meowlab), section 一: the field
+ *    table (sign 1, exponent 8, mantissa 7) and the order-0 entropy used as a
+ *    lower bound for any code that stores each weight independently.
+ *
+ * Readings taken where the pages are silent (each is listed in the design doc):
+ *  - only the 8-bit exponent is coded; sign and mantissa stay in one raw byte
+ *    (sign in bit 7, mantissa in bits 6..0);
+ *  - the alphabet is the 15 most frequent exponents (count descending, ties to
+ *    the smaller exponent); codes 0..n_codes-1 go to them in ascending
+ *    exponent order; code 15 means "escape";
+ *  - an escape stores the full 8-bit exponent as one byte, in flat element
+ *    order; tiles are 1024 consecutive weights and a uint32 prefix-sum index
+ *    idx[t] gives where tile t's escapes start (idx[n_t] = number of escapes);
+ *  - element i's code is nibble (i & 1) of nibble-plane byte i >> 1 (low
+ *    nibble for even i).
+ *
+ * Blob layout (format v1), all integers little-endian:
+ *   [0,256)             header (see put_header)
+ *   [off_raw, ...)      raw plane: n bytes, zero padded to n_t*1024
+ *   [off_nib, ...)      nibble plane: ceil(n/2) bytes, zero padded to n_t*512
+ *   [off_idx, ...)      idx plane: uint32[n_t + 1]
+ *   [off_esc, ...)      escape stream: n_esc bytes
+ * Every plane starts at a multiple of 256 and blob_bytes is a multiple of 256.
+ *
+ * The header's 96 meaningful bytes:
+ *   0 u32 magic 0x3146424C ("LBF1") | 4 u16 version 1 | 6 u16 tile_log2 10
+ *   8 u64 rows | 16 u64 cols | 24 u64 n_esc | 32 u64 off_raw | 40 u64 off_nib
+ *   48 u64 off_idx | 56 u64 off_esc | 64 u64 blob_bytes | 72 u8 lut[16]
+ *   88 u8 n_codes | 89..91 zero | 92 u32 CRC-32 of bytes [0,92); rest zero.
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <math.h>
+
+#define TILE 1024u
+#define HEADER 256u
+
+/* ---- small helpers --------------------------------------------------- */
+
+static uint64_t round_up_256(uint64_t v) { return (v + 255u) / 256u * 256u; }
+
+static void put_u16(uint8_t* p, uint16_t v) { p[0] = (uint8_t)v; p[1] = (uint8_t)(v >> 8); }
+static void put_u32(uint8_t* p, uint32_t v) { for (int i = 0; i < 4; i++) p[i] = (uint8_t)(v >> (8 * i)); }
+static void put_u64(uint8_t* p, uint64_t v) { for (int i = 0; i < 8; i++) p[i] = (uint8_t)(v >> (8 * i)); }
+static uint32_t get_u32(const uint8_t* p) {
+  uint32_t v = 0;
+  for (int i = 3; i >= 0; i--) v = (v << 8) | p[i];
+  return v;
+}
+static uint64_t get_u64(const uint8_t* p) {
+  uint64_t v = 0;
+  for (int i = 7; i >= 0; i--) v = (v << 8) | p[i];
+  return v;
+}
+
+/* CRC-32 (IEEE 802.3, reflected polynomial 0xEDB88320), bit by bit. */
+uint32_t lbfo_crc32(const uint8_t* data, uint64_t len) {
+  uint32_t crc = 0xFFFFFFFFu;
+  for (uint64_t i = 0; i < len; i++) {
+    crc ^= data[i];
+    for (int b = 0; b < 8; b++) crc = (crc & 1u) ? (crc >> 1) ^ 0xEDB88320u : crc >> 1;
+  }
+  return ~crc;
+}
+
+/* ---- the three BF16 fields (meowlab page, section 一, field table) ---- */
+
+static unsigned sign_of(uint16_t w) { return (w >> 15) & 1u; }
+static unsigned exponent_of(uint16_t w) { return (w >> 7) & 0xFFu; }
+static unsigned mantissa_of(uint16_t w) { return w & 0x7Fu; }
+
+/* ---- step 1: exponent histogram -------------------------------------- */
+
+void lbfo_histogram(const uint16_t* w, uint64_t n, uint64_t hist[256]) {
+  for (int e = 0; e < 256; e++) hist[e] = 0;
+  for (uint64_t i = 0; i < n; i++) hist[exponent_of(w[i])]++;
+}
+
+/* ---- step 2: the code table (frequent exponents get 4-bit codes) ------
+ * Pick up to 15 exponents: repeatedly take the most frequent exponent not yet
+ * taken; a tie goes to the smaller exponent (the scan runs upward and only a
+ * strictly larger count replaces the current best).  Exponents that never
+ * occur are never taken.  Codes are then handed out in ascending exponent
+ * order.  Unused table slots, and slot 15 (escape), hold 0.
+ */
+void lbfo_code_table(const uint64_t hist[256], uint8_t lut[16], uint8_t* n_codes) {
+  int taken[256] = {0};
+  int chosen = 0;
+  for (int round = 0; round < 15; round++) {
+    int best = -1;
+    for (int e = 0; e < 256; e++) {
+      if (taken[e] || hist[e] == 0) continue;
+      if (best < 0 || hist[e] > hist[best]) best = e;
+    }
+    if (best < 0) break;
+    taken[best] = 1;
+    chosen++;
+  }
+  for (int c = 0; c < 16; c++) lut[c] = 0;
+  int c = 0;
+  for (int e = 0; e < 256; e++)
+    if (taken[e]) lut[c++] = (uint8_t)e;
+  *n_codes = (uint8_t)chosen;
+}
+
+/* the code an exponent gets: its slot in the table, or 15 (escape) */
+static unsigned code_of(unsigned e, const uint8_t lut[16], unsigned n_codes) {
+  for (unsigned c = 0; c < n_codes; c++)
+    if (lut[c] == e) return c;
+  return 15u;
+}
+
+/* ---- sizes ----------------------------------------------------------- */
+
+typedef struct {
+  uint64_t n, n_tiles, n_esc;
+  uint64_t off_raw, off_nib, off_idx, off_esc, blob_bytes;
+} layout_t;
+
+static layout_t layout_for(uint64_t rows, uint64_t cols, uint64_t n_esc) {
+  layout_t L;
+  L.n = rows * cols;
+  L.n_tiles = (L.n + TILE - 1) / TILE;
+  L.n_esc = n_esc;
+  L.off_raw = HEADER;
+  L.off_nib = round_up_256(L.off_raw + L.n_tiles * TILE);
+  L.off_idx = round_up_256(L.off_nib + L.n_tiles * (TILE / 2));
+  L.off_esc = round_up_256(L.off_idx + 4u * (L.n_tiles + 1));
+  L.blob_bytes = round_up_256(L.off_esc + n_esc);
+  return L;
+}
+
+/* Escape count: weights whose exponent did not get a code. */
+static uint64_t escape_count(const uint64_t hist[256], const uint8_t lut[16], unsigned n_codes) {
+  uint64_t n = 0;
+  for (int e = 0; e < 256; e++)
+    if (code_of((unsigned)e, lut, n_codes) == 15u) n += hist[e];
+  return n;
+}
+
+/* Everything the encoder decides before writing: table, escape count, size. */
+int lbfo_plan(const uint16_t* w, uint64_t rows, uint64_t cols, uint8_t lut[16], uint8_t* n_codes,
+              uint64_t* n_esc, uint64_t* blob_bytes) {
+  uint64_t hist[256];
+  if (cols != 0 && rows > UINT64_MAX / cols) return -1;
+  uint64_t n = rows * cols;
+  if (n >= (1ull << 32)) return -1; /* uint32 escape index */
+  lbfo_histogram(w, n, hist);
+  lbfo_code_table(hist, lut, n_codes);
+  *n_esc = escape_count(hist, lut, *n_codes);
+  *blob_bytes = layout_for(rows, cols, *n_esc).blob_bytes;
+  return 0;
+}
+
+/* ---- step 3: write the blob ------------------------------------------ */
+
+static void put_header(uint8_t* blob, uint64_t rows, uint64_t cols, const layout_t* L,
+                       const uint8_t lut[16], uint8_t n_codes) {
+  memset(blob, 0, HEADER);
+  put_u32(blob + 0, 0x3146424Cu);
+  put_u16(blob + 4, 1);
+  put_u16(blob + 6, 10);
+  put_u64(blob + 8, rows);
+  put_u64(blob + 16, cols);
+  put_u64(blob + 24, L->n_esc);
+  put_u64(blob + 32, L->off_raw);
+  put_u64(blob + 40, L->off_nib);
+  put_u64(blob + 48, L->off_idx);
+  put_u64(blob + 56, L->off_esc);
+  put_u64(blob + 64, L->blob_bytes);
+  memcpy(blob + 72, lut, 16);
+  blob[88] = n_codes;
+  put_u32(blob + 92, lbfo_crc32(blob, 92));
+}
+
+int lbfo_encode(const uint16_t* w, uint64_t rows, uint64_t cols, uint8_t* blob, uint64_t blob_cap) {
+  uint8_t lut[16], n_codes;
+  uint64_t n_esc, blob_bytes;
+  if (lbfo_plan(w, rows, cols, lut, &n_codes, &n_esc, &blob_bytes) != 0) return -1;
+  if (blob_cap < blob_bytes) return -2;
+  layout_t L = layout_for(rows, cols, n_esc);
+  memset(blob, 0, blob_bytes);
+  put_header(blob, rows, cols, &L, lut, n_codes);
+
+  uint8_t* raw = blob + L.off_raw;
+  uint8_t* nib = blob + L.off_nib;
+  uint8_t* idx = blob + L.off_idx;
+  uint8_t* esc = blob + L.off_esc;
+  uint64_t* tile_escapes = (uint64_t*)calloc(L.n_tiles + 1, sizeof(uint64_t));
+  if (!tile_escapes) return -3;
+
+  uint64_t written = 0;
+  for (uint64_t i = 0; i < L.n; i++) {
+    unsigned s = sign_of(w[i]), e = exponent_of(w[i]), m = mantissa_of(w[i]);
+    raw[i] = (uint8_t)((s << 7) | m);
+    unsigned code = code_of(e, lut, n_codes);
+    nib[i >> 1] |= (uint8_t)(code << (4u * (unsigned)(i & 1u)));
+    if (code == 15u) {
+      esc[written++] = (uint8_t)e; /* flat element order */
+      tile_escapes[i / TILE]++;
+    }
+  }
+  /* prefix-sum index: idx[0] = 0, idx[t+1] = idx[t] + escapes in tile t */
+  uint64_t run = 0;
+  put_u32(idx, 0);
+  for (uint64_t t = 0; t < L.n_tiles; t++) {
+    run += tile_escapes[t];
+    put_u32(idx + 4u * (t + 1), (uint32_t)run);
+  }
+  free(tile_escapes);
+  return (written == n_esc && run == n_esc) ? 0 : -4;
+}
+
+/* ---- header reading (used by decode) ---------------------------------- */
+
+int lbfo_read_header(const uint8_t* blob, uint64_t blob_len, uint64_t* rows, uint64_t* cols,
+                     uint64_t* n_esc, uint8_t lut[16], uint8_t* n_codes) {
+  if (blob_len < HEADER) return -1;
+  if (get_u32(blob) != 0x3146424Cu) return -1;
+  if (blob[4] != 1 || blob[5] != 0 || blob[6] != 10 || blob[7] != 0) return -1;
+  if (get_u32(blob + 92) != lbfo_crc32(blob, 92)) return -1;
+  *rows = get_u64(blob + 8);
+  *cols = get_u64(blob + 16);
+  *n_esc = get_u64(blob + 24);
+  memcpy(lut, blob + 72, 16);
+  *n_codes = blob[88];
+  if (*n_codes > 15) return -1;
+  if (*cols != 0 && *rows > UINT64_MAX / *cols) return -1;
+  if (*rows * *cols >= (1ull << 32)) return -1;
+  layout_t L = layout_for(*rows, *cols, *n_esc);
+  if (get_u64(blob + 32) != L.off_raw || get_u64(blob + 40) != L.off_nib ||
+      get_u64(blob + 48) != L.off_idx || get_u64(blob + 56) != L.off_esc ||
+      get_u64(blob + 64) != L.blob_bytes || blob_len < L.blob_bytes)
+    return -1;
+  return 0;
+}
+
+/* ---- decode: rebuild each weight from its raw byte and its exponent ---- */
+
+int lbfo_decode(const uint8_t* blob, uint64_t blob_len, uint16_t* out, uint64_t out_len) {
+  uint64_t rows, cols, n_esc;
+  uint8_t lut[16], n_codes;
+  if (lbfo_read_header(blob, blob_len, &rows, &cols, &n_esc, lut, &n_codes) != 0) return -1;
+  layout_t L = layout_for(rows, cols, n_esc);
+  if (out_len < L.n) return -2;
+  const uint8_t* raw = blob + L.off_raw;
+  const uint8_t* nib = blob + L.off_nib;
+  const uint8_t* idx = blob + L.off_idx;
+  const uint8_t* esc = blob + L.off_esc;
+  if (get_u32(idx) != 0 || get_u32(idx + 4u * L.n_tiles) != n_esc) return -3;
+
+  for (uint64_t t = 0; t < L.n_tiles; t++) {
+    uint64_t first = get_u32(idx + 4u * t), last = get_u32(idx + 4u * (t + 1));
+    if (last < first || last > n_esc) return -3;
+    uint64_t seen = 0; /* escapes met so far inside this tile */
+    uint64_t end = (t + 1) * TILE < L.n ? (t + 1) * TILE : L.n;
+    for (uint64_t i = t * TILE; i < end; i++) {
+      unsigned code = (nib[i >> 1] >> (4u * (unsigned)(i & 1u))) & 15u;
+      unsigned e;
+      if (code == 15u) {
+        if (first + seen >= last) return -3;
+        e = esc[first + seen];
+        seen++;
+      } else {
+        if (code >= n_codes) return -3;
+        e = lut[code];
+      }
+      unsigned s = raw[i] >> 7, m = raw[i] & 0x7Fu;
+      out[i] = (uint16_t)((s << 15) | (e << 7) | m);
+    }
+    if (first + seen != last) return -3;
+  }
+  return 0;
+}
+
+/* ---- y = W x in float64 ------------------------------------------------
+ * y[b*rows + r] = sum_k W[r,k] * x[b,k], summed in k order in double;
+ * a[b*rows + r] = sum_k |W[r,k]| * |x[b,k]|, the scale the error bound uses.
+ * W is row-major [rows x cols]; x is row-major [batch x cols]; both bf16.
+ */
+static double bf16_to_double(uint16_t v) {
+  uint32_t bits = (uint32_t)v << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+void lbfo_matvec(const uint16_t* W, uint64_t rows, uint64_t cols, const uint16_t* x, uint64_t batch,
+                 double* y, double* a) {
+  for (uint64_t b = 0; b < batch; b++) {
+    for (uint64_t r = 0; r < rows; r++) {
+      double sum = 0.0, mag = 0.0;
+      for (uint64_t k = 0; k < cols; k++) {
+        double wv = bf16_to_double(W[r * cols + k]);
+        double xv = bf16_to_double(x[b * cols + k]);
+        sum += wv * xv;
+        mag += fabs(wv) * fabs(xv);
+      }
+      y[b * rows + r] = sum;
+      if (a) a[b * rows + r] = mag;
+    }
+  }
+}
+
+/* Same product, rows [r0, r1) only (lets a caller sample rows of a big W). */
+void lbfo_matvec_rows(const uint16_t* W, uint64_t rows, uint64_t cols, uint64_t r0, uint64_t r1,
+                      const uint16_t* x, uint64_t batch, double* y, double* a) {
+  for (uint64_t b = 0; b < batch; b++) {
+    for (uint64_t r = r0; r < r1 && r < rows; r++) {
+      double sum = 0.0, mag = 0.0;
+      for (uint64_t k = 0; k < cols; k++) {
+        double wv = bf16_to_double(W[r * cols + k]);
+        double xv = bf16_to_double(x[b * cols + k]);
+        sum += wv * xv;
+        mag += fabs(wv) * fabs(xv);
+      }
+      y[b * (r1 - r0) + (r - r0)] = sum;
+      if (a) a[b * (r1 - r0) + (r - r0)] = mag;
+    }
+  }
+}
+
+/* ---- order-0 entropy of the 16-bit values, in bits per weight ----------
+ * (meowlab page, section 二: the lower bound for any code that stores each
+ * weight on its own)  H0 = -sum_v p_v log2 p_v over the 65,536 patterns.
+ */
+double lbfo_entropy16(const uint16_t* w, uint64_t n) {
+  if (n == 0) return 0.0;
+  uint64_t* count = (uint64_t*)calloc(65536, sizeof(uint64_t));
+  if (!count) return -1.0;
+  for (uint64_t i = 0; i < n; i++) count[w[i]]++;
+  double h = 0.0;
+  for (int v = 0; v < 65536; v++) {
+    if (count[v] == 0) continue;
+    double p = (double)count[v] / (double)n;
+    h -= p * log2(p);
+  }
+  free(count);
+  return h;
+}
+
+/* Order-0 entropy of the exponent field alone (same page, section 一 table). */
+double lbfo_entropy_exponent(const uint16_t* w, uint64_t n) {
+  if (n == 0) return 0.0;
+  uint64_t hist[256];
+  lbfo_histogram(w, n, hist);
+  double h = 0.0;
+  for (int e = 0; e < 256; e++) {
+    if (hist[e] == 0) continue;
+    double p = (double)hist[e] / (double)n;
+    h -= p * log2(p);
+  }
+  return h;
+}
