@@ -1,0 +1,257 @@
+// lbf_api.cpp — the C ABI of liblbf.so: argument and descriptor checks, the
+// host part of encoding (choice of the 15 coded exponents), and dispatch to
+// the gfx950 kernels.  Declarations and conventions: include/lbf.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstddef>
+#include <cstring>
+#include <vector>
+
+#include "lbf.h"
+#include "lbf_internal.h"
+
+static_assert(sizeof(lbf_desc) == 96, "descriptor must be 96 bytes");
+static_assert(offsetof(lbf_desc, lut) == 72, "descriptor layout");
+static_assert(offsetof(lbf_desc, n_codes) == 88, "descriptor layout");
+static_assert(offsetof(lbf_desc, desc_crc) == 92, "descriptor layout");
+
+namespace lbf {
+
+Layout layout_of(uint64_t rows, uint64_t cols, uint64_t n_esc) {
+  auto up = [](uint64_t v) { return (v + 255) & ~uint64_t(255); };
+  Layout L;
+  L.n = rows * cols;
+  L.n_tiles = (L.n + LBF_TILE - 1) / LBF_TILE;
+  L.n_esc = n_esc;
+  L.off_raw = LBF_HEADER_BYTES;
+  L.off_nib = up(L.off_raw + L.n_tiles * LBF_TILE);
+  L.off_idx = up(L.off_nib + L.n_tiles * (LBF_TILE / 2));
+  L.off_esc = up(L.off_idx + 4 * (L.n_tiles + 1));
+  L.blob_bytes = up(L.off_esc + n_esc);
+  return L;
+}
+
+// CRC-32 (IEEE 802.3), table driven.
+uint32_t crc32(const void* data, size_t len) {
+  static uint32_t table[256];
+  static bool ready = false;  // benign race: every writer stores the same table
+  if (!ready) {
+    for (uint32_t i = 0; i < 256; i++) {
+      uint32_t c = i;
+      for (int k = 0; k < 8; k++) c = (c >> 1) ^ (0xEDB88320u & (0u - (c & 1u)));
+      table[i] = c;
+    }
+    ready = true;
+  }
+  const uint8_t* p = static_cast<const uint8_t*>(data);
+  uint32_t c = 0xFFFFFFFFu;
+  for (size_t i = 0; i < len; i++) c = table[(c ^ p[i]) & 0xFFu] ^ (c >> 8);
+  return c ^ 0xFFFFFFFFu;
+}
+
+KLut klut_of(const lbf_desc& d) {
+  KLut k;
+  for (int q = 0; q < 4; q++)
+    k.t[q] = d.lut[4 * q] | (d.lut[4 * q + 1] << 8) | (d.lut[4 * q + 2] << 16) | ((uint32_t)d.lut[4 * q + 3] << 24);
+  k.base4 = d.lut[0] * 0x01010101u;
+  k.contiguous = d.n_codes > 0;
+  for (int c = 0; c < d.n_codes; c++)
+    if (d.lut[c] != d.lut[0] + c) k.contiguous = 0;
+  // codes >= n_codes never occur, so lut[0] + c only has to be right below n_codes;
+  // the byte-wise add must not carry: lut[0] + 15 <= 255
+  if (d.lut[0] > 240) k.contiguous = 0;
+  return k;
+}
+
+static bool shape_ok(uint64_t rows, uint64_t cols) {
+  if (cols != 0 && rows > UINT64_MAX / cols) return false;
+  return rows * cols < (uint64_t(1) << 32);
+}
+
+static int check(const lbf_desc* d) {
+  if (!d) return LBF_E_INVAL;
+  if (d->magic != LBF_MAGIC || d->version != LBF_VERSION || d->tile_log2 != LBF_TILE_LOG2) return LBF_E_DESC;
+  if (crc32(d, offsetof(lbf_desc, desc_crc)) != d->desc_crc) return LBF_E_DESC;
+  if (!shape_ok(d->rows, d->cols)) return LBF_E_DESC;
+  const Layout L = layout_of(d->rows, d->cols, d->n_esc);
+  if (d->n_esc > L.n) return LBF_E_DESC;
+  if (d->off_raw != L.off_raw || d->off_nib != L.off_nib || d->off_idx != L.off_idx || d->off_esc != L.off_esc ||
+      d->blob_bytes != L.blob_bytes)
+    return LBF_E_DESC;
+  if (d->n_codes > 15) return LBF_E_DESC;
+  for (int c = 1; c < d->n_codes; c++)
+    if (d->lut[c] <= d->lut[c - 1]) return LBF_E_DESC;
+  for (int c = d->n_codes; c < 16; c++)
+    if (d->lut[c] != 0) return LBF_E_DESC;
+  if (d->reserved[0] | d->reserved[1] | d->reserved[2]) return LBF_E_DESC;
+  // fewer than 15 coded exponents means every exponent present got a code
+  if (d->n_codes < 15 && d->n_esc != 0) return LBF_E_DESC;
+  if (L.n > 0 && d->n_codes == 0) return LBF_E_DESC;
+  return LBF_OK;
+}
+
+static bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Choose the coded exponents from the histogram: sort by count descending,
+// ties to the smaller exponent, keep the first 15 present ones, then hand
+// codes out in ascending exponent order.
+static void fill_desc(const uint32_t hist[256], uint64_t rows, uint64_t cols, lbf_desc* d) {
+  std::vector<int> order;
+  for (int e = 0; e < 256; e++)
+    if (hist[e]) order.push_back(e);
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return hist[a] > hist[b]; });
+  if (order.size() > 15) order.resize(15);
+  std::sort(order.begin(), order.end());
+  uint64_t coded = 0;
+  for (int e : order) coded += hist[e];
+
+  std::memset(d, 0, sizeof(*d));
+  d->magic = LBF_MAGIC;
+  d->version = LBF_VERSION;
+  d->tile_log2 = LBF_TILE_LOG2;
+  d->rows = rows;
+  d->cols = cols;
+  d->n_esc = rows * cols - coded;
+  const Layout L = layout_of(rows, cols, d->n_esc);
+  d->off_raw = L.off_raw;
+  d->off_nib = L.off_nib;
+  d->off_idx = L.off_idx;
+  d->off_esc = L.off_esc;
+  d->blob_bytes = L.blob_bytes;
+  for (size_t c = 0; c < order.size(); c++) d->lut[c] = (uint8_t)order[c];
+  d->n_codes = (uint8_t)order.size();
+  d->desc_crc = crc32(d, offsetof(lbf_desc, desc_crc));
+}
+
+// Per-group kernel records for the product calls; checks every group.
+static int build_groups(const lbf_desc* descs, const void* const* d_blobs, int n_groups, const void* const* d_x,
+                        void* const* d_y, std::vector<GemvGroup>& out) {
+  if (!descs || !d_blobs || !d_x || !d_y || n_groups < 1) return LBF_E_INVAL;
+  out.resize((size_t)n_groups);
+  for (int g = 0; g < n_groups; g++) {
+    const lbf_desc& d = descs[g];
+    const int rc = check(&d);
+    if (rc) return rc;
+    if (!d_blobs[g] || !d_x[g] || !d_y[g]) return LBF_E_INVAL;
+    if (!aligned(d_blobs[g], 256) || !aligned(d_x[g], 16) || !aligned(d_y[g], 4)) return LBF_E_ALIGN;
+    if (d.rows == 0 || d.cols == 0 || d.cols % LBF_TILE != 0) return LBF_E_SHAPE;
+    const KLut k = klut_of(d);
+    GemvGroup& G = out[(size_t)g];
+    G.blob = static_cast<const uint8_t*>(d_blobs[g]);
+    G.x = static_cast<const uint16_t*>(d_x[g]);
+    G.y = d_y[g];
+    G.rows = (uint32_t)d.rows;
+    G.cols = (uint32_t)d.cols;
+    G.n_esc = (uint32_t)d.n_esc;
+    G.unit_begin = 0;
+    for (int q = 0; q < 4; q++) G.lut[q] = k.t[q];
+    G.base4 = k.base4;
+    G.flags = k.contiguous ? 1u : 0u;
+  }
+  return LBF_OK;
+}
+
+}  // namespace lbf
+
+using namespace lbf;
+
+extern "C" {
+
+const char* lbf_strerror(int status) {
+  switch (status) {
+    case LBF_OK: return "ok";
+    case LBF_E_INVAL: return "invalid argument";
+    case LBF_E_SHAPE: return "unsupported or mismatched shape";
+    case LBF_E_ALIGN: return "misaligned device pointer";
+    case LBF_E_DESC: return "descriptor failed validation";
+    case LBF_E_CAPACITY: return "buffer too small";
+    case LBF_E_HIP: return "HIP runtime error";
+    case LBF_E_UNSUPPORTED: return "unsupported request";
+    default: return "unknown status";
+  }
+}
+
+uint64_t lbf_encode_work_bytes(uint64_t rows, uint64_t cols) {
+  if (!shape_ok(rows, cols)) return 0;
+  const Layout L = layout_of(rows, cols, 0);
+  return kWorkHistBytes + ((4 * L.n_tiles + 255) & ~uint64_t(255));
+}
+
+int lbf_desc_check(const lbf_desc* desc) { return check(desc); }
+
+int lbf_encode(const void* d_w, uint64_t rows, uint64_t cols, void* d_work, uint64_t work_bytes, void* d_blob,
+               uint64_t blob_cap, lbf_desc* desc, hipStream_t s) {
+  if (!desc || !d_work) return LBF_E_INVAL;
+  if (!shape_ok(rows, cols)) return LBF_E_SHAPE;
+  const uint64_t n = rows * cols;
+  if (n && !d_w) return LBF_E_INVAL;
+  if (!aligned(d_w, 16) || !aligned(d_work, 256)) return LBF_E_ALIGN;
+  if (work_bytes < lbf_encode_work_bytes(rows, cols)) return LBF_E_CAPACITY;
+  uint32_t* hist = static_cast<uint32_t*>(d_work);
+  uint32_t* tile_cnt = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(d_work) + kWorkHistBytes);
+  if (!d_blob) {  // phase 1
+    uint32_t h[256];
+    if (n) {
+      if (launch_hist(static_cast<const uint16_t*>(d_w), n, hist, s) != hipSuccess) return LBF_E_HIP;
+      if (hipMemcpyAsync(h, hist, sizeof h, hipMemcpyDeviceToHost, s) != hipSuccess) return LBF_E_HIP;
+      if (hipStreamSynchronize(s) != hipSuccess) return LBF_E_HIP;
+    } else {
+      std::memset(h, 0, sizeof h);
+    }
+    uint64_t total = 0;
+    for (int e = 0; e < 256; e++) total += h[e];
+    if (total != n) return LBF_E_HIP;  // the histogram must account for every weight
+    fill_desc(h, rows, cols, desc);
+    return LBF_OK;
+  }
+  // phase 2
+  const int rc = check(desc);
+  if (rc) return rc;
+  if (desc->rows != rows || desc->cols != cols) return LBF_E_SHAPE;
+  if (!aligned(d_blob, 256)) return LBF_E_ALIGN;
+  if (blob_cap < desc->blob_bytes) return LBF_E_CAPACITY;
+  if (launch_pack(static_cast<const uint16_t*>(d_w), *desc, static_cast<uint8_t*>(d_blob), tile_cnt, s) != hipSuccess)
+    return LBF_E_HIP;
+  return LBF_OK;
+}
+
+int lbf_decode(const lbf_desc* desc, const void* d_blob, void* d_w_out, hipStream_t s) {
+  const int rc = check(desc);
+  if (rc) return rc;
+  const uint64_t n = desc->rows * desc->cols;
+  if (n == 0) return LBF_OK;
+  if (!d_blob || !d_w_out) return LBF_E_INVAL;
+  if (!aligned(d_blob, 256) || !aligned(d_w_out, 16)) return LBF_E_ALIGN;
+  if (launch_decode(*desc, static_cast<const uint8_t*>(d_blob), static_cast<uint16_t*>(d_w_out), s) != hipSuccess)
+    return LBF_E_HIP;
+  return LBF_OK;
+}
+
+static int product(bool mfma, const lbf_desc* descs, const void* const* d_blobs, int n_groups,
+                   const void* const* d_x, int batch, void* const* d_y, int y_dtype, hipStream_t s) {
+  if (y_dtype != LBF_F32 && y_dtype != LBF_BF16) return LBF_E_INVAL;
+  if (mfma ? (batch < 9 || batch > 256) : (batch < 1 || batch > 8)) return LBF_E_INVAL;
+  std::vector<GemvGroup> groups;
+  const int rc = build_groups(descs, d_blobs, n_groups, d_x, d_y, groups);
+  if (rc) return rc;
+  for (int g0 = 0; g0 < n_groups; g0 += LBF_MAX_GROUPS) {
+    const int cnt = std::min(LBF_MAX_GROUPS, n_groups - g0);
+    const hipError_t e = mfma ? launch_gemm(groups.data() + g0, cnt, batch, y_dtype, s)
+                              : launch_gemv(groups.data() + g0, cnt, batch, y_dtype, s);
+    if (e != hipSuccess) return LBF_E_HIP;
+  }
+  return LBF_OK;
+}
+
+int lbf_gemv(const lbf_desc* descs, const void* const* d_blobs, int n_groups, const void* const* d_x, int batch,
+             void* const* d_y, int y_dtype, hipStream_t s) {
+  return product(false, descs, d_blobs, n_groups, d_x, batch, d_y, y_dtype, s);
+}
+
+int lbf_gemm(const lbf_desc* descs, const void* const* d_blobs, int n_groups, const void* const* d_x, int batch,
+             void* const* d_y, int y_dtype, hipStream_t s) {
+  return product(true, descs, d_blobs, n_groups, d_x, batch, d_y, y_dtype, s);
+}
+
+}  // extern "C"

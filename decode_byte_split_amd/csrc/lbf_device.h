@@ -1,0 +1,170 @@
+// lbf_device.h — device-side building blocks shared by the gfx950 kernels:
+// nibble-code expansion, exponent lookup, BF16 reassembly, escape placement
+// and wave-level integer prefix sums.
+//
+// Format (see include/lbf.h): per weight one raw byte (sign << 7 | mantissa)
+// and one 4-bit code; code c < 15 stands for exponent lut[c], code 15 takes
+// the next byte of the tile's escape slice.  The pages this follows:
+// "Lossless LLM Weight Compression vs 8-bit GGUF" (wavect.io), sections
+// "What does 'lossless' mean for LLM weights?" (exact rebuild in registers
+// right before the multiply) and "What did the GLM-5.2 experiment actually
+// prove?" (fixed short codes for frequent exponents, exact escape stream).
+//
+// Lane work unit: 16 consecutive weights of a 1024-weight tile, i.e. one
+// 16-byte raw load (4 words, 4 weights each) and one 8-byte nibble load
+// (2 words, 8 codes each).  Decoded weights leave as 8 packed bf16 pairs,
+// pair j = weights (2j, 2j+1), low half first: the operand layout of
+// v_dot2_f32_bf16 and of memory.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lbf {
+
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+constexpr int kTile = 1024;
+constexpr int kWave = 64;
+
+// Code table as four little-endian words: t[q] bytes = lut[4q .. 4q+3].
+struct Lut {
+  uint32_t t0, t1, t2, t3;
+};
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// Four code bytes (each 0..15) -> four exponent bytes, lut[c] per byte.
+// v_perm_b32 looks bytes up in an 8-byte table; codes 0..7 use lut[0..7],
+// codes 8..15 use lut[8..15] with the selector's bit 3 cleared, and a
+// per-byte mask built from bit 3 (selector 4 -> 0xFF byte, 12 -> 0x00)
+// picks between the two lookups.
+__device__ __forceinline__ uint32_t lut_lookup(uint32_t c, const Lut& L) {
+  uint32_t c7 = c & 0x07070707u;
+  uint32_t lo = perm(L.t1, L.t0, c7);
+  uint32_t hi = perm(L.t3, L.t2, c7);
+  uint32_t sel = (c & 0x08080808u) | 0x04040404u;
+  uint32_t keep_lo = perm(0xFFFFFFFFu, 0u, sel);
+  return (lo & keep_lo) | (hi & ~keep_lo);
+}
+
+// Exponent bytes of a lane's 16 weights from its two nibble words.
+//   E[0] = weights 0,2,4,6   E[1] = weights 1,3,5,7
+//   E[2] = weights 8,...,14  E[3] = weights 9,...,15   (byte j = j-th of them)
+// CONTIG: the table is lut[c] = lut[0] + c (the common case for trained
+// weights), so a byte-wise add replaces the lookup; `base4` = lut[0] * 0x01010101.
+template <bool CONTIG>
+__device__ __forceinline__ void exponents16(u32x2 nib, const Lut& L, uint32_t base4, uint32_t E[4]) {
+  uint32_t c[4];
+  c[0] = nib.x & 0x0F0F0F0Fu;
+  c[1] = (nib.x >> 4) & 0x0F0F0F0Fu;
+  c[2] = nib.y & 0x0F0F0F0Fu;
+  c[3] = (nib.y >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+  for (int q = 0; q < 4; q++) E[q] = CONTIG ? c[q] + base4 : lut_lookup(c[q], L);
+}
+
+// Rebuild 8 bf16 pairs: w = (sign << 15) | (exponent << 7) | mantissa.
+// The raw byte is duplicated into both bytes of its 16-bit half, masked to
+// keep bit 15 (sign) and bits 6..0 (mantissa); the exponent bytes are moved
+// to bits 7..14 of each half.
+__device__ __forceinline__ void assemble16(u32x4 raw, const uint32_t E[4], uint32_t w[8]) {
+  const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    const int g = j >> 2, jj = j & 3;
+    uint32_t f = perm(E[2 * g + 1], E[2 * g], 0x0C000C00u | (uint32_t)jj | ((uint32_t)(4 + jj) << 16)) << 7;
+    const uint32_t b = (uint32_t)(j & 1) * 2u;
+    uint32_t r = perm(rw[j >> 1], rw[j >> 1], b | (b << 8) | ((b + 1) << 16) | ((b + 1) << 24));
+    w[j] = (r & 0x807F807Fu) | f;
+  }
+}
+
+// Bit 4i set iff nibble i of `n` is 15 (the escape code).
+__device__ __forceinline__ uint32_t escape_bits(uint32_t n) {
+  uint32_t t = n & (n >> 2);
+  return t & (t >> 1) & 0x11111111u;
+}
+
+__device__ __forceinline__ int lane_id() { return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+// Number of set bits of a wave-wide ballot in lanes below this one.
+__device__ __forceinline__ uint32_t ballot_rank(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Exclusive prefix sum over the wave of v (0 <= v < 32), bit by bit:
+// sum_b 2^b * #{lower lanes with bit b of v set}.
+__device__ __forceinline__ uint32_t wave_excl_scan_small(uint32_t v) {
+  uint32_t r = 0;
+#pragma unroll
+  for (int b = 0; b < 5; b++) r += ballot_rank(__builtin_amdgcn_ballot_w64(((v >> b) & 1u) != 0)) << b;
+  return r;
+}
+
+// Overwrite the exponent byte of weight i (0..15) in the E[] layout above.
+__device__ __forceinline__ void patch_exponent(uint32_t E[4], uint32_t i, uint32_t e) {
+  const uint32_t word = ((i >> 3) << 1) | (i & 1u);
+  const uint32_t sh = ((i & 7u) >> 1) * 8u;
+  const uint32_t m = 0xFFu << sh, v = e << sh;
+#pragma unroll
+  for (uint32_t q = 0; q < 4; q++) E[q] = (word == q) ? ((E[q] & ~m) | v) : E[q];
+}
+
+// Escape placement for one tile held by one wave (called by all 64 lanes,
+// only when the tile has escapes).  The tile's escape slice
+// esc[first, first + cnt) is staged in this wave's LDS slot (one byte per
+// escape, cnt <= 1024), each lane finds how many escapes lie in lower lanes
+// (wave prefix sum of per-lane counts), and patches its exponent bytes in
+// element order.  Reads beyond cnt (only possible on a corrupt blob) yield 0.
+__device__ __forceinline__ void place_escapes(u32x2 nib, const uint8_t* __restrict__ esc, uint32_t first,
+                                              uint32_t cnt, uint8_t* lds_slot, uint32_t E[4]) {
+  const int lane = lane_id();
+  for (uint32_t p = (uint32_t)lane; p < cnt; p += kWave) lds_slot[p] = esc[first + p];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  uint32_t m0 = escape_bits(nib.x), m1 = escape_bits(nib.y);
+  uint32_t k = (uint32_t)(__builtin_popcount(m0) + __builtin_popcount(m1));
+  uint32_t j = wave_excl_scan_small(k);
+  while (m0) {
+    const uint32_t i = (uint32_t)__builtin_ctz(m0) >> 2;
+    const uint32_t e = j < cnt ? lds_slot[j] : 0u;
+    patch_exponent(E, i, e);
+    m0 &= m0 - 1;
+    j++;
+  }
+  while (m1) {
+    const uint32_t i = 8u + ((uint32_t)__builtin_ctz(m1) >> 2);
+    const uint32_t e = j < cnt ? lds_slot[j] : 0u;
+    patch_exponent(E, i, e);
+    m1 &= m1 - 1;
+    j++;
+  }
+  // the slot is reused by the next tile: finish reading before anyone rewrites it
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Escape range of tile t from the index plane, clamped so that a corrupt
+// index can neither read past the escape stream nor overflow an LDS slot.
+__device__ __forceinline__ void tile_escape_range(const uint32_t* __restrict__ idx, uint32_t t, uint32_t n_esc,
+                                                  uint32_t& first, uint32_t& cnt) {
+  uint32_t a = idx[t], b = idx[t + 1];
+  if (b > n_esc) b = n_esc;
+  if (a > b) a = b;
+  first = a;
+  cnt = b - a;
+  if (cnt > (uint32_t)kTile) cnt = kTile;
+}
+
+__device__ __forceinline__ u32x4 load_nt(const u32x4* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ u32x2 load_nt(const u32x2* p) { return __builtin_nontemporal_load(p); }
+
+__device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+}  // namespace lbf

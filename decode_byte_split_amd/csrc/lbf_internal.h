@@ -1,0 +1,52 @@
+// lbf_internal.h — host-side declarations shared by the library's sources.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include "lbf.h"
+
+namespace lbf {
+
+// Byte layout of a format-v1 blob for a [rows, cols] tensor with n_esc escapes.
+struct Layout {
+  uint64_t n, n_tiles, n_esc;
+  uint64_t off_raw, off_nib, off_idx, off_esc, blob_bytes;
+};
+Layout layout_of(uint64_t rows, uint64_t cols, uint64_t n_esc);
+
+uint32_t crc32(const void* data, size_t len);
+
+// Code table as handed to kernels.
+struct KLut {
+  uint32_t t[4];   // lut bytes, little-endian words
+  uint32_t base4;  // lut[0] * 0x01010101
+  int contiguous;  // lut[c] == lut[0] + c for every c < n_codes
+};
+KLut klut_of(const lbf_desc& d);
+
+// Launchers (defined next to their kernels).  All enqueue on `s` and return
+// the launch status.
+hipError_t launch_decode(const lbf_desc& d, const uint8_t* blob, uint16_t* out, hipStream_t s);
+
+hipError_t launch_hist(const uint16_t* w, uint64_t n, uint32_t* hist, hipStream_t s);
+hipError_t launch_pack(const uint16_t* w, const lbf_desc& d, uint8_t* blob, uint32_t* tile_cnt, hipStream_t s);
+
+struct GemvGroup {
+  const uint8_t* blob;
+  const uint16_t* x;
+  void* y;
+  uint32_t rows, cols, n_esc;
+  uint32_t unit_begin;  // first work unit of this group
+  uint32_t lut[4];
+  uint32_t base4;
+  uint32_t flags;  // bit 0: contiguous table
+  uint32_t geom;   // filled by the launcher: rows per unit | slices << 16 | row phases << 20
+  uint32_t pad;
+};
+hipError_t launch_gemv(const GemvGroup* groups, int n_groups, int batch, int y_dtype, hipStream_t s);
+hipError_t launch_gemm(const GemvGroup* groups, int n_groups, int batch, int y_dtype, hipStream_t s);
+
+// Workspace layout of lbf_encode: hist[256] u32, then tile counts u32[n_tiles].
+constexpr uint64_t kWorkHistBytes = 1024;
+
+}  // namespace lbf

@@ -1,0 +1,247 @@
+"""ctypes binding of liblbf.so (C ABI in include/lbf.h).
+
+Argument marshalling only: every step of encode, decode and the fused
+products runs in the library's HIP kernels.  PyTorch provides device memory
+and the current stream.  The library must be built (``__graft_entry__.build()``
+or ``python -m decode_byte_split_amd.build_lib``); importing this module
+without it raises, there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Sequence
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblbf.so")
+
+LBF_OK = 0
+LBF_E_INVAL = -1
+LBF_E_SHAPE = -2
+LBF_E_ALIGN = -3
+LBF_E_DESC = -4
+LBF_E_CAPACITY = -5
+LBF_E_HIP = -6
+LBF_E_UNSUPPORTED = -7
+LBF_F32 = 0
+LBF_BF16 = 1
+TILE = 1024
+MAX_GROUPS = 32
+
+
+class Desc(ctypes.Structure):
+    """Mirror of ``lbf_desc`` (96 bytes, the first bytes of every blob)."""
+
+    _fields_ = [
+        ("magic", ctypes.c_uint32),
+        ("version", ctypes.c_uint16),
+        ("tile_log2", ctypes.c_uint16),
+        ("rows", ctypes.c_uint64),
+        ("cols", ctypes.c_uint64),
+        ("n_esc", ctypes.c_uint64),
+        ("off_raw", ctypes.c_uint64),
+        ("off_nib", ctypes.c_uint64),
+        ("off_idx", ctypes.c_uint64),
+        ("off_esc", ctypes.c_uint64),
+        ("blob_bytes", ctypes.c_uint64),
+        ("lut", ctypes.c_uint8 * 16),
+        ("n_codes", ctypes.c_uint8),
+        ("reserved", ctypes.c_uint8 * 3),
+        ("desc_crc", ctypes.c_uint32),
+    ]
+
+    def to_bytes(self) -> bytes:
+        return ctypes.string_at(ctypes.addressof(self), ctypes.sizeof(self))
+
+    @classmethod
+    def from_bytes(cls, b) -> "Desc":
+        b = bytes(b)[:ctypes.sizeof(cls)]
+        return cls.from_buffer_copy(b)
+
+
+assert ctypes.sizeof(Desc) == 96
+
+
+class LbfError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s: %s (%d)" % (what, strerror(status), status))
+
+
+_lib = None
+
+
+def lib():
+    """Load liblbf.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("liblbf.so is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, u64, i32 = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int
+        dp = ctypes.POINTER(Desc)
+        vpp = ctypes.POINTER(ctypes.c_void_p)
+        L.lbf_strerror.restype = ctypes.c_char_p
+        L.lbf_strerror.argtypes = [i32]
+        L.lbf_encode_work_bytes.restype = u64
+        L.lbf_encode_work_bytes.argtypes = [u64, u64]
+        L.lbf_desc_check.restype = i32
+        L.lbf_desc_check.argtypes = [dp]
+        L.lbf_encode.restype = i32
+        L.lbf_encode.argtypes = [vp, u64, u64, vp, u64, vp, u64, dp, vp]
+        L.lbf_decode.restype = i32
+        L.lbf_decode.argtypes = [dp, vp, vp, vp]
+        for name in ("lbf_gemv", "lbf_gemm"):
+            f = getattr(L, name)
+            f.restype = i32
+            f.argtypes = [dp, vpp, i32, vpp, i32, vpp, i32, vp]
+        _lib = L
+    return _lib
+
+
+EXPORTS = ("lbf_strerror", "lbf_encode_work_bytes", "lbf_desc_check", "lbf_encode", "lbf_decode", "lbf_gemv",
+           "lbf_gemm")
+
+
+def strerror(status: int) -> str:
+    return lib().lbf_strerror(status).decode()
+
+
+def desc_check(d: Desc) -> int:
+    return int(lib().lbf_desc_check(ctypes.byref(d)))
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _stream(stream=None) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _ptr(t) -> int:
+    return int(t.data_ptr())
+
+
+@dataclass
+class Blob:
+    """A coded weight tensor: host descriptor + device blob (torch uint8)."""
+
+    desc: Desc
+    data: "object"  # torch.Tensor, uint8, on the GPU
+
+    @property
+    def rows(self) -> int:
+        return int(self.desc.rows)
+
+    @property
+    def cols(self) -> int:
+        return int(self.desc.cols)
+
+    @property
+    def n_esc(self) -> int:
+        return int(self.desc.n_esc)
+
+    @property
+    def nbytes(self) -> int:
+        return int(self.desc.blob_bytes)
+
+
+def _check(rc: int, what: str):
+    if rc != LBF_OK:
+        raise LbfError(rc, what)
+
+
+def encode(w, stream=None) -> Blob:
+    """Code a 2-D BF16 tensor (torch.bfloat16 or int16/uint16 bit patterns on the GPU)."""
+    torch = _torch()
+    if w.dim() != 2 or not w.is_cuda or w.element_size() != 2:
+        raise ValueError("encode takes a 2-D 16-bit tensor on the GPU")
+    w = w.contiguous()
+    rows, cols = w.shape
+    L = lib()
+    s = _stream(stream)
+    wb = int(L.lbf_encode_work_bytes(rows, cols))
+    work = torch.empty(max(wb, 256), dtype=torch.uint8, device=w.device)
+    d = Desc()
+    _check(L.lbf_encode(_ptr(w), rows, cols, _ptr(work), work.numel(), None, 0, ctypes.byref(d), s), "lbf_encode phase 1")
+    blob = torch.empty(int(d.blob_bytes), dtype=torch.uint8, device=w.device)
+    _check(L.lbf_encode(_ptr(w), rows, cols, _ptr(work), work.numel(), _ptr(blob), blob.numel(), ctypes.byref(d), s),
+           "lbf_encode phase 2")
+    if stream is not None:  # keep the workspace alive until the stream has used it
+        work.record_stream(stream)
+        blob.record_stream(stream)
+    return Blob(d, blob)
+
+
+def from_host_blob(blob_bytes: np.ndarray, device="cuda") -> Blob:
+    """Wrap a blob produced elsewhere (e.g. a saved file) as a device Blob."""
+    torch = _torch()
+    b = np.ascontiguousarray(blob_bytes, dtype=np.uint8)
+    d = Desc.from_bytes(b[:96].tobytes())
+    _check(desc_check(d), "blob header")
+    t = torch.from_numpy(b.copy()).to(device)
+    return Blob(d, t)
+
+
+def decode(blob: Blob, out=None, stream=None):
+    """Rebuild the exact BF16 tensor (torch.bfloat16 [rows, cols])."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty((blob.rows, blob.cols), dtype=torch.bfloat16, device=blob.data.device)
+    _check(lib().lbf_decode(ctypes.byref(blob.desc), _ptr(blob.data), _ptr(out), _stream(stream)), "lbf_decode")
+    return out
+
+
+def _product(fn, what, blobs: Sequence[Blob], xs, y_dtype, outs, stream):
+    torch = _torch()
+    n = len(blobs)
+    if len(xs) != n:
+        raise ValueError("one x per blob")
+    batch = int(xs[0].shape[0])
+    descs = (Desc * n)(*[b.desc for b in blobs])
+    pb = (ctypes.c_void_p * n)(*[_ptr(b.data) for b in blobs])
+    xs = [x.contiguous() for x in xs]
+    for x, b in zip(xs, blobs):
+        if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[0] != batch or x.shape[1] != b.cols:
+            raise ValueError("x must be bfloat16 [batch, cols] with the same batch for every group")
+    px = (ctypes.c_void_p * n)(*[_ptr(x) for x in xs])
+    tdt = torch.float32 if y_dtype == LBF_F32 else torch.bfloat16
+    if outs is None:
+        outs = [torch.empty((batch, b.rows), dtype=tdt, device=b.data.device) for b in blobs]
+    py = (ctypes.c_void_p * n)(*[_ptr(y) for y in outs])
+    _check(fn(descs, pb, n, px, batch, py, y_dtype, _stream(stream)), what)
+    return outs
+
+
+def gemv(blobs, xs, y_dtype: int = LBF_F32, outs=None, stream=None):
+    """Fused decode-GEMV, batch 1..8: y_g = x_g @ W_g^T for each group (one launch)."""
+    single = isinstance(blobs, Blob)
+    if single:
+        blobs, xs = [blobs], [xs]
+        outs = None if outs is None else [outs]
+    ys = _product(lib().lbf_gemv, "lbf_gemv", blobs, xs, y_dtype, outs, stream)
+    return ys[0] if single else ys
+
+
+def gemm(blobs, xs, y_dtype: int = LBF_BF16, outs=None, stream=None):
+    """Fused decode-GEMM on MFMA, batch >= 9."""
+    single = isinstance(blobs, Blob)
+    if single:
+        blobs, xs = [blobs], [xs]
+        outs = None if outs is None else [outs]
+    ys = _product(lib().lbf_gemm, "lbf_gemm", blobs, xs, y_dtype, outs, stream)
+    return ys[0] if single else ys
+
+
+def matmul(blobs, xs, y_dtype: int = LBF_F32, outs=None, stream=None):
+    """Dispatch by batch: gemv for 1..8, gemm above."""
+    b = (xs if not isinstance(blobs, Blob) else [xs])[0].shape[0]
+    return (gemv if b <= 8 else gemm)(blobs, xs, y_dtype, outs, stream)

@@ -1,0 +1,163 @@
+/*
+ * lbf.h — C ABI of liblbf.so: lossless byte-split BF16 weights decoded on an
+ * MI355X (gfx950) straight into the matrix-vector or matrix product.
+ *
+ * The method (pages this library follows):
+ *  - "Lossless LLM Weight Compression vs 8-bit GGUF" (wavect.io, English),
+ *    section "What does 'lossless' mean for LLM weights?": coded weights may
+ *    stay in GPU memory and be rebuilt, exactly, in registers or shared
+ *    memory right before the multiply; the round trip decides losslessness.
+ *  - same page, section "What did the GLM-5.2 experiment actually prove?":
+ *    BF16 is sign (1) + exponent (8) + mantissa (7) bits; the frequent
+ *    exponents get short fixed-width codes and the others go, verbatim, to an
+ *    escape stream.
+ *  - same page, opening section: the byte-split representation; "K15", read
+ *    here as an alphabet of 15 coded symbols plus one escape code.
+ *
+ * Format v1 (one "blob" per weight tensor, one contiguous device buffer):
+ *   [0, 256)        header: the 96-byte lbf_desc below, then zeros
+ *   off_raw = 256   raw plane, one byte per weight: sign << 7 | mantissa,
+ *                   zero padded to n_tiles * 1024 bytes
+ *   off_nib         nibble plane: weight i's 4-bit code is the low (i even) or
+ *                   high (i odd) nibble of byte i >> 1; code c < 15 means
+ *                   exponent lut[c], code 15 means "next escape byte";
+ *                   zero padded to n_tiles * 512 bytes
+ *   off_idx         uint32 idx[n_tiles + 1]: idx[0] = 0 and idx[t + 1] - idx[t]
+ *                   is the number of escapes in tile t (1024 weights)
+ *   off_esc         escape stream: one exponent byte per escaped weight, in
+ *                   flat element order; tile t's escapes are [idx[t], idx[t+1])
+ * Each plane starts at a multiple of 256; blob_bytes is a multiple of 256.
+ * n = rows * cols, n_tiles = ceil(n / 1024); W is row-major [rows, cols]
+ * (rows = out_features, cols = in_features: the nn.Linear layout).
+ *
+ * Code table: the (up to) 15 most frequent exponents of the tensor, count
+ * descending, ties to the smaller exponent; codes are given in ascending
+ * exponent order.  Unused lut slots and lut[15] are 0.
+ *
+ * Conventions for every call:
+ *  - d_* arguments are device pointers (or host arrays of device pointers
+ *    where the type says so); the caller allocates and owns all memory.  The
+ *    library allocates no device memory and keeps no mutable global state.
+ *  - every call checks its arguments and descriptors on the host before it
+ *    launches anything and returns a negative LBF_E_* status, with no side
+ *    effect, when a check fails.  A failed launch returns LBF_E_HIP.
+ *  - every call except encode phase 1 only enqueues work on the stream `s`
+ *    (a hipStream_t; NULL is the null stream) and returns.
+ *  - identical inputs give bitwise-identical outputs (no floating-point
+ *    atomics; fixed reduction order).
+ */
+#ifndef LBF_H
+#define LBF_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LBF_MAGIC 0x3146424Cu /* "LBF1" little-endian */
+#define LBF_VERSION 1
+#define LBF_TILE_LOG2 10
+#define LBF_TILE 1024
+#define LBF_HEADER_BYTES 256
+#define LBF_MAX_GROUPS 32 /* groups per kernel launch; larger calls are split */
+
+/* Host copy of a blob's header; byte-for-byte the first 96 bytes of the blob. */
+typedef struct lbf_desc {
+  uint32_t magic;      /* LBF_MAGIC */
+  uint16_t version;    /* LBF_VERSION */
+  uint16_t tile_log2;  /* LBF_TILE_LOG2 */
+  uint64_t rows, cols; /* W is [rows, cols], row-major; rows * cols < 2^32 */
+  uint64_t n_esc;      /* number of escaped weights */
+  uint64_t off_raw, off_nib, off_idx, off_esc, blob_bytes;
+  uint8_t lut[16];     /* lut[c] = exponent of code c, c < n_codes */
+  uint8_t n_codes;     /* 0..15 */
+  uint8_t reserved[3]; /* zero */
+  uint32_t desc_crc;   /* CRC-32 (IEEE) of the 92 bytes before this field */
+} lbf_desc;
+
+enum {
+  LBF_OK = 0,
+  LBF_E_INVAL = -1,       /* null pointer, bad enum, batch out of range */
+  LBF_E_SHAPE = -2,       /* shape not supported by this call, or mismatched */
+  LBF_E_ALIGN = -3,       /* a device pointer is not aligned as required */
+  LBF_E_DESC = -4,        /* descriptor fails validation (corrupt or foreign) */
+  LBF_E_CAPACITY = -5,    /* destination or workspace buffer too small */
+  LBF_E_HIP = -6,         /* a HIP runtime call or launch failed */
+  LBF_E_UNSUPPORTED = -7  /* valid request this build does not handle */
+};
+
+enum { LBF_F32 = 0, LBF_BF16 = 1 }; /* output element types */
+
+/* Human-readable text for a status code (static storage). */
+const char* lbf_strerror(int status);
+
+/* Bytes of device workspace lbf_encode needs for a [rows, cols] tensor. */
+uint64_t lbf_encode_work_bytes(uint64_t rows, uint64_t cols);
+
+/* Host-only check of a descriptor (magic, version, CRC, offsets, table).
+ * Returns LBF_OK or LBF_E_DESC.  Needs no GPU. */
+int lbf_desc_check(const lbf_desc* desc);
+
+/*
+ * lbf_encode — code a BF16 tensor into a blob (two phases).
+ *   d_w        device, bf16 bit patterns [rows, cols], row-major, 2-byte aligned
+ *   d_work     device workspace of at least lbf_encode_work_bytes(rows, cols)
+ *              bytes, 256-byte aligned; its contents on entry do not matter
+ *   desc       host; phase 1 writes it, phase 2 reads it
+ * Phase 1 (d_blob == NULL): exponent histogram on the GPU, then the code table,
+ *   escape count and plane offsets on the host; fills *desc.  This call waits
+ *   for the stream (the only synchronising call in the library).
+ * Phase 2 (d_blob != NULL): writes the whole blob (header included) on `s`;
+ *   desc must be the unchanged phase-1 result for the same d_w.  d_blob must
+ *   be 256-byte aligned and blob_cap >= desc->blob_bytes (else
+ *   LBF_E_CAPACITY).
+ * Shapes: any rows, cols with rows * cols < 2^32 (LBF_E_SHAPE otherwise).
+ */
+int lbf_encode(const void* d_w, uint64_t rows, uint64_t cols, void* d_work, uint64_t work_bytes,
+               void* d_blob, uint64_t blob_cap, lbf_desc* desc, hipStream_t s);
+
+/*
+ * lbf_decode — rebuild the exact BF16 tensor from a blob.
+ *   desc       host copy of the blob's header (checked with lbf_desc_check)
+ *   d_blob     device, 256-byte aligned, desc->blob_bytes long
+ *   d_w_out    device, bf16 [rows, cols], 4-byte aligned; fully overwritten
+ * Bit-exact: NaN payloads, signed zeros, infinities and denormals survive.
+ */
+int lbf_decode(const lbf_desc* desc, const void* d_blob, void* d_w_out, hipStream_t s);
+
+/*
+ * lbf_gemv — y[g][b, r] = sum_k W_g[r, k] * x[g][b, k] for each group g, with
+ * each W_g decoded in registers only, products accumulated in fp32.
+ * (Fused decode and multiply: same page, section "What does 'lossless' mean
+ * for LLM weights?".)
+ *   descs      host array [n_groups] of descriptors, one per weight tensor
+ *   d_blobs    host array [n_groups] of device blob pointers (256-B aligned)
+ *   d_x        host array [n_groups] of device pointers to bf16 x_g
+ *              [batch, cols_g], row-major, 16-byte aligned
+ *   batch      1..8
+ *   d_y        host array [n_groups] of device pointers to y_g [batch, rows_g]
+ *              (row-major, the F.linear output layout), 4-byte aligned,
+ *              element type y_dtype (LBF_F32, or LBF_BF16 rounded to nearest
+ *              even from the fp32 sum); fully overwritten
+ * Requires cols_g % 1024 == 0 (LBF_E_SHAPE otherwise).  n_groups >= 1; calls
+ * with more than LBF_MAX_GROUPS groups are issued as several launches.
+ * Every group runs in the same launch when n_groups <= LBF_MAX_GROUPS.
+ */
+int lbf_gemv(const lbf_desc* descs, const void* const* d_blobs, int n_groups, const void* const* d_x,
+             int batch, void* const* d_y, int y_dtype, hipStream_t s);
+
+/*
+ * lbf_gemm — the same product for batch >= 9, on bf16 MFMA (matrix cores)
+ * with fp32 accumulation; the decoded weights go straight into the MFMA
+ * operand registers.  Arguments as lbf_gemv; batch 9..256.
+ */
+int lbf_gemm(const lbf_desc* descs, const void* const* d_blobs, int n_groups, const void* const* d_x,
+             int batch, void* const* d_y, int y_dtype, hipStream_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LBF_H */

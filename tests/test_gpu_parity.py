@@ -1,0 +1,240 @@
+"""GPU parity: liblbf.so (HIP, gfx950) against the CPU oracle, through the C ABI.
+
+Bar: decode and encode are bit-exact (byte-equal blobs, byte-equal tensors);
+the fused products stay within |y - y_ref| <= 1e-3 * sum_k |W[r,k]| |x[b,k]|
+of the float64 oracle (plus half a bf16 ulp of y_ref when y is rounded to
+bf16); non-finite outputs must match in class (NaN <-> NaN, same-signed Inf).
+"""
+import os
+import sys
+import time
+
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+from decode_byte_split_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    sys.stdout.write("[gpu-parity] %s\n" % msg)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    from decode_byte_split_amd import lbf
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    lbf.lib()
+    return torch, lbf
+
+
+def dev(torch, a: np.ndarray):
+    """uint16 bf16 patterns (numpy) -> torch.bfloat16 on the GPU."""
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def host(t) -> np.ndarray:
+    return t.view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+
+
+def tensors():
+    g = {}
+    g["single_1024x1024"] = synth.single_tensor()[0]
+    g["patterns_256x256"] = synth.all_patterns(256, 256)
+    rng = np.random.default_rng(7)
+    g["ragged_7x333"] = synth.gaussian(rng, 7, 333, 0.02, 0.01, 100.0)
+    g["ragged_1x1"] = synth.gaussian(rng, 1, 1, 0.02, 0.0, 1.0)
+    g["ragged_5x4097"] = synth.gaussian(rng, 5, 4097, 0.02, 0.002, 100.0)
+    g["uniform_bits_3x1500"] = rng.integers(0, 65536, (3, 1500), dtype=np.uint32).astype(np.uint16)
+    g["expert_rate20pct_256x1024"] = synth.gaussian(rng, 256, 1024, 0.02, 0.2, 100.0)
+    g["laplace_128x2048"] = synth.laplace(rng, 128, 2048, 0.02)
+    # an escape in every tile at the first and last element, and a tile of escapes
+    W = synth.gaussian(rng, 4, 4096, 0.02, 0.0, 1.0)
+    flat = W.reshape(-1)
+    flat[::1024] = 0x7F80  # +Inf, exponent 255: never coded here
+    flat[1023::1024] = 0x0001  # smallest denormal, exponent 0
+    flat[4096:5120] = (np.arange(1024) % 65536).astype(np.uint16) | 0x7000
+    g["edge_escapes_4x4096"] = W
+    return g
+
+
+TENSORS = tensors()
+
+
+@pytest.mark.parametrize("name", sorted(TENSORS))
+def test_decode_oracle_blob_bit_exact(env, name):
+    torch, lbf = env
+    W = TENSORS[name]
+    say("decode %s %s" % (name, W.shape))
+    blob = lbf.from_host_blob(O.encode(W))
+    out = lbf.decode(blob)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out), W)
+
+
+@pytest.mark.parametrize("name", sorted(TENSORS))
+def test_encode_blob_equals_oracle(env, name):
+    torch, lbf = env
+    W = TENSORS[name]
+    say("encode %s %s" % (name, W.shape))
+    b = lbf.encode(dev(torch, W))
+    torch.cuda.synchronize()
+    ref = O.encode(W)
+    got = b.data.cpu().numpy()
+    assert got.size == ref.size
+    assert np.array_equal(got, ref)
+    assert np.array_equal(O.decode(got), W)  # the oracle decodes the GPU's blob
+
+
+def test_encode_decode_empty(env):
+    torch, lbf = env
+    W = np.zeros((0, 1024), dtype=np.uint16)
+    b = lbf.encode(torch.zeros((0, 1024), dtype=torch.bfloat16, device="cuda"))
+    torch.cuda.synchronize()
+    assert np.array_equal(b.data.cpu().numpy(), O.encode(W))
+    assert lbf.decode(b).shape == (0, 1024)
+
+
+def test_decode_leaves_neighbours_untouched(env):
+    torch, lbf = env
+    W = TENSORS["ragged_7x333"]
+    blob = lbf.from_host_blob(O.encode(W))
+    n = W.size
+    guard = 4096
+    buf = torch.full((guard + n + guard,), -12345, dtype=torch.int16, device="cuda")
+    out = buf[guard:guard + n].view(torch.bfloat16).view(7, 333)
+    lbf.decode(blob, out=out)
+    torch.cuda.synchronize()
+    h = buf.cpu().numpy()
+    assert (h[:guard] == -12345).all() and (h[guard + n:] == -12345).all()
+    assert np.array_equal(h[guard:guard + n].view(np.uint16).reshape(7, 333), W)
+
+
+def check_product(y_gpu, y_ref, a_ref, bf16_out):
+    y = y_gpu.float().cpu().numpy().astype(np.float64)
+    fin = np.isfinite(y_ref)
+    # non-finite reference entries: same class on the GPU
+    assert np.array_equal(np.isnan(y[~fin]), np.isnan(y_ref[~fin]))
+    inf = np.isinf(y_ref)
+    assert np.array_equal(y[inf], y_ref[inf])
+    tol = 1e-3 * a_ref[fin]
+    if bf16_out:
+        tol = tol + 2.0 ** -8 * np.abs(y_ref[fin])
+    err = np.abs(y[fin] - y_ref[fin])
+    worst = np.max(err - tol) if err.size else -1
+    assert np.all(err <= tol), "max excess %g" % worst
+
+
+@pytest.mark.parametrize("batch", [1, 2, 3, 4, 5, 8])
+def test_gemv_single_tensor(env, batch):
+    torch, lbf = env
+    W, x1 = synth.single_tensor()
+    x = x1 if batch == 1 else synth.activations(np.random.default_rng([0, 1, batch]), batch, 1024)
+    say("gemv single_tensor B=%d" % batch)
+    blob = lbf.from_host_blob(O.encode(W))
+    y_ref, a_ref = O.matvec(W, x)
+    y = lbf.gemv(blob, dev(torch, x), lbf.LBF_F32)
+    torch.cuda.synchronize()
+    check_product(y, y_ref, a_ref, False)
+    yb = lbf.gemv(blob, dev(torch, x), lbf.LBF_BF16)
+    torch.cuda.synchronize()
+    check_product(yb, y_ref, a_ref, True)
+
+
+def test_gemv_one_hot_extracts_column_exactly(env):
+    torch, lbf = env
+    W = TENSORS["laplace_128x2048"]
+    blob = lbf.from_host_blob(O.encode(W))
+    x = np.zeros((8, 2048), dtype=np.uint16)
+    ks = [0, 1, 15, 16, 1023, 1024, 2000, 2047]
+    for b, k in enumerate(ks):
+        x[b, k] = 0x3F80
+    y = lbf.gemv(blob, dev(torch, x), lbf.LBF_F32)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    for b, k in enumerate(ks):
+        assert np.array_equal(y[b], synth.bf16_to_f32(W[:, k])), k
+
+
+def test_gemv_deterministic(env):
+    torch, lbf = env
+    W = synth.layer_tensor(1)
+    x = synth.layer_x(1, 4)
+    blob = lbf.encode(dev(torch, W))
+    xs = dev(torch, x)
+    y1 = lbf.gemv(blob, xs).cpu().numpy()
+    y2 = lbf.gemv(blob, xs).cpu().numpy()
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
+def test_gemv_nonfinite_all_patterns(env):
+    torch, lbf = env
+    W = synth.all_patterns(1536, 4096)
+    x = synth.expert_x(63)
+    say("gemv all-patterns expert B=4")
+    blob = lbf.encode(dev(torch, W))
+    y_ref, a_ref = O.matvec(W, x)
+    y = lbf.gemv(blob, dev(torch, x))
+    torch.cuda.synchronize()
+    check_product(y, y_ref, a_ref, False)
+
+
+def test_gemv_layer_grouped_full(env):
+    """One 8B-shaped layer (7 tensors) in one grouped launch, every output checked."""
+    torch, lbf = env
+    t0 = time.time()
+    Ws = [synth.layer_tensor(m) for m in range(len(synth.LAYER))]
+    xs = [synth.layer_x(m) for m in range(len(synth.LAYER))]
+    say("layer generated in %.1fs" % (time.time() - t0))
+    blobs = [lbf.encode(dev(torch, W)) for W in Ws]
+    # the GPU blob of the largest tensor equals the oracle's, byte for byte
+    ref = O.encode(Ws[synth.GATE])
+    assert np.array_equal(blobs[synth.GATE].data.cpu().numpy(), ref)
+    ys = lbf.gemv(blobs, [dev(torch, x) for x in xs], lbf.LBF_F32)
+    torch.cuda.synchronize()
+    for m, (W, x, y) in enumerate(zip(Ws, xs, ys)):
+        y_ref, a_ref = O.matvec(W, x)
+        check_product(y, y_ref, a_ref, False)
+        say("layer %s ok" % synth.LAYER[m][0])
+    # standalone decode of every tensor is bit-exact
+    for W, b in zip(Ws, blobs):
+        assert np.array_equal(host(lbf.decode(b)), W)
+
+
+def test_gemv_gate_batch_sweep(env):
+    torch, lbf = env
+    W = synth.layer_tensor(synth.GATE)
+    blob = lbf.encode(dev(torch, W))
+    for batch in (1, 2, 4, 8):
+        x = synth.gate_batch_x(batch)
+        y_ref, a_ref = O.matvec(W, x, rows=(0, 14336))
+        yb = lbf.gemv(blob, dev(torch, x), lbf.LBF_BF16)
+        yf = lbf.gemv(blob, dev(torch, x), lbf.LBF_F32)
+        torch.cuda.synchronize()
+        check_product(yb, y_ref, a_ref, True)
+        check_product(yf, y_ref, a_ref, False)
+        say("gate sweep B=%d ok" % batch)
+
+
+def test_gemv_experts_grouped(env):
+    """64 expert tensors (escape-rate stress) at batch 4, grouped launches."""
+    torch, lbf = env
+    t0 = time.time()
+    Ws = [synth.expert_tensor(e) for e in range(64)]
+    xs = [synth.expert_x(e) for e in range(64)]
+    say("experts generated in %.1fs" % (time.time() - t0))
+    blobs = [lbf.encode(dev(torch, W)) for W in Ws]
+    for e in (0, 3, 4, 62, 63):
+        assert np.array_equal(blobs[e].data.cpu().numpy(), O.encode(Ws[e])), e
+    ys = lbf.gemv(blobs, [dev(torch, x) for x in xs], lbf.LBF_F32)
+    torch.cuda.synchronize()
+    for e in range(64):
+        y_ref, a_ref = O.matvec(Ws[e], xs[e])
+        check_product(ys[e], y_ref, a_ref, False)
+    for e in (4, 62, 63):
+        assert np.array_equal(host(lbf.decode(blobs[e])), Ws[e]), e

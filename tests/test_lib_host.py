@@ -1,0 +1,124 @@
+"""Host-side checks of liblbf.so that need no GPU: it loads, exports every
+symbol include/lbf.h declares, and its descriptor validation (which runs before
+any launch) agrees with the oracle's header and rejects corrupt descriptors."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+from decode_byte_split_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lbf():
+    from decode_byte_split_amd import lbf
+
+    return lbf
+
+
+def test_header_declarations_are_exported():
+    lbf = _lbf()
+    L = lbf.lib()
+    with open(os.path.join(ROOT, "include", "lbf.h")) as f:
+        text = f.read()
+    declared = set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]*?\b(lbf_\w+)\s*\(", text, flags=re.M))
+    assert declared, "no declarations found"
+    assert declared == set(lbf.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_strerror():
+    lbf = _lbf()
+    assert lbf.strerror(0) == "ok"
+    assert "descriptor" in lbf.strerror(lbf.LBF_E_DESC)
+
+
+def test_work_bytes():
+    lbf = _lbf()
+    n = lbf.lib().lbf_encode_work_bytes(14336, 4096)
+    assert n >= 1024 + 4 * (14336 * 4096 // 1024)
+    assert lbf.lib().lbf_encode_work_bytes(1 << 20, 1 << 20) == 0  # n >= 2^32
+
+
+def _oracle_desc(W):
+    lbf = _lbf()
+    blob = O.encode(W)
+    return lbf.Desc.from_bytes(blob[:96].tobytes()), blob
+
+
+@pytest.mark.parametrize("shape", [(1024, 1024), (3, 5), (0, 8), (256, 256)])
+def test_oracle_headers_pass_library_check(shape):
+    lbf = _lbf()
+    if shape == (256, 256):
+        W = synth.all_patterns(256, 256)
+    else:
+        W = synth.gaussian(np.random.default_rng(1), shape[0], shape[1], 0.02, 0.001, 100.0)
+    d, blob = _oracle_desc(W)
+    assert lbf.desc_check(d) == 0
+    assert d.blob_bytes == blob.size
+
+
+def test_corrupt_descriptors_rejected():
+    lbf = _lbf()
+    W, _ = synth.single_tensor()
+    d, _ = _oracle_desc(W)
+    raw = bytearray(d.to_bytes())
+    for off in range(0, 96):
+        bad = bytearray(raw)
+        bad[off] ^= 0x10
+        bd = lbf.Desc.from_bytes(bytes(bad))
+        assert lbf.desc_check(bd) == lbf.LBF_E_DESC, off
+
+
+def test_self_consistent_but_invalid_descriptors_rejected():
+    # fields re-signed with a valid CRC but violating the format's invariants
+    lbf = _lbf()
+    W, _ = synth.single_tensor()
+    d, _ = _oracle_desc(W)
+
+    def resign(x):
+        x.desc_crc = O.crc32(np.frombuffer(x.to_bytes()[:92], dtype=np.uint8))
+        return x
+
+    assert lbf.desc_check(resign(lbf.Desc.from_bytes(d.to_bytes()))) == 0
+    bad = lbf.Desc.from_bytes(d.to_bytes())
+    bad.lut[0], bad.lut[1] = bad.lut[1], bad.lut[0]  # table not ascending
+    assert lbf.desc_check(resign(bad)) == lbf.LBF_E_DESC
+    bad = lbf.Desc.from_bytes(d.to_bytes())
+    bad.off_esc += 256
+    assert lbf.desc_check(resign(bad)) == lbf.LBF_E_DESC
+    bad = lbf.Desc.from_bytes(d.to_bytes())
+    bad.n_esc = bad.rows * bad.cols + 1
+    assert lbf.desc_check(resign(bad)) == lbf.LBF_E_DESC
+    bad = lbf.Desc.from_bytes(d.to_bytes())
+    bad.n_codes = 16
+    assert lbf.desc_check(resign(bad)) == lbf.LBF_E_DESC
+
+
+def test_calls_validate_before_touching_the_gpu():
+    # A corrupt descriptor is refused before any HIP call, so this runs on a
+    # machine without a GPU; the pointers are never dereferenced.
+    lbf = _lbf()
+    L = lbf.lib()
+    W, _ = synth.single_tensor()
+    d, _ = _oracle_desc(W)
+    bad = lbf.Desc.from_bytes(d.to_bytes())
+    bad.rows += 1
+    assert L.lbf_decode(ctypes.byref(bad), 256, 256, None) == lbf.LBF_E_DESC
+    descs = (lbf.Desc * 1)(bad)
+    p = (ctypes.c_void_p * 1)(256)
+    assert L.lbf_gemv(descs, p, 1, p, 1, p, 0, None) == lbf.LBF_E_DESC
+    good = (lbf.Desc * 1)(d)
+    assert L.lbf_gemv(good, p, 1, p, 9, p, 0, None) == lbf.LBF_E_INVAL  # batch 9 is not a GEMV
+    assert L.lbf_gemv(good, p, 1, p, 1, p, 7, None) == lbf.LBF_E_INVAL  # unknown output type
+    assert L.lbf_gemm(good, p, 1, p, 8, p, 0, None) == lbf.LBF_E_INVAL
+    misaligned = (ctypes.c_void_p * 1)(256 + 8)
+    assert L.lbf_gemv(good, misaligned, 1, p, 1, p, 0, None) == lbf.LBF_E_ALIGN
+    small = _oracle_desc(np.zeros((3, 5), dtype=np.uint16))[0]
+    assert L.lbf_gemv((lbf.Desc * 1)(small), p, 1, p, 1, p, 0, None) == lbf.LBF_E_SHAPE  # cols % 1024
+    assert L.lbf_encode(256, 1 << 20, 1 << 20, 256, 1 << 30, None, 0, ctypes.byref(lbf.Desc()), None) == lbf.LBF_E_SHAPE
