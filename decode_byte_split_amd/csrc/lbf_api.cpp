@@ -144,10 +144,13 @@ static int build_groups(const lbf_desc* descs, const void* const* d_blobs, int n
     G.rows = (uint32_t)d.rows;
     G.cols = (uint32_t)d.cols;
     G.n_esc = (uint32_t)d.n_esc;
-    G.unit_begin = 0;
     for (int q = 0; q < 4; q++) G.lut[q] = k.t[q];
     G.base4 = k.base4;
     G.flags = k.contiguous ? 1u : 0u;
+    G.geom = 0;
+    G.cost_begin = 0;
+    G.unit_cost = 0;
+    G.n_units = 0;
   }
   return LBF_OK;
 }

@@ -114,40 +114,56 @@ __device__ __forceinline__ void patch_exponent(uint32_t E[4], uint32_t i, uint32
   for (uint32_t q = 0; q < 4; q++) E[q] = (word == q) ? ((E[q] & ~m) | v) : E[q];
 }
 
-// Escape placement for one tile held by one wave (called by all 64 lanes,
-// only when the tile has escapes).  The tile's escape slice
-// esc[first, first + cnt) is staged in this wave's LDS slot (one byte per
-// escape, cnt <= 1024), each lane finds how many escapes lie in lower lanes
-// (wave prefix sum of per-lane counts), and patches its exponent bytes in
-// element order.  Reads beyond cnt (only possible on a corrupt blob) yield 0.
-__device__ __forceinline__ void place_escapes(u32x2 nib, const uint8_t* __restrict__ esc, uint32_t first,
-                                              uint32_t cnt, uint8_t* lds_slot, uint32_t E[4]) {
-  const int lane = lane_id();
-  for (uint32_t p = (uint32_t)lane; p < cnt; p += kWave) lds_slot[p] = esc[first + p];
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  uint32_t m0 = escape_bits(nib.x), m1 = escape_bits(nib.y);
-  uint32_t k = (uint32_t)(__builtin_popcount(m0) + __builtin_popcount(m1));
-  uint32_t j = wave_excl_scan_small(k);
+// Escapes of one tile, one wave (all 64 lanes must call): which of the lane's
+// 16 weights escape (bit 4i of m0 / m1 for weight i / 8 + i) and how many
+// escapes of the tile precede the lane's first one.  When no lane holds more
+// than one escape a single ballot gives the rank.
+__device__ __forceinline__ uint32_t escape_rank(u32x2 nib, uint32_t& m0, uint32_t& m1) {
+  m0 = escape_bits(nib.x);
+  m1 = escape_bits(nib.y);
+  const uint32_t k = (uint32_t)(__builtin_popcount(m0) + __builtin_popcount(m1));
+  if (__builtin_amdgcn_ballot_w64(k > 1u) == 0) return ballot_rank(__builtin_amdgcn_ballot_w64(k != 0u));
+  return wave_excl_scan_small(k);
+}
+
+// Patch the lane's escaped exponents, in element order, from src[j ...],
+// a byte array in LDS holding the tile's escapes; reads at or past cnt (a
+// corrupt blob) yield exponent 0 and touch nothing outside src[0, cnt).
+__device__ __forceinline__ void patch_escapes(const uint8_t* src, uint32_t j, uint32_t cnt, uint32_t m0, uint32_t m1,
+                                              uint32_t E[4]) {
   while (m0) {
     const uint32_t i = (uint32_t)__builtin_ctz(m0) >> 2;
-    const uint32_t e = j < cnt ? lds_slot[j] : 0u;
-    patch_exponent(E, i, e);
+    patch_exponent(E, i, j < cnt ? src[j] : 0u);
     m0 &= m0 - 1;
     j++;
   }
   while (m1) {
     const uint32_t i = 8u + ((uint32_t)__builtin_ctz(m1) >> 2);
-    const uint32_t e = j < cnt ? lds_slot[j] : 0u;
-    patch_exponent(E, i, e);
+    patch_exponent(E, i, j < cnt ? src[j] : 0u);
     m1 &= m1 - 1;
     j++;
   }
-  // the slot is reused by the next tile: finish reading before anyone rewrites it
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Escape placement for one tile held by one wave (called by all 64 lanes,
+// only when the tile has escapes).  The tile's escape slice
+// esc[first, first + cnt) is staged in this wave's LDS slot (cnt <= 1024),
+// then each lane patches its exponent bytes in element order.
+__device__ __forceinline__ void place_escapes(u32x2 nib, const uint8_t* __restrict__ esc, uint32_t first,
+                                              uint32_t cnt, uint8_t* lds_slot, uint32_t E[4]) {
+  const int lane = lane_id();
+  for (uint32_t p = (uint32_t)lane; p < cnt; p += kWave) lds_slot[p] = esc[first + p];
+  wave_lds_sync();
+  uint32_t m0, m1;
+  const uint32_t j = escape_rank(nib, m0, m1);
+  patch_escapes(lds_slot, j, cnt, m0, m1, E);
+  wave_lds_sync();  // the slot is rewritten for the next tile
 }
 
 // Escape range of tile t from the index plane, clamped so that a corrupt

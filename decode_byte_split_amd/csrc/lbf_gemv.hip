@@ -6,22 +6,29 @@
 // the in-VRAM use of lossless coding described on "Lossless LLM Weight
 // Compression vs 8-bit GGUF", section "What does 'lossless' mean for LLM
 // weights?".  Weight bandwidth is the bound (same page, section "Lossless
-// compression or Q8 GGUF: which should you deploy?", on weight-bandwidth-bound
-// fleets), so the kernel is shaped for HBM streaming:
+// compression or Q8 GGUF: which should you deploy?", on fleets whose
+// bottleneck is weight bandwidth), so the kernel is built for HBM streaming:
 //
-//  * work unit = (weight tensor, block of rows); one 256-thread workgroup per
-//    unit, several tensors ("groups") per launch;
-//  * K-stationary waves: within a unit each wave owns a fixed slice of whole
-//    1024-weight tiles of every row it handles, keeps the matching x values
-//    in VGPRs (B x tiles x 8 registers) and walks rows; the tensor's 4 waves
-//    split K into 1, 2 or 4 slices and the rows between them;
-//  * per tile and lane: one 16-byte raw load and one 8-byte nibble load, both
-//    non-temporal and coalesced; the escape index is read with scalar loads
-//    and the escape path runs only for tiles that hold escapes;
+//  * persistent workgroups (as many as fit on the chip), each taking one
+//    contiguous, cost-balanced range of work units across the launch's
+//    weight tensors ("groups"); a unit is `phases` consecutive rows of one
+//    tensor, all K;
+//  * K-stationary waves: each of the 4 waves owns a fixed slice of whole
+//    1024-weight tiles (1, 2 or 4 slices per row) and one row of every unit
+//    (the row phase), keeps the matching x values in VGPRs and walks rows;
+//  * per tile and lane one 16-byte raw load and one 8-byte nibble load, both
+//    non-temporal and coalesced; the loads for the next row are issued before
+//    the current row is decoded (two row buffers, ping-pong);
+//  * the escape bytes of a workgroup's whole range of one tensor are one
+//    contiguous slice of the escape stream: they are preloaded into LDS once,
+//    so a tile with escapes costs no extra memory round trip; the tile index
+//    is read with scalar loads;
 //  * each row's lane partials are summed across the wave with DPP and lane
-//    reads in a fixed order, slices are combined in LDS in slice order: no
+//    reads in a fixed order, K slices are combined in LDS in slice order: no
 //    floating-point atomics, bitwise-reproducible output.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 
 #include "lbf_device.h"
 #include "lbf_internal.h"
@@ -29,11 +36,12 @@
 namespace lbf {
 
 constexpr int kGemvWaves = 4;
-constexpr int kMaxUnitRows = 64;
-constexpr int kUnitTiles = 128;  // target tiles of weights per work unit
+constexpr int kSubUnits = 32;     // units whose partial sums share one LDS batch
+constexpr int kEscShared = 8192;  // escape bytes a workgroup preloads per tensor range
 
 struct GemvLaunch {
   GemvGroup g[LBF_MAX_GROUPS];
+  uint64_t total_cost;
   int n_groups;
   int y_bf16;
 };
@@ -69,145 +77,248 @@ __device__ __forceinline__ void dot16(const uint32_t w[8], const uint32_t (*xr)[
   }
 }
 
-template <int B, int SMAX>
-__global__ __launch_bounds__(kGemvWaves * kWave) void k_gemv(GemvLaunch L) {
-  __shared__ float part[kGemvWaves][kMaxUnitRows][B];
-  __shared__ uint8_t esc_lds[kGemvWaves][kTile];
+// One row's coded data for one wave's K slice.
+template <int SMAX>
+struct RowBuf {
+  u32x4 raw[SMAX];
+  u32x2 nib[SMAX];
+  uint32_t ix[SMAX + 1];  // escape index of the S tiles (and the next one)
+};
 
-  const uint32_t u = blockIdx.x;
-  int gi = 0;
-  while (gi + 1 < L.n_groups && L.g[gi + 1].unit_begin <= u) gi++;
-  const GemvGroup& G = L.g[gi];
+template <int SMAX>
+__device__ __forceinline__ void load_row(RowBuf<SMAX>& R, const uint8_t* raw_p, const uint8_t* nib_p,
+                                         const uint32_t* idx_p, uint64_t t0, uint32_t S, int lane) {
+#pragma unroll
+  for (int j = 0; j < SMAX; j++) {
+    if ((uint32_t)j < S) {
+      R.raw[j] = load_nt(reinterpret_cast<const u32x4*>(raw_p + (t0 + j) * kTile) + lane);
+      R.nib[j] = load_nt(reinterpret_cast<const u32x2*>(nib_p + (t0 + j) * (kTile / 2)) + lane);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j <= SMAX; j++)
+    if ((uint32_t)j <= S) R.ix[j] = idx_p[t0 + j];
+}
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const uint32_t T = G.cols >> 10;  // tiles per row
-  const uint32_t rb = G.geom & 0xFFFFu;
-  const uint32_t nks = (G.geom >> 16) & 0xFu;
-  const uint32_t phases = (G.geom >> 20) & 0xFu;
-  const uint32_t r0 = (u - G.unit_begin) * rb;
-  const uint32_t nr = min(rb, G.rows - r0);
-  const uint32_t slice = (uint32_t)wave % nks, phase = (uint32_t)wave / nks;
+struct SegCtx {
+  const uint8_t* esc_p;  // escape stream of the tensor
+  const uint8_t* esc_sh; // LDS copy of escapes [e_lo, e_hi) when preloaded
+  uint8_t* esc_wave;     // this wave's 1 KiB staging slot otherwise
+  uint32_t e_lo, e_hi;   // escape range of the workgroup's rows (clamped)
+  bool preload;
+  Lut lut;
+  uint32_t base4;
+};
 
+template <int B, int SMAX, bool CONTIG>
+__device__ __forceinline__ void row_dot(const RowBuf<SMAX>& R, uint32_t S, const uint32_t (*xr)[B][8],
+                                        const SegCtx& C, float acc[B][2]) {
+#pragma unroll
+  for (int b = 0; b < B; b++) acc[b][0] = acc[b][1] = 0.f;
+#pragma unroll
+  for (int j = 0; j < SMAX; j++) {
+    if ((uint32_t)j < S) {
+      uint32_t E[4];
+      exponents16<CONTIG>(R.nib[j], C.lut, C.base4, E);
+      // clamp the index into the range this workgroup knows, so a corrupt
+      // blob can only give wrong values, never an out-of-range access
+      const uint32_t a = min(max(R.ix[j], C.e_lo), C.e_hi);
+      const uint32_t e = min(max(R.ix[j + 1], a), C.e_hi);
+      const uint32_t cnt = min(e - a, (uint32_t)kTile);
+      if (cnt) {
+        if (C.preload) {
+          uint32_t m0, m1;
+          const uint32_t r = escape_rank(R.nib[j], m0, m1);
+          patch_escapes(C.esc_sh + (a - C.e_lo), r, cnt, m0, m1, E);
+        } else {
+          place_escapes(R.nib[j], C.esc_p, a, cnt, C.esc_wave, E);
+        }
+      }
+      uint32_t w[8];
+      assemble16(R.raw[j], E, w);
+      dot16<B>(w, xr[j], acc);
+    }
+  }
+}
+
+// One workgroup's units [u_lo, u_hi) of group G.
+template <int B, int SMAX, bool CONTIG>
+__device__ __forceinline__ void run_segment(const GemvGroup& G, uint32_t u_lo, uint32_t u_hi, bool y_bf16,
+                                            float (*part)[kGemvWaves][B], uint8_t* esc_sh, uint8_t* esc_wave,
+                                            uint32_t wave, int lane) {
+  const uint32_t T = G.cols >> 10;
+  const uint32_t nks = G.geom & 0xFu, phases = (G.geom >> 4) & 0xFu;
+  const uint32_t slice = wave % nks, phase = wave / nks;
   const uint64_t n_tiles = (uint64_t)G.rows * T;
   const uint8_t* raw_p = G.blob + LBF_HEADER_BYTES;
   const uint8_t* nib_p = raw_p + n_tiles * kTile;
   const uint32_t* idx_p = reinterpret_cast<const uint32_t*>(nib_p + n_tiles * (kTile / 2));
-  const uint8_t* esc_p = G.blob + ((LBF_HEADER_BYTES + n_tiles * (kTile + kTile / 2) + 4 * (n_tiles + 1) + 255) & ~uint64_t(255));
-  const Lut lut{G.lut[0], G.lut[1], G.lut[2], G.lut[3]};
-  const bool contig = G.flags & 1u;
+  const uint8_t* esc_p =
+      G.blob + ((LBF_HEADER_BYTES + n_tiles * (kTile + kTile / 2) + 4 * (n_tiles + 1) + 255) & ~uint64_t(255));
+  const uint32_t r_lo = u_lo * phases, r_hi = min(G.rows, u_hi * phases);
 
-  for (uint32_t c0 = 0; c0 < T; c0 += nks * SMAX) {
-    const uint32_t tb = c0 + slice * SMAX;
-    const uint32_t S = tb < T ? min((uint32_t)SMAX, T - tb) : 0u;
-    uint32_t xr[SMAX][B][8];
+  SegCtx C;
+  C.esc_p = esc_p;
+  C.esc_sh = esc_sh;
+  C.esc_wave = esc_wave;
+  C.lut = Lut{G.lut[0], G.lut[1], G.lut[2], G.lut[3]};
+  C.base4 = G.base4;
+  C.e_hi = min(idx_p[(uint64_t)r_hi * T], G.n_esc);
+  C.e_lo = min(idx_p[(uint64_t)r_lo * T], C.e_hi);
+  C.preload = C.e_hi - C.e_lo <= (uint32_t)kEscShared;
+  if (!C.preload) {  // dense escapes: per-tile staging, bounded by the stream itself
+    C.e_lo = 0;
+    C.e_hi = G.n_esc;
+  }
+  __syncthreads();  // the previous segment is done with esc_sh and part
+  if (C.preload)
+    for (uint32_t p = threadIdx.x; p < C.e_hi - C.e_lo; p += kGemvWaves * kWave) esc_sh[p] = esc_p[C.e_lo + p];
+  __syncthreads();
+
+  for (uint32_t sub = u_lo; sub < u_hi; sub += kSubUnits) {
+    const uint32_t nsub = min((uint32_t)kSubUnits, u_hi - sub);
+    for (uint32_t c0 = 0; c0 < T; c0 += nks * SMAX) {
+      const uint32_t tb = c0 + slice * SMAX;
+      const uint32_t S = tb < T ? min((uint32_t)SMAX, T - tb) : 0u;
+      uint32_t xr[SMAX][B][8];
 #pragma unroll
-    for (int j = 0; j < SMAX; j++) {
-      if ((uint32_t)j < S) {
+      for (int j = 0; j < SMAX; j++) {
+        if ((uint32_t)j < S) {
+#pragma unroll
+          for (int b = 0; b < B; b++) {
+            const u32x4* xp =
+                reinterpret_cast<const u32x4*>(G.x + (size_t)b * G.cols + (size_t)(tb + j) * kTile) + lane * 2;
+            const u32x4 a0 = xp[0], a1 = xp[1];
+            xr[j][b][0] = a0.x; xr[j][b][1] = a0.y; xr[j][b][2] = a0.z; xr[j][b][3] = a0.w;
+            xr[j][b][4] = a1.x; xr[j][b][5] = a1.y; xr[j][b][6] = a1.z; xr[j][b][7] = a1.w;
+          }
+        }
+      }
+      // this wave's rows: r(ul) = (sub + ul) * phases + phase, ul < nsub, r < rows
+      uint32_t n_mine = 0;
+      while (n_mine < nsub && (sub + n_mine) * phases + phase < G.rows) n_mine++;
+      auto tile0 = [&](uint32_t ul) { return (uint64_t)((sub + ul) * phases + phase) * T + tb; };
+      auto finish = [&](uint32_t ul, float acc[B][2]) {
 #pragma unroll
         for (int b = 0; b < B; b++) {
-          const u32x4* xp = reinterpret_cast<const u32x4*>(G.x + (size_t)b * G.cols + (size_t)(tb + j) * kTile) + lane * 2;
-          const u32x4 a0 = xp[0], a1 = xp[1];
-          xr[j][b][0] = a0.x; xr[j][b][1] = a0.y; xr[j][b][2] = a0.z; xr[j][b][3] = a0.w;
-          xr[j][b][4] = a1.x; xr[j][b][5] = a1.y; xr[j][b][6] = a1.z; xr[j][b][7] = a1.w;
+          const float s = wave_sum(acc[b][0] + acc[b][1]);
+          if (lane == 0) part[ul][wave][b] = (c0 == 0 ? 0.f : part[ul][wave][b]) + s;
+        }
+      };
+      RowBuf<SMAX> A, Bf;
+      if (n_mine > 0 && S > 0) load_row<SMAX>(A, raw_p, nib_p, idx_p, tile0(0), S, lane);
+      for (uint32_t ul = 0; ul < n_mine; ul += 2) {
+        float acc[B][2];
+        if (S > 0 && ul + 1 < n_mine) load_row<SMAX>(Bf, raw_p, nib_p, idx_p, tile0(ul + 1), S, lane);
+        row_dot<B, SMAX, CONTIG>(A, S, xr, C, acc);
+        finish(ul, acc);
+        if (ul + 1 < n_mine) {
+          if (S > 0 && ul + 2 < n_mine) load_row<SMAX>(A, raw_p, nib_p, idx_p, tile0(ul + 2), S, lane);
+          row_dot<B, SMAX, CONTIG>(Bf, S, xr, C, acc);
+          finish(ul + 1, acc);
         }
       }
     }
-    for (uint32_t rl = phase; rl < nr; rl += phases) {
-      const uint64_t t0 = (uint64_t)(r0 + rl) * T + tb;
-      u32x4 raw[SMAX];
-      u32x2 nib[SMAX];
-#pragma unroll
-      for (int j = 0; j < SMAX; j++) {
-        if ((uint32_t)j < S) {
-          raw[j] = load_nt(reinterpret_cast<const u32x4*>(raw_p + (t0 + j) * kTile) + lane);
-          nib[j] = load_nt(reinterpret_cast<const u32x2*>(nib_p + (t0 + j) * (kTile / 2)) + lane);
-        }
-      }
-      float acc[B][2];
-#pragma unroll
-      for (int b = 0; b < B; b++) acc[b][0] = acc[b][1] = 0.f;
-#pragma unroll
-      for (int j = 0; j < SMAX; j++) {
-        if ((uint32_t)j < S) {
-          uint32_t first, cnt;
-          tile_escape_range(idx_p, (uint32_t)(t0 + j), G.n_esc, first, cnt);
-          uint32_t E[4];
-          if (contig)
-            exponents16<true>(nib[j], lut, G.base4, E);
-          else
-            exponents16<false>(nib[j], lut, G.base4, E);
-          if (cnt) place_escapes(nib[j], esc_p, first, cnt, esc_lds[wave], E);
-          uint32_t w[8];
-          assemble16(raw[j], E, w);
-          dot16<B>(w, xr[j], acc);
-        }
-      }
-#pragma unroll
-      for (int b = 0; b < B; b++) {
-        const float s = wave_sum(acc[b][0] + acc[b][1]);
-        if (lane == 0) part[slice][rl][b] = (c0 == 0 ? 0.f : part[slice][rl][b]) + s;
-      }
+    __syncthreads();
+    const uint32_t nrow = min(nsub * phases, G.rows - sub * phases);
+    for (uint32_t i = threadIdx.x; i < nrow * B; i += kGemvWaves * kWave) {
+      const uint32_t b = i / nrow, rl = i % nrow;
+      const uint32_t ul = rl / phases, ph = rl % phases;
+      float v = part[ul][ph * nks][b];
+      for (uint32_t s = 1; s < nks; s++) v += part[ul][ph * nks + s][b];
+      const size_t o = (size_t)b * G.rows + (size_t)sub * phases + rl;
+      if (y_bf16)
+        static_cast<uint16_t*>(G.y)[o] = f32_to_bf16_rne(v);
+      else
+        static_cast<float*>(G.y)[o] = v;
     }
-  }
-  __syncthreads();
-  for (uint32_t i = threadIdx.x; i < nr * B; i += kGemvWaves * kWave) {
-    const uint32_t b = i / nr, rl = i % nr;
-    float v = part[0][rl][b];
-    for (uint32_t s = 1; s < nks; s++) v += part[s][rl][b];
-    const size_t o = (size_t)b * G.rows + r0 + rl;
-    if (L.y_bf16)
-      static_cast<uint16_t*>(G.y)[o] = f32_to_bf16_rne(v);
-    else
-      static_cast<float*>(G.y)[o] = v;
+    __syncthreads();
   }
 }
 
 template <int B, int SMAX>
-static hipError_t run(GemvLaunch& L, uint32_t units, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemv<B, SMAX>), dim3(units), dim3(kGemvWaves * kWave), 0, s, L);
+__global__ __launch_bounds__(kGemvWaves * kWave) void k_gemv(GemvLaunch L) {
+  __shared__ float part[kSubUnits][kGemvWaves][B];
+  __shared__ uint8_t esc_sh[kEscShared];
+  __shared__ uint8_t esc_wave[kGemvWaves][kTile];
+  const uint32_t wave = uniform(threadIdx.x >> 6);
+  const int lane = lane_id();
+  // this workgroup's share of the total cost: units whose start cost is in [c_lo, c_hi)
+  const uint64_t c_lo = L.total_cost * blockIdx.x / gridDim.x;
+  const uint64_t c_hi = L.total_cost * (blockIdx.x + 1) / gridDim.x;
+  for (int gi = 0; gi < L.n_groups; gi++) {
+    const GemvGroup& G = L.g[gi];
+    const uint64_t g_lo = G.cost_begin, g_hi = G.cost_begin + (uint64_t)G.n_units * G.unit_cost;
+    if (g_hi <= c_lo) continue;
+    if (g_lo >= c_hi) break;
+    const uint32_t u_lo = c_lo > g_lo ? (uint32_t)((c_lo - g_lo + G.unit_cost - 1) / G.unit_cost) : 0u;
+    const uint32_t u_hi = (uint32_t)min((uint64_t)G.n_units, (c_hi - g_lo + G.unit_cost - 1) / G.unit_cost);
+    if (u_lo >= u_hi) continue;
+    if (G.flags & 1u)
+      run_segment<B, SMAX, true>(G, u_lo, u_hi, L.y_bf16, part, esc_sh, esc_wave[wave], wave, lane);
+    else
+      run_segment<B, SMAX, false>(G, u_lo, u_hi, L.y_bf16, part, esc_sh, esc_wave[wave], wave, lane);
+  }
+}
+
+// Unit geometry of one group: K slices (1, 2 or 4 per row, each at most
+// smax tiles per pass) and row phases (waves per slice, 4 / slices).
+static uint32_t geometry(uint32_t T, uint32_t smax) {
+  uint32_t nks = 1;
+  while (nks < (uint32_t)kGemvWaves && (T + nks - 1) / nks > smax) nks *= 2;
+  return nks | ((kGemvWaves / nks) << 4);
+}
+
+template <int B, int SMAX>
+static hipError_t run(GemvLaunch& L, hipStream_t s) {
+  static int per_cu = 0, cus = 0;
+  if (!per_cu) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return hipErrorUnknown;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_gemv<B, SMAX>, kGemvWaves * kWave, 0) != hipSuccess || n < 1)
+      n = 1;
+    per_cu = n;
+  }
+  uint64_t units = 0;
+  for (int g = 0; g < L.n_groups; g++) units += L.g[g].n_units;
+  const uint64_t grid = std::min<uint64_t>((uint64_t)per_cu * cus, units);
+  hipLaunchKernelGGL((k_gemv<B, SMAX>), dim3((unsigned)grid), dim3(kGemvWaves * kWave), 0, s, L);
   return hipGetLastError();
 }
 
-// Unit geometry of one group for a given SMAX: K slices (1, 2 or 4), row
-// phases (waves per slice) and rows per unit (a multiple of the phases, about
-// kUnitTiles tiles of weights in total, at most kMaxUnitRows).
-static uint32_t geometry(uint32_t rows, uint32_t T, uint32_t smax) {
-  uint32_t nks = 1;
-  while (nks < 4 && (T + nks - 1) / nks > smax) nks *= 2;
-  const uint32_t phases = kGemvWaves / nks;
-  uint32_t rb = kUnitTiles / T;
-  rb = rb / phases * phases;
-  if (rb < phases) rb = phases;
-  if (rb > kMaxUnitRows) rb = kMaxUnitRows;
-  if (rb > rows) rb = (rows + phases - 1) / phases * phases;
-  if (rb > kMaxUnitRows) rb = kMaxUnitRows;
-  return rb | (nks << 16) | (phases << 20);
-}
-
 hipError_t launch_gemv(const GemvGroup* groups, int n_groups, int batch, int y_dtype, hipStream_t s) {
-  static const int smax_of[9] = {0, 8, 4, 2, 2, 1, 1, 1, 1};
-  const int smax = smax_of[batch];
+  static const int smax_of[9] = {0, 4, 4, 2, 2, 1, 1, 1, 1};
+  const uint32_t smax = (uint32_t)smax_of[batch];
   GemvLaunch L;
   L.n_groups = n_groups;
   L.y_bf16 = y_dtype == LBF_BF16;
-  uint32_t units = 0;
+  uint64_t cost = 0;
   for (int g = 0; g < n_groups; g++) {
-    L.g[g] = groups[g];
-    const uint32_t geom = geometry(groups[g].rows, groups[g].cols >> 10, (uint32_t)smax);
-    L.g[g].geom = geom;
-    L.g[g].unit_begin = units;
-    const uint32_t rb = geom & 0xFFFFu;
-    units += (groups[g].rows + rb - 1) / rb;
+    GemvGroup G = groups[g];
+    const uint32_t T = G.cols >> 10;
+    G.geom = geometry(T, smax);
+    const uint32_t phases = (G.geom >> 4) & 0xFu;
+    G.n_units = (G.rows + phases - 1) / phases;
+    // cost of a tile in 1/16 units: 16 plus the escape work, ~1/8 per escape
+    const uint64_t n_tiles = (uint64_t)G.rows * T;
+    const uint32_t esc_per_tile = (uint32_t)std::min<uint64_t>(1024, (G.n_esc + n_tiles - 1) / n_tiles);
+    G.unit_cost = phases * T * (16u + esc_per_tile / 8u);
+    G.cost_begin = cost;
+    cost += (uint64_t)G.n_units * G.unit_cost;
+    L.g[g] = G;
   }
+  L.total_cost = cost;
   switch (batch) {
-    case 1: return run<1, 8>(L, units, s);
-    case 2: return run<2, 4>(L, units, s);
-    case 3: return run<3, 2>(L, units, s);
-    case 4: return run<4, 2>(L, units, s);
-    case 5: return run<5, 1>(L, units, s);
-    case 6: return run<6, 1>(L, units, s);
-    case 7: return run<7, 1>(L, units, s);
-    default: return run<8, 1>(L, units, s);
+    case 1: return run<1, 4>(L, s);
+    case 2: return run<2, 4>(L, s);
+    case 3: return run<3, 2>(L, s);
+    case 4: return run<4, 2>(L, s);
+    case 5: return run<5, 1>(L, s);
+    case 6: return run<6, 1>(L, s);
+    case 7: return run<7, 1>(L, s);
+    default: return run<8, 1>(L, s);
   }
 }
 

@@ -36,12 +36,13 @@ struct GemvGroup {
   const uint16_t* x;
   void* y;
   uint32_t rows, cols, n_esc;
-  uint32_t unit_begin;  // first work unit of this group
+  uint32_t flags;  // bit 0: contiguous table (lut[c] = lut[0] + c)
   uint32_t lut[4];
-  uint32_t base4;
-  uint32_t flags;  // bit 0: contiguous table
-  uint32_t geom;   // filled by the launcher: rows per unit | slices << 16 | row phases << 20
-  uint32_t pad;
+  uint32_t base4;       // lut[0] * 0x01010101
+  uint32_t geom;        // set by the launcher: K slices (bits 0..3) | row phases (bits 4..7)
+  uint64_t cost_begin;  // set by the launcher: cost of all earlier groups' units
+  uint32_t unit_cost;   // set by the launcher: cost of one unit of this group
+  uint32_t n_units;     // set by the launcher
 };
 hipError_t launch_gemv(const GemvGroup* groups, int n_groups, int batch, int y_dtype, hipStream_t s);
 hipError_t launch_gemm(const GemvGroup* groups, int n_groups, int batch, int y_dtype, hipStream_t s);

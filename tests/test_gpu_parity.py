@@ -238,3 +238,47 @@ def test_gemv_experts_grouped(env):
         check_product(ys[e], y_ref, a_ref, False)
     for e in (4, 62, 63):
         assert np.array_equal(host(lbf.decode(blobs[e])), Ws[e]), e
+
+
+@pytest.mark.parametrize("rows,cols,batch", [(1, 1024, 1), (5, 3072, 2), (7, 14336, 8), (33, 5120, 3),
+                                             (130, 2048, 4), (3, 30720, 1)])
+def test_gemv_odd_shapes(env, rows, cols, batch):
+    torch, lbf = env
+    rng = np.random.default_rng([5, rows, cols])
+    W = synth.gaussian(rng, rows, cols, 0.03, 0.003, 80.0)
+    x = synth.activations(rng, batch, cols)
+    say("gemv odd shape %dx%d B=%d" % (rows, cols, batch))
+    blob = lbf.from_host_blob(O.encode(W))
+    y_ref, a_ref = O.matvec(W, x)
+    guard = 256
+    buf = torch.full((batch * rows + 2 * guard,), 7.0, dtype=torch.float32, device="cuda")
+    y = buf[guard:guard + batch * rows].view(batch, rows)
+    lbf.gemv(blob, dev(torch, x), lbf.LBF_F32, outs=y)
+    torch.cuda.synchronize()
+    check_product(y, y_ref, a_ref, False)
+    h = buf.cpu().numpy()
+    assert (h[:guard] == 7.0).all() and (h[guard + batch * rows:] == 7.0).all()
+
+
+def test_gemv_many_groups_mixed_shapes(env):
+    """More groups than one launch takes, with mixed shapes and both table kinds."""
+    torch, lbf = env
+    rng = np.random.default_rng(77)
+    Ws, xs = [], []
+    for g in range(40):
+        rows = int(rng.integers(1, 300))
+        cols = 1024 * int(rng.integers(1, 9))
+        if g % 3 == 0:
+            W = synth.gaussian(rng, rows, cols, 0.02, 0.002, 100.0)
+        elif g % 3 == 1:
+            W = synth.laplace(rng, rows, cols, 0.05)
+        else:
+            W = synth.all_patterns(rows, cols)
+        Ws.append(W)
+        xs.append(synth.activations(rng, 2, cols))
+    blobs = [lbf.from_host_blob(O.encode(W)) for W in Ws]
+    ys = lbf.gemv(blobs, [dev(torch, x) for x in xs], lbf.LBF_F32)
+    torch.cuda.synchronize()
+    for W, x, y in zip(Ws, xs, ys):
+        y_ref, a_ref = O.matvec(W, x)
+        check_product(y, y_ref, a_ref, False)
