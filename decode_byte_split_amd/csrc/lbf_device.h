@@ -11,10 +11,12 @@
 // prove?" (fixed short codes for frequent exponents, exact escape stream).
 //
 // Lane work unit: 16 consecutive weights of a 1024-weight tile, i.e. one
-// 16-byte raw load (4 words, 4 weights each) and one 8-byte nibble load
-// (2 words, 8 codes each).  Decoded weights leave as 8 packed bf16 pairs,
-// pair j = weights (2j, 2j+1), low half first: the operand layout of
-// v_dot2_f32_bf16 and of memory.
+// 16-byte raw load (4 words: weights 4q .. 4q+3 in word q) and one 8-byte
+// nibble load (word 0: weights 0..7, word 1: weights 8..15; in each word,
+// byte j holds weight j in its low nibble and weight 4 + j in its high one).
+// The raw byte of weight i is mantissa_i << 1 | sign of its partner i ^ 1.
+// Decoded weights leave as 8 packed bf16 pairs, pair p = weights (2p, 2p+1),
+// low half first: the operand layout of v_dot2_f32_bf16 and of memory.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -51,9 +53,8 @@ __device__ __forceinline__ uint32_t lut_lookup(uint32_t c, const Lut& L) {
   return (lo & keep_lo) | (hi & ~keep_lo);
 }
 
-// Exponent bytes of a lane's 16 weights from its two nibble words.
-//   E[0] = weights 0,2,4,6   E[1] = weights 1,3,5,7
-//   E[2] = weights 8,...,14  E[3] = weights 9,...,15   (byte j = j-th of them)
+// Exponent bytes of a lane's 16 weights from its two nibble words:
+// E[q] byte j = exponent of weight 4q + j.
 // CONTIG: the table is lut[c] = lut[0] + c (the common case for trained
 // weights), so a byte-wise add replaces the lookup; `base4` = lut[0] * 0x01010101.
 template <bool CONTIG>
@@ -67,26 +68,27 @@ __device__ __forceinline__ void exponents16(u32x2 nib, const Lut& L, uint32_t ba
   for (int q = 0; q < 4; q++) E[q] = CONTIG ? c[q] + base4 : lut_lookup(c[q], L);
 }
 
-// Rebuild 8 bf16 pairs: w = (sign << 15) | (exponent << 7) | mantissa.
-// The raw byte is duplicated into both bytes of its 16-bit half, masked to
-// keep bit 15 (sign) and bits 6..0 (mantissa); the exponent bytes are moved
-// to bits 7..14 of each half.
+// Rebuild 8 bf16 pairs.  For weights a = 2p, b = 2p + 1 one v_perm_b32 forms
+// the word [raw_a, e_a, raw_b, e_b] (low byte first); rotating it right by
+// one bit puts mantissa_a in bits 0..6, e_a in 7..14, sign_a (bit 0 of
+// raw_b) in bit 15, mantissa_b in 16..22, e_b in 23..30 and sign_b (bit 0 of
+// raw_a) in bit 31: exactly the two bf16 values.
 __device__ __forceinline__ void assemble16(u32x4 raw, const uint32_t E[4], uint32_t w[8]) {
   const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-  for (int j = 0; j < 8; j++) {
-    const int g = j >> 2, jj = j & 3;
-    uint32_t f = perm(E[2 * g + 1], E[2 * g], 0x0C000C00u | (uint32_t)jj | ((uint32_t)(4 + jj) << 16)) << 7;
-    const uint32_t b = (uint32_t)(j & 1) * 2u;
-    uint32_t r = perm(rw[j >> 1], rw[j >> 1], b | (b << 8) | ((b + 1) << 16) | ((b + 1) << 24));
-    w[j] = (r & 0x807F807Fu) | f;
+  for (int p = 0; p < 8; p++) {
+    const uint32_t v = perm(E[p >> 1], rw[p >> 1], (p & 1) ? 0x07030602u : 0x05010400u);
+    w[p] = __builtin_amdgcn_alignbit(v, v, 1u);
   }
 }
 
-// Bit 4i set iff nibble i of `n` is 15 (the escape code).
-__device__ __forceinline__ uint32_t escape_bits(uint32_t n) {
+// Escape flags of the 8 weights of one nibble word, in weight order: bit 8i
+// is set iff weight i's code is 15.
+__device__ __forceinline__ uint64_t escape_mask8(uint32_t n) {
   uint32_t t = n & (n >> 2);
-  return t & (t >> 1) & 0x11111111u;
+  t &= t >> 1;  // bit 4k: all four bits of nibble k are set
+  const uint32_t lo = t & 0x01010101u, hi = (t >> 4) & 0x01010101u;
+  return (uint64_t)lo | ((uint64_t)hi << 32);
 }
 
 __device__ __forceinline__ int lane_id() { return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
@@ -107,21 +109,21 @@ __device__ __forceinline__ uint32_t wave_excl_scan_small(uint32_t v) {
 
 // Overwrite the exponent byte of weight i (0..15) in the E[] layout above.
 __device__ __forceinline__ void patch_exponent(uint32_t E[4], uint32_t i, uint32_t e) {
-  const uint32_t word = ((i >> 3) << 1) | (i & 1u);
-  const uint32_t sh = ((i & 7u) >> 1) * 8u;
+  const uint32_t word = i >> 2;
+  const uint32_t sh = (i & 3u) * 8u;
   const uint32_t m = 0xFFu << sh, v = e << sh;
 #pragma unroll
   for (uint32_t q = 0; q < 4; q++) E[q] = (word == q) ? ((E[q] & ~m) | v) : E[q];
 }
 
 // Escapes of one tile, one wave (all 64 lanes must call): which of the lane's
-// 16 weights escape (bit 4i of m0 / m1 for weight i / 8 + i) and how many
+// 16 weights escape (bit 8i of m0 / m1 for weight i / 8 + i) and how many
 // escapes of the tile precede the lane's first one.  When no lane holds more
 // than one escape a single ballot gives the rank.
-__device__ __forceinline__ uint32_t escape_rank(u32x2 nib, uint32_t& m0, uint32_t& m1) {
-  m0 = escape_bits(nib.x);
-  m1 = escape_bits(nib.y);
-  const uint32_t k = (uint32_t)(__builtin_popcount(m0) + __builtin_popcount(m1));
+__device__ __forceinline__ uint32_t escape_rank(u32x2 nib, uint64_t& m0, uint64_t& m1) {
+  m0 = escape_mask8(nib.x);
+  m1 = escape_mask8(nib.y);
+  const uint32_t k = (uint32_t)(__builtin_popcountll(m0) + __builtin_popcountll(m1));
   if (__builtin_amdgcn_ballot_w64(k > 1u) == 0) return ballot_rank(__builtin_amdgcn_ballot_w64(k != 0u));
   return wave_excl_scan_small(k);
 }
@@ -129,16 +131,16 @@ __device__ __forceinline__ uint32_t escape_rank(u32x2 nib, uint32_t& m0, uint32_
 // Patch the lane's escaped exponents, in element order, from src[j ...],
 // a byte array in LDS holding the tile's escapes; reads at or past cnt (a
 // corrupt blob) yield exponent 0 and touch nothing outside src[0, cnt).
-__device__ __forceinline__ void patch_escapes(const uint8_t* src, uint32_t j, uint32_t cnt, uint32_t m0, uint32_t m1,
+__device__ __forceinline__ void patch_escapes(const uint8_t* src, uint32_t j, uint32_t cnt, uint64_t m0, uint64_t m1,
                                               uint32_t E[4]) {
   while (m0) {
-    const uint32_t i = (uint32_t)__builtin_ctz(m0) >> 2;
+    const uint32_t i = (uint32_t)__builtin_ctzll(m0) >> 3;
     patch_exponent(E, i, j < cnt ? src[j] : 0u);
     m0 &= m0 - 1;
     j++;
   }
   while (m1) {
-    const uint32_t i = 8u + ((uint32_t)__builtin_ctz(m1) >> 2);
+    const uint32_t i = 8u + ((uint32_t)__builtin_ctzll(m1) >> 3);
     patch_exponent(E, i, j < cnt ? src[j] : 0u);
     m1 &= m1 - 1;
     j++;
@@ -160,7 +162,7 @@ __device__ __forceinline__ void place_escapes(u32x2 nib, const uint8_t* __restri
   const int lane = lane_id();
   for (uint32_t p = (uint32_t)lane; p < cnt; p += kWave) lds_slot[p] = esc[first + p];
   wave_lds_sync();
-  uint32_t m0, m1;
+  uint64_t m0, m1;
   const uint32_t j = escape_rank(nib, m0, m1);
   patch_escapes(lds_slot, j, cnt, m0, m1, E);
   wave_lds_sync();  // the slot is rewritten for the next tile

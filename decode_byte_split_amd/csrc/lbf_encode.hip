@@ -95,17 +95,20 @@ __device__ __forceinline__ void lane_fields(const uint16_t* __restrict__ w, uint
       h[q] = lo | (hi << 16);
     }
   }
+  // raw byte of weight i: mantissa_i << 1 | sign of partner i ^ 1;
+  // code of weight i: nibble word i >> 3, byte i & 3, high nibble if bit 2 of i
   raw[0] = raw[1] = raw[2] = raw[3] = 0u;
   code[0] = code[1] = 0u;
   esc_mask = 0u;
 #pragma unroll
   for (int i = 0; i < 16; i++) {
     const uint32_t v = (h[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+    const uint32_t partner = (h[i >> 1] >> (16 * ((i & 1) ^ 1))) & 0xFFFFu;
     const bool valid = e0 + (uint64_t)i < n;
-    const uint32_t r = ((v >> 8) & 0x80u) | (v & 0x7Fu);
+    const uint32_t r = ((v & 0x7Fu) << 1) | (partner >> 15);
     const uint32_t c = valid ? (uint32_t)inv[(v >> 7) & 0xFFu] : 0u;
-    raw[i >> 2] |= (valid ? r : 0u) << (8 * (i & 3));
-    code[i >> 3] |= c << (4 * (i & 7));
+    raw[i >> 2] |= r << (8 * (i & 3));
+    code[i >> 3] |= c << (8 * (i & 3) + 4 * ((i >> 2) & 1));
     if (c == 15u) esc_mask |= 1u << i;
   }
 }

@@ -36,7 +36,7 @@
 namespace lbf {
 
 constexpr int kGemvWaves = 4;
-constexpr int kSubUnits = 32;     // units whose partial sums share one LDS batch
+constexpr int kSubUnits = 64;     // units whose partial sums share one LDS batch
 constexpr int kEscShared = 8192;  // escape bytes a workgroup preloads per tensor range
 
 struct GemvLaunch {
@@ -77,27 +77,31 @@ __device__ __forceinline__ void dot16(const uint32_t w[8], const uint32_t (*xr)[
   }
 }
 
-// One row's coded data for one wave's K slice.
+// One row's coded data for one wave's K slice.  The tile index travels with
+// the data as a vector load (lane j holds idx[t0 + j]), so that waiting for
+// it never waits on LDS traffic (scalar loads share LDS's wait counter).
 template <int SMAX>
 struct RowBuf {
   u32x4 raw[SMAX];
   u32x2 nib[SMAX];
-  uint32_t ix[SMAX + 1];  // escape index of the S tiles (and the next one)
+  uint32_t ixv;
 };
 
+// Loads are never conditional: a tile past the slice end (S < SMAX) reloads
+// the slice's last tile, and the prefetch after a wave's last row reloads
+// that row.  The redundant requests hit cache; in exchange the compiler can
+// count outstanding loads exactly and keeps the next row in flight while the
+// current one is decoded.
 template <int SMAX>
 __device__ __forceinline__ void load_row(RowBuf<SMAX>& R, const uint8_t* raw_p, const uint8_t* nib_p,
                                          const uint32_t* idx_p, uint64_t t0, uint32_t S, int lane) {
 #pragma unroll
   for (int j = 0; j < SMAX; j++) {
-    if ((uint32_t)j < S) {
-      R.raw[j] = load_nt(reinterpret_cast<const u32x4*>(raw_p + (t0 + j) * kTile) + lane);
-      R.nib[j] = load_nt(reinterpret_cast<const u32x2*>(nib_p + (t0 + j) * (kTile / 2)) + lane);
-    }
+    const uint64_t t = t0 + min((uint32_t)j, S - 1);
+    R.raw[j] = load_nt(reinterpret_cast<const u32x4*>(raw_p + t * kTile) + lane);
+    R.nib[j] = load_nt(reinterpret_cast<const u32x2*>(nib_p + t * (kTile / 2)) + lane);
   }
-#pragma unroll
-  for (int j = 0; j <= SMAX; j++)
-    if ((uint32_t)j <= S) R.ix[j] = idx_p[t0 + j];
+  R.ixv = idx_p[t0 + min((uint32_t)lane, S)];
 }
 
 struct SegCtx {
@@ -105,12 +109,13 @@ struct SegCtx {
   const uint8_t* esc_sh; // LDS copy of escapes [e_lo, e_hi) when preloaded
   uint8_t* esc_wave;     // this wave's 1 KiB staging slot otherwise
   uint32_t e_lo, e_hi;   // escape range of the workgroup's rows (clamped)
-  bool preload;
   Lut lut;
   uint32_t base4;
 };
 
-template <int B, int SMAX, bool CONTIG>
+// PRELOAD: the segment's escapes sit in LDS (the common case).  Otherwise
+// (dense escapes) each tile's slice is staged from memory when needed.
+template <int B, int SMAX, bool CONTIG, bool PRELOAD>
 __device__ __forceinline__ void row_dot(const RowBuf<SMAX>& R, uint32_t S, const uint32_t (*xr)[B][8],
                                         const SegCtx& C, float acc[B][2]) {
 #pragma unroll
@@ -122,12 +127,14 @@ __device__ __forceinline__ void row_dot(const RowBuf<SMAX>& R, uint32_t S, const
       exponents16<CONTIG>(R.nib[j], C.lut, C.base4, E);
       // clamp the index into the range this workgroup knows, so a corrupt
       // blob can only give wrong values, never an out-of-range access
-      const uint32_t a = min(max(R.ix[j], C.e_lo), C.e_hi);
-      const uint32_t e = min(max(R.ix[j + 1], a), C.e_hi);
+      const uint32_t ia = (uint32_t)__builtin_amdgcn_readlane((int)R.ixv, j);
+      const uint32_t ib = (uint32_t)__builtin_amdgcn_readlane((int)R.ixv, j + 1);
+      const uint32_t a = min(max(ia, C.e_lo), C.e_hi);
+      const uint32_t e = min(max(ib, a), C.e_hi);
       const uint32_t cnt = min(e - a, (uint32_t)kTile);
       if (cnt) {
-        if (C.preload) {
-          uint32_t m0, m1;
+        if (PRELOAD) {
+          uint64_t m0, m1;
           const uint32_t r = escape_rank(R.nib[j], m0, m1);
           patch_escapes(C.esc_sh + (a - C.e_lo), r, cnt, m0, m1, E);
         } else {
@@ -138,6 +145,34 @@ __device__ __forceinline__ void row_dot(const RowBuf<SMAX>& R, uint32_t S, const
       assemble16(R.raw[j], E, w);
       dot16<B>(w, xr[j], acc);
     }
+  }
+}
+
+// The rows of one pass (one K chunk of one batch of units) for one wave.
+template <int B, int SMAX, bool CONTIG, bool PRELOAD>
+__device__ __forceinline__ void run_rows(RowBuf<SMAX>& A, const uint8_t* raw_p, const uint8_t* nib_p,
+                                         const uint32_t* idx_p, uint64_t row_tile0, uint64_t row_stride,
+                                         uint32_t n_mine, uint32_t S, const uint32_t (*xr)[B][8], const SegCtx& C,
+                                         float (*part)[kGemvWaves][B], uint32_t wave, bool accumulate, int lane) {
+  RowBuf<SMAX> Bf;
+  auto finish = [&](uint32_t ul, float acc[B][2]) {
+#pragma unroll
+    for (int b = 0; b < B; b++) {
+      const float s = wave_sum(acc[b][0] + acc[b][1]);
+      if (lane == 0) part[ul][wave][b] = (accumulate ? part[ul][wave][b] : 0.f) + s;
+    }
+  };
+  const uint32_t last = n_mine - 1;
+  for (uint32_t ul = 0;; ul += 2) {
+    float acc[B][2];
+    load_row<SMAX>(Bf, raw_p, nib_p, idx_p, row_tile0 + (uint64_t)min(ul + 1, last) * row_stride, S, lane);
+    row_dot<B, SMAX, CONTIG, PRELOAD>(A, S, xr, C, acc);
+    finish(ul, acc);
+    if (ul + 1 > last) break;
+    load_row<SMAX>(A, raw_p, nib_p, idx_p, row_tile0 + (uint64_t)min(ul + 2, last) * row_stride, S, lane);
+    row_dot<B, SMAX, CONTIG, PRELOAD>(Bf, S, xr, C, acc);
+    finish(ul + 1, acc);
+    if (ul + 2 > last) break;
   }
 }
 
@@ -163,60 +198,61 @@ __device__ __forceinline__ void run_segment(const GemvGroup& G, uint32_t u_lo, u
   C.esc_wave = esc_wave;
   C.lut = Lut{G.lut[0], G.lut[1], G.lut[2], G.lut[3]};
   C.base4 = G.base4;
-  C.e_hi = min(idx_p[(uint64_t)r_hi * T], G.n_esc);
-  C.e_lo = min(idx_p[(uint64_t)r_lo * T], C.e_hi);
-  C.preload = C.e_hi - C.e_lo <= (uint32_t)kEscShared;
-  if (!C.preload) {  // dense escapes: per-tile staging, bounded by the stream itself
-    C.e_lo = 0;
-    C.e_hi = G.n_esc;
-  }
+  // escape range of the whole segment (scalar loads, waited for only after
+  // the first row's loads are on their way)
+  const uint32_t seg_hi = idx_p[(uint64_t)r_hi * T];
+  const uint32_t seg_lo = idx_p[(uint64_t)r_lo * T];
   __syncthreads();  // the previous segment is done with esc_sh and part
-  if (C.preload)
-    for (uint32_t p = threadIdx.x; p < C.e_hi - C.e_lo; p += kGemvWaves * kWave) esc_sh[p] = esc_p[C.e_lo + p];
-  __syncthreads();
 
+  bool first = true, preload = true;
   for (uint32_t sub = u_lo; sub < u_hi; sub += kSubUnits) {
     const uint32_t nsub = min((uint32_t)kSubUnits, u_hi - sub);
     for (uint32_t c0 = 0; c0 < T; c0 += nks * SMAX) {
+      // this wave's K slice: tiles [tb, tb + S) of each row (S = 0: the
+      // slice is past the row's end; loads then use the row's last tile)
       const uint32_t tb = c0 + slice * SMAX;
       const uint32_t S = tb < T ? min((uint32_t)SMAX, T - tb) : 0u;
+      const uint32_t tl = tb < T ? tb : T - 1;
+      const uint32_t SL = S ? S : 1u;
+      // this wave's rows: r(ul) = (sub + ul) * phases + phase, ul < n_mine
+      uint32_t n_mine = 0;
+      while (n_mine < nsub && (sub + n_mine) * phases + phase < G.rows) n_mine++;
+      const uint64_t row_tile0 = (uint64_t)(sub * phases + phase) * T + tl;
+      const uint64_t row_stride = (uint64_t)phases * T;
+      RowBuf<SMAX> A;
+      if (n_mine) load_row<SMAX>(A, raw_p, nib_p, idx_p, row_tile0, SL, lane);
       uint32_t xr[SMAX][B][8];
 #pragma unroll
       for (int j = 0; j < SMAX; j++) {
-        if ((uint32_t)j < S) {
-#pragma unroll
-          for (int b = 0; b < B; b++) {
-            const u32x4* xp =
-                reinterpret_cast<const u32x4*>(G.x + (size_t)b * G.cols + (size_t)(tb + j) * kTile) + lane * 2;
-            const u32x4 a0 = xp[0], a1 = xp[1];
-            xr[j][b][0] = a0.x; xr[j][b][1] = a0.y; xr[j][b][2] = a0.z; xr[j][b][3] = a0.w;
-            xr[j][b][4] = a1.x; xr[j][b][5] = a1.y; xr[j][b][6] = a1.z; xr[j][b][7] = a1.w;
-          }
-        }
-      }
-      // this wave's rows: r(ul) = (sub + ul) * phases + phase, ul < nsub, r < rows
-      uint32_t n_mine = 0;
-      while (n_mine < nsub && (sub + n_mine) * phases + phase < G.rows) n_mine++;
-      auto tile0 = [&](uint32_t ul) { return (uint64_t)((sub + ul) * phases + phase) * T + tb; };
-      auto finish = [&](uint32_t ul, float acc[B][2]) {
+        const uint32_t tj = tl + min((uint32_t)j, SL - 1);
 #pragma unroll
         for (int b = 0; b < B; b++) {
-          const float s = wave_sum(acc[b][0] + acc[b][1]);
-          if (lane == 0) part[ul][wave][b] = (c0 == 0 ? 0.f : part[ul][wave][b]) + s;
+          const u32x4* xp = reinterpret_cast<const u32x4*>(G.x + (size_t)b * G.cols + (size_t)tj * kTile) + lane * 2;
+          const u32x4 a0 = xp[0], a1 = xp[1];
+          xr[j][b][0] = a0.x; xr[j][b][1] = a0.y; xr[j][b][2] = a0.z; xr[j][b][3] = a0.w;
+          xr[j][b][4] = a1.x; xr[j][b][5] = a1.y; xr[j][b][6] = a1.z; xr[j][b][7] = a1.w;
         }
-      };
-      RowBuf<SMAX> A, Bf;
-      if (n_mine > 0 && S > 0) load_row<SMAX>(A, raw_p, nib_p, idx_p, tile0(0), S, lane);
-      for (uint32_t ul = 0; ul < n_mine; ul += 2) {
-        float acc[B][2];
-        if (S > 0 && ul + 1 < n_mine) load_row<SMAX>(Bf, raw_p, nib_p, idx_p, tile0(ul + 1), S, lane);
-        row_dot<B, SMAX, CONTIG>(A, S, xr, C, acc);
-        finish(ul, acc);
-        if (ul + 1 < n_mine) {
-          if (S > 0 && ul + 2 < n_mine) load_row<SMAX>(A, raw_p, nib_p, idx_p, tile0(ul + 2), S, lane);
-          row_dot<B, SMAX, CONTIG>(Bf, S, xr, C, acc);
-          finish(ul + 1, acc);
+      }
+      if (first) {  // uniform across the workgroup: preload the segment's escapes
+        first = false;
+        C.e_hi = min(seg_hi, G.n_esc);
+        C.e_lo = min(seg_lo, C.e_hi);
+        preload = C.e_hi - C.e_lo <= (uint32_t)kEscShared;
+        if (!preload) {  // dense escapes: per-tile staging, bounded by the stream itself
+          C.e_lo = 0;
+          C.e_hi = G.n_esc;
+        } else {
+          for (uint32_t p = threadIdx.x; p < C.e_hi - C.e_lo; p += kGemvWaves * kWave) esc_sh[p] = esc_p[C.e_lo + p];
         }
+        __syncthreads();
+      }
+      if (n_mine) {
+        if (preload)
+          run_rows<B, SMAX, CONTIG, true>(A, raw_p, nib_p, idx_p, row_tile0, row_stride, n_mine, S, xr, C, part, wave,
+                                          c0 != 0, lane);
+        else
+          run_rows<B, SMAX, CONTIG, false>(A, raw_p, nib_p, idx_p, row_tile0, row_stride, n_mine, S, xr, C, part,
+                                           wave, c0 != 0, lane);
       }
     }
     __syncthreads();

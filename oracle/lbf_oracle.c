@@ -23,21 +23,25 @@
  *    lower bound for any code that stores each weight independently.
  *
  * Readings taken where the pages are silent (each is listed in the design doc):
- *  - only the 8-bit exponent is coded; sign and mantissa stay in one raw byte
- *    (sign in bit 7, mantissa in bits 6..0);
+ *  - only the 8-bit exponent is coded; sign and mantissa stay in the raw
+ *    plane, one byte per weight: weight i's byte holds its mantissa in bits
+ *    7..1 and, in bit 0, the sign of its pair partner i ^ 1 (weights pair up
+ *    as 2j, 2j+1; a missing partner past the end counts as +0.0);
  *  - the alphabet is the 15 most frequent exponents (count descending, ties to
  *    the smaller exponent); codes 0..n_codes-1 go to them in ascending
  *    exponent order; code 15 means "escape";
  *  - an escape stores the full 8-bit exponent as one byte, in flat element
  *    order; tiles are 1024 consecutive weights and a uint32 prefix-sum index
  *    idx[t] gives where tile t's escapes start (idx[n_t] = number of escapes);
- *  - element i's code is nibble (i & 1) of nibble-plane byte i >> 1 (low
- *    nibble for even i).
+ *  - codes go in groups of 8 weights, one 4-byte word per group: weight
+ *    8g + j (j = 0..3) has the low nibble and weight 8g + 4 + j the high
+ *    nibble of nibble-plane byte 4g + j.
  *
  * Blob layout (format v1), all integers little-endian:
  *   [0,256)             header (see put_header)
- *   [off_raw, ...)      raw plane: n bytes, zero padded to n_t*1024
- *   [off_nib, ...)      nibble plane: ceil(n/2) bytes, zero padded to n_t*512
+ *   [off_raw, ...)      raw plane: n bytes, padded to n_t*1024 (padding weights
+ *                       are +0.0 with code 0; byte n carries sign n-1 if n is odd)
+ *   [off_nib, ...)      nibble plane: n_t*512 bytes (codes of padding are 0)
  *   [off_idx, ...)      idx plane: uint32[n_t + 1]
  *   [off_esc, ...)      escape stream: n_esc bytes
  * Every plane starts at a multiple of 256 and blob_bytes is a multiple of 256.
@@ -123,6 +127,10 @@ void lbfo_code_table(const uint64_t hist[256], uint8_t lut[16], uint8_t* n_codes
     if (taken[e]) lut[c++] = (uint8_t)e;
   *n_codes = (uint8_t)chosen;
 }
+
+/* where weight i's 4-bit code lives: byte of the nibble plane and shift */
+static uint64_t code_byte(uint64_t i) { return (i / 8) * 4 + (i % 4); }
+static unsigned code_shift(uint64_t i) { return (unsigned)((i % 8) / 4) * 4u; }
 
 /* the code an exponent gets: its slot in the table, or 15 (escape) */
 static unsigned code_of(unsigned e, const uint8_t lut[16], unsigned n_codes) {
@@ -213,9 +221,10 @@ int lbfo_encode(const uint16_t* w, uint64_t rows, uint64_t cols, uint8_t* blob, 
   uint64_t written = 0;
   for (uint64_t i = 0; i < L.n; i++) {
     unsigned s = sign_of(w[i]), e = exponent_of(w[i]), m = mantissa_of(w[i]);
-    raw[i] = (uint8_t)((s << 7) | m);
+    raw[i] |= (uint8_t)(m << 1);
+    raw[i ^ 1u] |= (uint8_t)s; /* the partner's byte carries this sign */
     unsigned code = code_of(e, lut, n_codes);
-    nib[i >> 1] |= (uint8_t)(code << (4u * (unsigned)(i & 1u)));
+    nib[code_byte(i)] |= (uint8_t)(code << code_shift(i));
     if (code == 15u) {
       esc[written++] = (uint8_t)e; /* flat element order */
       tile_escapes[i / TILE]++;
@@ -276,7 +285,7 @@ int lbfo_decode(const uint8_t* blob, uint64_t blob_len, uint16_t* out, uint64_t 
     uint64_t seen = 0; /* escapes met so far inside this tile */
     uint64_t end = (t + 1) * TILE < L.n ? (t + 1) * TILE : L.n;
     for (uint64_t i = t * TILE; i < end; i++) {
-      unsigned code = (nib[i >> 1] >> (4u * (unsigned)(i & 1u))) & 15u;
+      unsigned code = (nib[code_byte(i)] >> code_shift(i)) & 15u;
       unsigned e;
       if (code == 15u) {
         if (first + seen >= last) return -3;
@@ -286,7 +295,7 @@ int lbfo_decode(const uint8_t* blob, uint64_t blob_len, uint16_t* out, uint64_t 
         if (code >= n_codes) return -3;
         e = lut[code];
       }
-      unsigned s = raw[i] >> 7, m = raw[i] & 0x7Fu;
+      unsigned s = raw[i ^ 1u] & 1u, m = raw[i] >> 1;
       out[i] = (uint16_t)((s << 15) | (e << 7) | m);
     }
     if (first + seen != last) return -3;
