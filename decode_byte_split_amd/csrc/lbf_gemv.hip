@@ -87,21 +87,32 @@ struct RowBuf {
   uint32_t ixv;
 };
 
-// Loads are never conditional: a tile past the slice end (S < SMAX) reloads
-// the slice's last tile, and the prefetch after a wave's last row reloads
-// that row.  The redundant requests hit cache; in exchange the compiler can
-// count outstanding loads exactly and keeps the next row in flight while the
-// current one is decoded.
+// Row loads are raw buffer loads: a descriptor per plane and row (built in
+// scalar registers), a per-lane offset fixed for the whole kernel and the
+// tile as an immediate offset.  They are never conditional (a tile past the
+// slice end lies outside the descriptor's range and reads as zeros without a
+// memory access) and need no per-row vector address arithmetic, so the
+// compiler counts outstanding loads exactly and keeps the next row in flight
+// while the current one is decoded.
+constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer access on gfx9
+constexpr int kNonTemporal = 2;         // cache policy: streaming
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
 template <int SMAX>
 __device__ __forceinline__ void load_row(RowBuf<SMAX>& R, const uint8_t* raw_p, const uint8_t* nib_p,
                                          const uint32_t* idx_p, uint64_t t0, uint32_t S, int lane) {
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(raw_p + t0 * kTile, S * kTile);
+  const __amdgpu_buffer_rsrc_t rn = make_rsrc(nib_p + t0 * (kTile / 2), S * (kTile / 2));
+  const __amdgpu_buffer_rsrc_t ri = make_rsrc(idx_p + t0, (S + 1) * 4);
 #pragma unroll
   for (int j = 0; j < SMAX; j++) {
-    const uint64_t t = t0 + min((uint32_t)j, S - 1);
-    R.raw[j] = load_nt(reinterpret_cast<const u32x4*>(raw_p + t * kTile) + lane);
-    R.nib[j] = load_nt(reinterpret_cast<const u32x2*>(nib_p + t * (kTile / 2)) + lane);
+    R.raw[j] = __builtin_amdgcn_raw_buffer_load_b128(rr, (uint32_t)lane * 16 + j * kTile, 0, kNonTemporal);
+    R.nib[j] = __builtin_amdgcn_raw_buffer_load_b64(rn, (uint32_t)lane * 8 + j * (kTile / 2), 0, kNonTemporal);
   }
-  R.ixv = idx_p[t0 + min((uint32_t)lane, S)];
+  R.ixv = __builtin_amdgcn_raw_buffer_load_b32(ri, (uint32_t)lane * 4, 0, 0);
 }
 
 struct SegCtx {
@@ -113,34 +124,70 @@ struct SegCtx {
   uint32_t base4;
 };
 
-// PRELOAD: the segment's escapes sit in LDS (the common case).  Otherwise
-// (dense escapes) each tile's slice is staged from memory when needed.
+// Escape information of the S tiles held in one row buffer: where each
+// tile's escapes start in the stream, how many there are, and (preloaded
+// case, one or two escapes) their exponent bytes.  The index values are
+// clamped into the range this workgroup knows, so a corrupt blob can only
+// give wrong values, never an out-of-range access.
+template <int SMAX, bool PRELOAD>
+__device__ __forceinline__ void chunk_escapes(uint32_t ixv, uint32_t S, const SegCtx& C, uint32_t first[SMAX],
+                                              uint32_t cnt[SMAX], uint32_t e1[SMAX], uint32_t e2[SMAX]) {
+#pragma unroll
+  for (int j = 0; j < SMAX; j++) {
+    const uint32_t ia = (uint32_t)__builtin_amdgcn_readlane((int)ixv, j);
+    const uint32_t ib = (uint32_t)__builtin_amdgcn_readlane((int)ixv, j + 1);
+    first[j] = min(max(ia, C.e_lo), C.e_hi);
+    cnt[j] = min(min(max(ib, first[j]), C.e_hi) - first[j], (uint32_t)kTile);
+    e1[j] = e2[j] = 0;
+    if (PRELOAD && (uint32_t)j < S && cnt[j] != 0 && cnt[j] <= 2) {
+      const uint32_t o = first[j] - C.e_lo;
+      e1[j] = uniform(C.esc_sh[o]);
+      e2[j] = cnt[j] == 2 ? uniform(C.esc_sh[o + 1]) : e1[j];
+    }
+  }
+}
+
+// Exponent bytes of one tile (PRELOAD: the segment's escapes sit in LDS, the
+// common case; otherwise, dense escapes, each tile's slice is staged from
+// memory when needed).
+//
+// A tile whose escapes all carry the same exponent (in practice: most tiles
+// with one or two escapes) needs no per-weight placement: that exponent
+// becomes the table entry of code 15 and the tile is decoded through the
+// table like any other.  Only the remaining tiles take the rank-and-patch
+// path.
+template <bool CONTIG, bool PRELOAD>
+__device__ __forceinline__ void tile_exponents(u32x2 nib, uint32_t first, uint32_t cnt, uint32_t e1, uint32_t e2,
+                                               const SegCtx& C, uint32_t E[4]) {
+  if (cnt == 0) {
+    exponents16<CONTIG>(nib, C.lut, C.base4, E);
+  } else if (PRELOAD && cnt <= 2 && e1 == e2) {
+    const Lut L{C.lut.t0, C.lut.t1, C.lut.t2, (C.lut.t3 & 0x00FFFFFFu) | (e1 << 24)};
+    exponents16<false>(nib, L, C.base4, E);
+  } else {
+    exponents16<CONTIG>(nib, C.lut, C.base4, E);
+    if (PRELOAD) {
+      uint64_t m0, m1;
+      const uint32_t r = escape_rank(nib, m0, m1);
+      patch_escapes(C.esc_sh + (first - C.e_lo), r, cnt, m0, m1, E);
+    } else {
+      place_escapes(nib, C.esc_p, first, cnt, C.esc_wave, E);
+    }
+  }
+}
+
 template <int B, int SMAX, bool CONTIG, bool PRELOAD>
 __device__ __forceinline__ void row_dot(const RowBuf<SMAX>& R, uint32_t S, const uint32_t (*xr)[B][8],
                                         const SegCtx& C, float acc[B][2]) {
 #pragma unroll
   for (int b = 0; b < B; b++) acc[b][0] = acc[b][1] = 0.f;
+  uint32_t first[SMAX], cnt[SMAX], e1[SMAX], e2[SMAX];
+  chunk_escapes<SMAX, PRELOAD>(R.ixv, S, C, first, cnt, e1, e2);
 #pragma unroll
   for (int j = 0; j < SMAX; j++) {
     if ((uint32_t)j < S) {
       uint32_t E[4];
-      exponents16<CONTIG>(R.nib[j], C.lut, C.base4, E);
-      // clamp the index into the range this workgroup knows, so a corrupt
-      // blob can only give wrong values, never an out-of-range access
-      const uint32_t ia = (uint32_t)__builtin_amdgcn_readlane((int)R.ixv, j);
-      const uint32_t ib = (uint32_t)__builtin_amdgcn_readlane((int)R.ixv, j + 1);
-      const uint32_t a = min(max(ia, C.e_lo), C.e_hi);
-      const uint32_t e = min(max(ib, a), C.e_hi);
-      const uint32_t cnt = min(e - a, (uint32_t)kTile);
-      if (cnt) {
-        if (PRELOAD) {
-          uint64_t m0, m1;
-          const uint32_t r = escape_rank(R.nib[j], m0, m1);
-          patch_escapes(C.esc_sh + (a - C.e_lo), r, cnt, m0, m1, E);
-        } else {
-          place_escapes(R.nib[j], C.esc_p, a, cnt, C.esc_wave, E);
-        }
-      }
+      tile_exponents<CONTIG, PRELOAD>(R.nib[j], first[j], cnt[j], e1[j], e2[j], C, E);
       uint32_t w[8];
       assemble16(R.raw[j], E, w);
       dot16<B>(w, xr[j], acc);
@@ -220,7 +267,7 @@ __device__ __forceinline__ void run_segment(const GemvGroup& G, uint32_t u_lo, u
       const uint64_t row_tile0 = (uint64_t)(sub * phases + phase) * T + tl;
       const uint64_t row_stride = (uint64_t)phases * T;
       RowBuf<SMAX> A;
-      if (n_mine) load_row<SMAX>(A, raw_p, nib_p, idx_p, row_tile0, SL, lane);
+      if (n_mine) load_row<SMAX>(A, raw_p, nib_p, idx_p, row_tile0, S, lane);
       uint32_t xr[SMAX][B][8];
 #pragma unroll
       for (int j = 0; j < SMAX; j++) {
@@ -324,7 +371,562 @@ static hipError_t run(GemvLaunch& L, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---- Row-streaming variant (batch 1..4, x staged in LDS) -------------------
+//
+// One 1024-thread workgroup per CU.  Every wave decodes whole rows (in
+// chunks of up to 4 tiles, the next chunk in flight while one is decoded)
+// and takes its next row from a counter in LDS, so the 16 waves of a CU
+// balance among themselves whatever their scheduling priority; workgroups
+// get equal-cost contiguous row ranges.  x for the current tensor is staged
+// in LDS (each lane's 16 values split in two 16-byte halves stored in
+// separate 1 KiB arrays, so the reads are conflict-free).
+constexpr int kRowWaves = 16;
+constexpr int kRowChunk = 4;
+constexpr uint32_t kRowEscShared = 16384;
+constexpr uint32_t kRowXMax = 98304;  // LDS bytes for x: B * K * 2
+
+struct RowLaunch {
+  GemvGroup g[LBF_MAX_GROUPS];
+  uint64_t total_cost;
+  int n_groups;
+  int y_bf16;
+  uint32_t x_bytes;
+};
+
+template <int B, bool CONTIG, bool PRELOAD>
+__device__ __forceinline__ void chunk_dot(const RowBuf<kRowChunk>& R, uint32_t S, uint32_t c, uint32_t T,
+                                          const uint8_t* x_sh, const SegCtx& C, float acc[B][2], int lane) {
+  uint32_t first[kRowChunk], cnt[kRowChunk], e1[kRowChunk], e2[kRowChunk];
+  chunk_escapes<kRowChunk, PRELOAD>(R.ixv, S, C, first, cnt, e1, e2);
+#pragma unroll
+  for (int j = 0; j < kRowChunk; j++) {
+    if ((uint32_t)j < S) {
+      uint32_t xr[B][8];
+#pragma unroll
+      for (int b = 0; b < B; b++) {
+        const uint8_t* xs = x_sh + (size_t)((b * T + c + j) * 2) * kTile + lane * 16;
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(xs);
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(xs + kTile);
+        xr[b][0] = a0.x; xr[b][1] = a0.y; xr[b][2] = a0.z; xr[b][3] = a0.w;
+        xr[b][4] = a1.x; xr[b][5] = a1.y; xr[b][6] = a1.z; xr[b][7] = a1.w;
+      }
+      uint32_t E[4];
+      tile_exponents<CONTIG, PRELOAD>(R.nib[j], first[j], cnt[j], e1[j], e2[j], C, E);
+      uint32_t w[8];
+      assemble16(R.raw[j], E, w);
+      dot16<B>(w, xr, acc);
+    }
+  }
+}
+
+template <int B, bool CONTIG, bool PRELOAD>
+__device__ __forceinline__ void stream_rows(const GemvGroup& G, uint32_t u_lo, uint32_t u_hi, bool y_bf16,
+                                            const uint8_t* raw_p, const uint8_t* nib_p, const uint32_t* idx_p,
+                                            const uint8_t* x_sh, const SegCtx& C, uint32_t* ctr, int lane) {
+  const uint32_t T = G.cols >> 10;
+  auto pull = [&]() -> uint32_t {
+    uint32_t v = 0;
+    if (lane == 0) v = atomicAdd(ctr, 1u);
+    return u_lo + uniform(v);
+  };
+  uint32_t r = pull();
+  if (r >= u_hi) return;
+  uint32_t rn = pull();
+  uint32_t c = 0;
+  RowBuf<kRowChunk> A, Bf;
+  load_row<kRowChunk>(A, raw_p, nib_p, idx_p, (uint64_t)r * T, min((uint32_t)kRowChunk, T), lane);
+  float acc[B][2];
+#pragma unroll
+  for (int b = 0; b < B; b++) acc[b][0] = acc[b][1] = 0.f;
+  // one step: prefetch the chunk after (r, c) into `nxt`, decode `cur`;
+  // returns false when the wave's stream has ended
+  auto step = [&](RowBuf<kRowChunk>& cur, RowBuf<kRowChunk>& nxt) -> bool {
+    const bool row_end = c + kRowChunk >= T;
+    const uint32_t r2 = row_end ? rn : r, c2 = row_end ? 0u : c + kRowChunk;
+    const bool more = r2 < u_hi;
+    const uint32_t lr = more ? r2 : r, lc = more ? c2 : c;
+    load_row<kRowChunk>(nxt, raw_p, nib_p, idx_p, (uint64_t)lr * T + lc, min((uint32_t)kRowChunk, T - lc), lane);
+    chunk_dot<B, CONTIG, PRELOAD>(cur, min((uint32_t)kRowChunk, T - c), c, T, x_sh, C, acc, lane);
+    if (row_end) {
+#pragma unroll
+      for (int b = 0; b < B; b++) {
+        const float v = wave_sum(acc[b][0] + acc[b][1]);
+        acc[b][0] = acc[b][1] = 0.f;
+        if (lane == 0) {
+          const size_t o = (size_t)b * G.rows + r;
+          if (y_bf16)
+            static_cast<uint16_t*>(G.y)[o] = f32_to_bf16_rne(v);
+          else
+            static_cast<float*>(G.y)[o] = v;
+        }
+      }
+      if (more) rn = pull();
+    }
+    r = r2;
+    c = c2;
+    return more;
+  };
+  while (step(A, Bf) && step(Bf, A)) {
+  }
+}
+
+template <int B>
+__global__ __launch_bounds__(kRowWaves * kWave) void k_gemv_rows(RowLaunch L) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint8_t* x_sh = smem;
+  uint8_t* esc_sh = smem + L.x_bytes;
+  uint8_t* stage = esc_sh + kRowEscShared;
+  uint32_t* ctr = reinterpret_cast<uint32_t*>(stage + kRowWaves * kTile);
+  const uint32_t wave = uniform(threadIdx.x >> 6);
+  const int lane = lane_id();
+  const uint64_t c_lo = L.total_cost * blockIdx.x / gridDim.x;
+  const uint64_t c_hi = L.total_cost * (blockIdx.x + 1) / gridDim.x;
+  for (int gi = 0; gi < L.n_groups; gi++) {
+    const GemvGroup& G = L.g[gi];
+    const uint64_t g_lo = G.cost_begin, g_hi = G.cost_begin + (uint64_t)G.n_units * G.unit_cost;
+    if (g_hi <= c_lo) continue;
+    if (g_lo >= c_hi) break;
+    const uint32_t u_lo = c_lo > g_lo ? (uint32_t)((c_lo - g_lo + G.unit_cost - 1) / G.unit_cost) : 0u;
+    const uint32_t u_hi = (uint32_t)min((uint64_t)G.n_units, (c_hi - g_lo + G.unit_cost - 1) / G.unit_cost);
+    if (u_lo >= u_hi) continue;
+    // segment: rows [u_lo, u_hi) of tensor gi
+    const uint32_t T = G.cols >> 10;
+    const uint64_t n_tiles = (uint64_t)G.rows * T;
+    const uint8_t* raw_p = G.blob + LBF_HEADER_BYTES;
+    const uint8_t* nib_p = raw_p + n_tiles * kTile;
+    const uint32_t* idx_p = reinterpret_cast<const uint32_t*>(nib_p + n_tiles * (kTile / 2));
+    const uint8_t* esc_p =
+        G.blob + ((LBF_HEADER_BYTES + n_tiles * (kTile + kTile / 2) + 4 * (n_tiles + 1) + 255) & ~uint64_t(255));
+    const uint32_t seg_hi = idx_p[(uint64_t)u_hi * T];
+    const uint32_t seg_lo = idx_p[(uint64_t)u_lo * T];
+    __syncthreads();  // the previous segment is done with x_sh, esc_sh and the counter
+    // x -> LDS: element (b, t, lane, half) = 16 bytes at ((b*T + t)*2 + half)*1024 + lane*16
+    const uint32_t nx = (uint32_t)B * T * kWave * 2;
+    for (uint32_t i = threadIdx.x; i < nx; i += kRowWaves * kWave) {
+      const uint32_t half = i & 1u, ln = (i >> 1) & 63u, bt = i >> 7;
+      const u32x4 v = reinterpret_cast<const u32x4*>(G.x)[(size_t)bt * 128 + ln * 2 + half];
+      *reinterpret_cast<u32x4*>(x_sh + (size_t)(bt * 2 + half) * kTile + ln * 16) = v;
+    }
+    SegCtx C;
+    C.esc_p = esc_p;
+    C.esc_sh = esc_sh;
+    C.esc_wave = stage + wave * kTile;
+    C.lut = Lut{G.lut[0], G.lut[1], G.lut[2], G.lut[3]};
+    C.base4 = G.base4;
+    C.e_hi = min(seg_hi, G.n_esc);
+    C.e_lo = min(seg_lo, C.e_hi);
+    const bool preload = C.e_hi - C.e_lo <= kRowEscShared;
+    if (preload) {
+      for (uint32_t p = threadIdx.x; p < C.e_hi - C.e_lo; p += kRowWaves * kWave) esc_sh[p] = esc_p[C.e_lo + p];
+    } else {  // dense escapes: per-tile staging, bounded by the stream itself
+      C.e_lo = 0;
+      C.e_hi = G.n_esc;
+    }
+    if (threadIdx.x == 0) *ctr = 0u;
+    __syncthreads();
+    const bool contig = G.flags & 1u;
+    if (preload) {
+      if (contig)
+        stream_rows<B, true, true>(G, u_lo, u_hi, L.y_bf16, raw_p, nib_p, idx_p, x_sh, C, ctr, lane);
+      else
+        stream_rows<B, false, true>(G, u_lo, u_hi, L.y_bf16, raw_p, nib_p, idx_p, x_sh, C, ctr, lane);
+    } else {
+      if (contig)
+        stream_rows<B, true, false>(G, u_lo, u_hi, L.y_bf16, raw_p, nib_p, idx_p, x_sh, C, ctr, lane);
+      else
+        stream_rows<B, false, false>(G, u_lo, u_hi, L.y_bf16, raw_p, nib_p, idx_p, x_sh, C, ctr, lane);
+    }
+  }
+}
+
+template <int B>
+static hipError_t run_rows_kernel(RowLaunch& L, hipStream_t s) {
+  static int cus = 0;
+  const uint32_t lds = L.x_bytes + kRowEscShared + kRowWaves * kTile + 16;
+  if (!cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return hipErrorUnknown;
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_rows<B>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)(kRowXMax + kRowEscShared + kRowWaves * kTile + 16));
+    if (e != hipSuccess) return e;
+  }
+  uint64_t units = 0;
+  for (int g = 0; g < L.n_groups; g++) units += L.g[g].n_units;
+  const uint64_t grid = std::min<uint64_t>((uint64_t)cus, units);
+  hipLaunchKernelGGL((k_gemv_rows<B>), dim3((unsigned)grid), dim3(kRowWaves * kWave), lds, s, L);
+  return hipGetLastError();
+}
+
+static bool rows_fit(const GemvGroup* groups, int n_groups, int batch) {
+  if (batch > 4) return false;
+  for (int g = 0; g < n_groups; g++)
+    if ((uint64_t)batch * groups[g].cols * 2 > kRowXMax) return false;
+  return true;
+}
+
+static hipError_t launch_rows(const GemvGroup* groups, int n_groups, int batch, int y_dtype, hipStream_t s) {
+  RowLaunch L;
+  L.n_groups = n_groups;
+  L.y_bf16 = y_dtype == LBF_BF16;
+  uint64_t cost = 0;
+  uint32_t x_bytes = 0;
+  for (int g = 0; g < n_groups; g++) {
+    GemvGroup G = groups[g];
+    const uint32_t T = G.cols >> 10;
+    G.n_units = G.rows;  // a unit is one row
+    const uint64_t n_tiles = (uint64_t)G.rows * T;
+    const uint32_t esc_per_tile = (uint32_t)std::min<uint64_t>(1024, (G.n_esc + n_tiles - 1) / n_tiles);
+    G.unit_cost = T * (16u + esc_per_tile / 8u);
+    G.cost_begin = cost;
+    cost += (uint64_t)G.n_units * G.unit_cost;
+    x_bytes = std::max<uint32_t>(x_bytes, (uint32_t)batch * G.cols * 2);
+    L.g[g] = G;
+  }
+  L.total_cost = cost;
+  L.x_bytes = x_bytes;
+  switch (batch) {
+    case 1: return run_rows_kernel<1>(L, s);
+    case 2: return run_rows_kernel<2>(L, s);
+    case 3: return run_rows_kernel<3>(L, s);
+    default: return run_rows_kernel<4>(L, s);
+  }
+}
+
+// ---- Ring GEMV (x of every tensor fits in LDS) ------------------------------
+//
+// The fastest form, used for batch 1..4 when x of every tensor of the call
+// fits in LDS.  One 1024-thread workgroup per CU.  The unit of work is one
+// row; rows of all tensors are dealt to the CUs cyclically (CU w takes rows
+// w, w + #CUs, ...), so every CU gets the same mix, and inside a CU the 16
+// waves take rows from a counter in LDS, so they finish together whatever
+// their scheduling priority.  Waves share nothing but x (staged once in
+// LDS) and never wait for each other.  Each wave streams its rows in chunks
+// of up to 4 tiles through a ring of three chunk slots: while chunk i is
+// decoded, the coded planes and the escape bytes of chunk i + 1 and the tile
+// index of chunk i + 2 are in flight (the escape bytes need the index, the
+// index needs nothing).  Every memory operation is issued unconditionally
+// (a disabled one gets a zero-length buffer range) and the ring is unrolled
+// by three, so the compiler counts outstanding loads exactly.
+constexpr int kRingWaves = 16;
+constexpr uint32_t kRingXMax = 98304;
+
+struct RingLaunch {
+  GemvGroup g[LBF_MAX_GROUPS];          // cost_begin: first global row of the group
+  uint32_t x_off[LBF_MAX_GROUPS];       // LDS offset of each group's x
+  uint32_t xsrc_group[LBF_MAX_GROUPS];  // groups whose x arrays are staged (distinct pointers)
+  uint32_t n_rows, n_xsrc;
+  int n_groups, y_bf16;
+};
+
+struct Slot {
+  u32x4 raw[kRowChunk];
+  u32x2 nib[kRowChunk];
+  uint32_t idxv;  // lane j: idx[t0 + j], j <= S
+  uint32_t escv;  // lane p: escape p of the chunk's slice, p < 64
+};
+
+// Position of a chunk: tiles [c, c + S) of row r of group g (T tiles a row).
+struct Pos {
+  uint32_t g, r, c, S, T;
+  bool valid;
+};
+
+struct GroupPtrs {
+  const uint8_t *raw, *nib, *esc;
+  const uint32_t* idx;
+};
+
+__device__ __forceinline__ GroupPtrs ptrs_of(const GemvGroup& G) {
+  const uint64_t n_tiles = (uint64_t)G.rows * (G.cols >> 10);
+  GroupPtrs P;
+  P.raw = G.blob + LBF_HEADER_BYTES;
+  P.nib = P.raw + n_tiles * kTile;
+  P.idx = reinterpret_cast<const uint32_t*>(P.nib + n_tiles * (kTile / 2));
+  P.esc = G.blob + ((LBF_HEADER_BYTES + n_tiles * (kTile + kTile / 2) + 4 * (n_tiles + 1) + 255) & ~uint64_t(255));
+  return P;
+}
+
+__device__ __forceinline__ Pos row_pos(const RingLaunch& L, uint32_t q) {
+  Pos p;
+  p.valid = q < L.n_rows;
+  const uint32_t qq = p.valid ? q : L.n_rows - 1;
+  uint32_t g = 0;
+  while (g + 1 < (uint32_t)L.n_groups && L.g[g + 1].cost_begin <= qq) g++;
+  p.g = g;
+  p.r = qq - (uint32_t)L.g[g].cost_begin;
+  p.T = L.g[g].cols >> 10;
+  p.c = 0;
+  p.S = p.valid ? min((uint32_t)kRowChunk, p.T) : 0u;
+  return p;
+}
+
+__device__ __forceinline__ uint64_t tile_of(const Pos& p) { return (uint64_t)p.r * p.T + p.c; }
+
+__device__ __forceinline__ void load_idx(Slot& s, const RingLaunch& L, const Pos& p, int lane) {
+  const GroupPtrs P = ptrs_of(L.g[p.g]);
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(P.idx + tile_of(p), p.valid ? (p.S + 1) * 4 : 0u);
+  s.idxv = __builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)lane * 4, 0, 0);
+}
+
+// Escape slice of the chunk (from its index, already loaded) and its planes.
+__device__ __forceinline__ void load_data(Slot& s, const RingLaunch& L, const Pos& p, uint32_t& e_first,
+                                          uint32_t& e_cnt, int lane) {
+  const GemvGroup& G = L.g[p.g];
+  const GroupPtrs P = ptrs_of(G);
+  const uint32_t hi = min((uint32_t)__builtin_amdgcn_readlane((int)s.idxv, (int)p.S), G.n_esc);
+  e_first = min((uint32_t)__builtin_amdgcn_readlane((int)s.idxv, 0), hi);
+  e_cnt = p.valid ? hi - e_first : 0u;
+  const __amdgpu_buffer_rsrc_t re = make_rsrc(P.esc + e_first, min(e_cnt, 64u));
+  s.escv = __builtin_amdgcn_raw_buffer_load_b8(re, (uint32_t)lane, 0, 0);
+  const uint64_t t0 = tile_of(p);
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(P.raw + t0 * kTile, p.S * kTile);
+  const __amdgpu_buffer_rsrc_t rn = make_rsrc(P.nib + t0 * (kTile / 2), p.S * (kTile / 2));
+#pragma unroll
+  for (int j = 0; j < kRowChunk; j++) {
+    s.raw[j] = __builtin_amdgcn_raw_buffer_load_b128(rr, (uint32_t)lane * 16 + j * kTile, 0, kNonTemporal);
+    s.nib[j] = __builtin_amdgcn_raw_buffer_load_b64(rn, (uint32_t)lane * 8 + j * (kTile / 2), 0, kNonTemporal);
+  }
+}
+
+// Exponent bytes of tile j of a chunk; the chunk's escapes are in escv (and,
+// for the patch path, in the wave's LDS slot) unless the chunk holds more
+// than 64 of them (dense: each tile's slice is staged from memory).
+__device__ __forceinline__ void ring_exponents(u32x2 nib, const GemvGroup& G, uint32_t ia, uint32_t ib, uint32_t escv,
+                                               uint32_t e_first, uint32_t e_cnt, const uint8_t* esc_p, uint8_t* slot,
+                                               uint32_t E[4]) {
+  const Lut lut{G.lut[0], G.lut[1], G.lut[2], G.lut[3]};
+  const bool contig = G.flags & 1u;
+  const bool dense = e_cnt > 64u;
+  const uint32_t lo = dense ? 0u : e_first, hi = dense ? G.n_esc : e_first + e_cnt;
+  const uint32_t first = min(max(ia, lo), hi);
+  const uint32_t cnt = min(min(max(ib, first), hi) - first, (uint32_t)kTile);
+  if (cnt == 0) {
+    if (contig)
+      exponents16<true>(nib, lut, G.base4, E);
+    else
+      exponents16<false>(nib, lut, G.base4, E);
+    return;
+  }
+  if (!dense) {
+    const uint32_t o = first - e_first;  // < 64 here
+    const uint32_t e1 = (uint32_t)__builtin_amdgcn_readlane((int)escv, (int)o);
+    const uint32_t e2 = cnt == 2 ? (uint32_t)__builtin_amdgcn_readlane((int)escv, (int)min(o + 1, 63u)) : e1;
+    if (cnt <= 2 && e1 == e2) {
+      const Lut L2{lut.t0, lut.t1, lut.t2, (lut.t3 & 0x00FFFFFFu) | (e1 << 24)};
+      exponents16<false>(nib, L2, G.base4, E);
+      return;
+    }
+  }
+  if (contig)
+    exponents16<true>(nib, lut, G.base4, E);
+  else
+    exponents16<false>(nib, lut, G.base4, E);
+  if (!dense) {
+    uint64_t m0, m1;
+    const uint32_t rk = escape_rank(nib, m0, m1);
+    patch_escapes(slot + (first - e_first), rk, cnt, m0, m1, E);
+  } else {
+    place_escapes(nib, esc_p, first, cnt, slot, E);
+  }
+}
+
+template <int B>
+__global__ __launch_bounds__(kRingWaves * kWave) void k_gemv_ring(RingLaunch L) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const uint32_t wave = uniform(threadIdx.x >> 6);
+  const int lane = lane_id();
+  uint8_t* slot_lds = smem + kRingXMax + wave * kTile;
+  uint32_t* lctr = reinterpret_cast<uint32_t*>(smem + kRingXMax + kRingWaves * kTile);
+
+  // rows of this CU: blockIdx.x + k * gridDim.x; the wave's first two come
+  // from k = wave, wave + 16, the rest from the LDS counter (starts at 32)
+  uint32_t k_static = 0;
+  auto next_row = [&]() -> Pos {
+    uint32_t k;
+    if (k_static < 2) {
+      k = wave + kRingWaves * k_static++;
+    } else {
+      uint32_t v = 0;
+      if (lane == 0) v = atomicAdd(lctr, 1u);
+      k = uniform(v);
+    }
+    const uint64_t q = blockIdx.x + (uint64_t)k * gridDim.x;
+    return row_pos(L, q < L.n_rows ? (uint32_t)q : L.n_rows);
+  };
+  auto advance = [&](const Pos& p) -> Pos {
+    if (p.valid && p.c + kRowChunk < p.T) {
+      Pos n = p;
+      n.c = p.c + kRowChunk;
+      n.S = min((uint32_t)kRowChunk, p.T - n.c);
+      return n;
+    }
+    if (!p.valid) return p;
+    return next_row();
+  };
+
+  Slot s0, s1, s2;
+  Pos p0 = next_row();
+  Pos p1 = advance(p0);
+  uint32_t f0, n0, f1, n1;
+  load_idx(s0, L, p0, lane);
+  load_idx(s1, L, p1, lane);
+  load_data(s0, L, p0, f0, n0, lane);
+  // stage every distinct x array while the first loads are in flight:
+  // element (b, t, lane, half) at x_off + ((b*T + t)*2 + half)*1024 + lane*16
+  for (uint32_t k = 0; k < L.n_xsrc; k++) {
+    const GemvGroup& G = L.g[L.xsrc_group[k]];
+    const uint32_t T = G.cols >> 10;
+    uint8_t* xd = smem + L.x_off[L.xsrc_group[k]];
+    const uint32_t nx = (uint32_t)B * T * kWave * 2;
+    for (uint32_t i = threadIdx.x; i < nx; i += kRingWaves * kWave) {
+      const uint32_t half = i & 1u, ln = (i >> 1) & 63u, bt = i >> 7;
+      const u32x4 v = reinterpret_cast<const u32x4*>(G.x)[(size_t)bt * 128 + ln * 2 + half];
+      *reinterpret_cast<u32x4*>(xd + (size_t)(bt * 2 + half) * kTile + ln * 16) = v;
+    }
+  }
+  if (threadIdx.x == 0) *lctr = 2u * kRingWaves;
+  __syncthreads();
+
+  float acc[B][2];
+#pragma unroll
+  for (int bb = 0; bb < B; bb++) acc[bb][0] = acc[bb][1] = 0.f;
+
+  // one step: chunk p0 in `cur` is decoded; the next chunk p1 (index in
+  // `nx1` already) gets its escapes and planes; the one after, p2, its index
+  auto step = [&](Slot& cur, Slot& nx1, Slot& nx2) -> bool {
+    const Pos p2 = advance(p1);
+    load_idx(nx2, L, p2, lane);
+    load_data(nx1, L, p1, f1, n1, lane);
+    const GemvGroup& G = L.g[p0.g];
+    const GroupPtrs P = ptrs_of(G);
+    const uint8_t* x_g = smem + L.x_off[p0.g];
+    slot_lds[lane] = (uint8_t)cur.escv;  // the chunk's escapes, for the patch path
+    wave_lds_sync();
+#pragma unroll
+    for (int j = 0; j < kRowChunk; j++) {
+      if ((uint32_t)j < p0.S) {
+        uint32_t xr[B][8];
+#pragma unroll
+        for (int bb = 0; bb < B; bb++) {
+          const uint8_t* xs = x_g + (size_t)((bb * p0.T + p0.c + j) * 2) * kTile + lane * 16;
+          const u32x4 a0 = *reinterpret_cast<const u32x4*>(xs);
+          const u32x4 a1 = *reinterpret_cast<const u32x4*>(xs + kTile);
+          xr[bb][0] = a0.x; xr[bb][1] = a0.y; xr[bb][2] = a0.z; xr[bb][3] = a0.w;
+          xr[bb][4] = a1.x; xr[bb][5] = a1.y; xr[bb][6] = a1.z; xr[bb][7] = a1.w;
+        }
+        const uint32_t ia = (uint32_t)__builtin_amdgcn_readlane((int)cur.idxv, j);
+        const uint32_t ib = (uint32_t)__builtin_amdgcn_readlane((int)cur.idxv, j + 1);
+        uint32_t E[4];
+        ring_exponents(cur.nib[j], G, ia, ib, cur.escv, f0, n0, P.esc, slot_lds, E);
+        uint32_t w[8];
+        assemble16(cur.raw[j], E, w);
+        dot16<B>(w, xr, acc);
+      }
+    }
+    // row end: the sums of row p0.r are stored by lane 0 (range 0 otherwise)
+    const bool row_end = p0.valid && p0.c + kRowChunk >= p0.T;
+    float v[B];
+#pragma unroll
+    for (int bb = 0; bb < B; bb++) v[bb] = 0.f;
+    if (row_end) {
+#pragma unroll
+      for (int bb = 0; bb < B; bb++) {
+        v[bb] = wave_sum(acc[bb][0] + acc[bb][1]);
+        acc[bb][0] = acc[bb][1] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int bb = 0; bb < B; bb++) {
+      if (L.y_bf16) {
+        const __amdgpu_buffer_rsrc_t yr = make_rsrc(static_cast<uint16_t*>(G.y) + (size_t)bb * G.rows + p0.r, row_end ? 2u : 0u);
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(v[bb]), yr, (uint32_t)lane * 2, 0, 0);
+      } else {
+        const __amdgpu_buffer_rsrc_t yr = make_rsrc(static_cast<float*>(G.y) + (size_t)bb * G.rows + p0.r, row_end ? 4u : 0u);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v[bb]), yr, (uint32_t)lane * 4, 0, 0);
+      }
+    }
+    wave_lds_sync();  // the slot is rewritten by the next chunk
+    p0 = p1;
+    p1 = p2;
+    f0 = f1;
+    n0 = n1;
+    return p0.valid;
+  };
+  if (p0.valid)
+    while (step(s0, s1, s2) && step(s1, s2, s0) && step(s2, s0, s1)) {
+    }
+}
+
+template <int B>
+static hipError_t run_ring_kernel(RingLaunch& L, hipStream_t s) {
+  static int cus = 0;
+  const uint32_t lds = kRingXMax + kRingWaves * kTile + 16;
+  if (!cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return hipErrorUnknown;
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_ring<B>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  const uint32_t grid = (uint32_t)std::min<uint64_t>((uint64_t)cus, L.n_rows);
+  hipLaunchKernelGGL((k_gemv_ring<B>), dim3(grid), dim3(kRingWaves * kWave), lds, s, L);
+  return hipGetLastError();
+}
+
+// Ring path if x of all groups (distinct arrays) fits in LDS.
+static hipError_t launch_ring(const GemvGroup* groups, int n_groups, int batch, int y_dtype, bool& used,
+                              hipStream_t s) {
+  used = false;
+  if (batch > 4) return hipSuccess;
+  RingLaunch L;
+  uint32_t x_bytes = 0;
+  L.n_xsrc = 0;
+  uint64_t rows = 0;
+  // longest rows first: rows are handed out in this order, so the coarsest
+  // units are taken early and the last ones are the shortest
+  int order[LBF_MAX_GROUPS];
+  for (int g = 0; g < n_groups; g++) order[g] = g;
+  std::stable_sort(order, order + n_groups, [&](int a, int b) { return groups[a].cols > groups[b].cols; });
+  for (int g = 0; g < n_groups; g++) {
+    const GemvGroup& G = groups[order[g]];
+    int same = -1;
+    for (uint32_t k = 0; k < L.n_xsrc; k++) {
+      const GemvGroup& H = L.g[L.xsrc_group[k]];
+      if (H.x == G.x && H.cols == G.cols) same = (int)L.xsrc_group[k];
+    }
+    if (same >= 0) {
+      L.x_off[g] = L.x_off[same];
+    } else {
+      L.x_off[g] = x_bytes;
+      L.xsrc_group[L.n_xsrc++] = (uint32_t)g;
+      x_bytes += (uint32_t)batch * G.cols * 2;
+      if (x_bytes > kRingXMax) return hipSuccess;
+    }
+    L.g[g] = G;
+    L.g[g].cost_begin = rows;
+    rows += G.rows;
+  }
+  if (rows >= (1ull << 31)) return hipSuccess;
+  L.n_rows = (uint32_t)rows;
+  L.n_groups = n_groups;
+  L.y_bf16 = y_dtype == LBF_BF16;
+  used = true;
+  switch (batch) {
+    case 1: return run_ring_kernel<1>(L, s);
+    case 2: return run_ring_kernel<2>(L, s);
+    case 3: return run_ring_kernel<3>(L, s);
+    default: return run_ring_kernel<4>(L, s);
+  }
+}
+
 hipError_t launch_gemv(const GemvGroup* groups, int n_groups, int batch, int y_dtype, hipStream_t s) {
+  bool used = false;
+  const hipError_t e = launch_ring(groups, n_groups, batch, y_dtype, used, s);
+  if (used || e != hipSuccess) return e;
+  if (rows_fit(groups, n_groups, batch)) return launch_rows(groups, n_groups, batch, y_dtype, s);
   static const int smax_of[9] = {0, 4, 4, 2, 2, 1, 1, 1, 1};
   const uint32_t smax = (uint32_t)smax_of[batch];
   GemvLaunch L;

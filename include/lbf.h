@@ -16,12 +16,14 @@
  *
  * Format v1 (one "blob" per weight tensor, one contiguous device buffer):
  *   [0, 256)        header: the 96-byte lbf_desc below, then zeros
- *   off_raw = 256   raw plane, one byte per weight: sign << 7 | mantissa,
- *                   zero padded to n_tiles * 1024 bytes
- *   off_nib         nibble plane: weight i's 4-bit code is the low (i even) or
- *                   high (i odd) nibble of byte i >> 1; code c < 15 means
- *                   exponent lut[c], code 15 means "next escape byte";
- *                   zero padded to n_tiles * 512 bytes
+ *   off_raw = 256   raw plane, one byte per weight: mantissa_i << 1 | sign of
+ *                   weight i ^ 1 (weights pair up as 2j, 2j + 1; padding
+ *                   weights count as +0.0), padded to n_tiles * 1024 bytes
+ *   off_nib         nibble plane, one 32-bit word per 8 weights: byte j of
+ *                   word g holds the code of weight 8g + j in its low nibble
+ *                   and of weight 8g + 4 + j in its high nibble; code c < 15
+ *                   means exponent lut[c], code 15 means "next escape byte";
+ *                   n_tiles * 512 bytes (padding codes are 0)
  *   off_idx         uint32 idx[n_tiles + 1]: idx[0] = 0 and idx[t + 1] - idx[t]
  *                   is the number of escapes in tile t (1024 weights)
  *   off_esc         escape stream: one exponent byte per escaped weight, in
@@ -102,7 +104,7 @@ int lbf_desc_check(const lbf_desc* desc);
 
 /*
  * lbf_encode — code a BF16 tensor into a blob (two phases).
- *   d_w        device, bf16 bit patterns [rows, cols], row-major, 2-byte aligned
+ *   d_w        device, bf16 bit patterns [rows, cols], row-major, 16-byte aligned
  *   d_work     device workspace of at least lbf_encode_work_bytes(rows, cols)
  *              bytes, 256-byte aligned; its contents on entry do not matter
  *   desc       host; phase 1 writes it, phase 2 reads it
@@ -122,7 +124,7 @@ int lbf_encode(const void* d_w, uint64_t rows, uint64_t cols, void* d_work, uint
  * lbf_decode — rebuild the exact BF16 tensor from a blob.
  *   desc       host copy of the blob's header (checked with lbf_desc_check)
  *   d_blob     device, 256-byte aligned, desc->blob_bytes long
- *   d_w_out    device, bf16 [rows, cols], 4-byte aligned; fully overwritten
+ *   d_w_out    device, bf16 [rows, cols], 16-byte aligned; fully overwritten
  * Bit-exact: NaN payloads, signed zeros, infinities and denormals survive.
  */
 int lbf_decode(const lbf_desc* desc, const void* d_blob, void* d_w_out, hipStream_t s);
