@@ -30,7 +30,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "fused decode-GEMV BF16-equiv weight GB/s + % HBM roofline, 8B-shaped layer"
-COUNTERS = os.path.join(ROOT, "profiles", "gemv_layer_b1_counters.json")
+COUNTERS = os.path.join(ROOT, "profiles", "gemv_ring_layer_b1_counters.json")
+KERNEL = "lbf::k_gemv_ring<1>"
 KERNEL_SOURCES = ("decode_byte_split_amd/csrc/lbf_gemv.hip", "decode_byte_split_amd/csrc/lbf_device.h")
 
 
@@ -59,26 +60,67 @@ def dev(torch, a):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
 
 
-def time_launches(torch, fn, steps: int, warmup: int):
-    """Run fn(i) warmup + steps times; returns (ms per step over the timed
-    region, mean ms per launch from per-launch events)."""
+def time_region(torch, fn, steps: int, warmup: int) -> float:
+    """Run fn(i) warmup times untimed, then steps times back to back between
+    two HIP events on the launch stream; returns ms per call.  One call is one
+    kernel launch here, so this is the mean launch duration (the gaps between
+    back-to-back launches are included, host marshalling is not: each call is
+    a single prepared ctypes call)."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0.record()
     for i in range(steps):
-        ev[i][0].record()
         fn(warmup + i)
-        ev[i][1].record()
     t1.record()
     torch.cuda.synchronize()
-    total = t0.elapsed_time(t1)
-    per = [a.elapsed_time(b) for a, b in ev]
-    return total / steps, float(np.mean(per)), float(np.median(per))
+    return t0.elapsed_time(t1) / steps
+
+
+COPY_ELEMS = 1 << 28  # float32 elements of the calibration copy: 1 GiB read, 1 GiB written
+
+
+def copy_calibration(torch, reps: int = 3):
+    """A plain elementwise kernel with known traffic (out = -in over 1 GiB of
+    float32) so a counter run can scale FETCH_SIZE / WRITE_SIZE to bytes."""
+    src = torch.ones(COPY_ELEMS, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+def _counter_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, kernel_key: str, alg_bytes: int):
+    """Scale the mean FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the
+    kernel whose name contains kernel_key by what the same counters read for
+    the calibration copy (4 * COPY_ELEMS bytes each way)."""
+    out = {"kernel_hash": kernel_hash(), "copy_bytes_each_way": 4 * COPY_ELEMS}
+    for label, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = [r for r in _counter_rows(path) if r["Counter_Name"] == label]
+        cal = [float(r["Counter_Value"]) for r in rows if "neg_kernel" in r["Kernel_Name"]]
+        ker = [float(r["Counter_Value"]) for r in rows if kernel_key in r["Kernel_Name"]]
+        if not cal or not ker:
+            raise SystemExit("%s: no calibration (%d) or kernel (%d) dispatches" % (path, len(cal), len(ker)))
+        factor = float(np.mean(cal)) * 1024.0 / (4 * COPY_ELEMS)
+        out[label] = {"kernel_kib_mean": float(np.mean(ker)), "kernel_dispatches": len(ker),
+                      "copy_kib_mean": float(np.mean(cal)), "copy_dispatches": len(cal),
+                      "factor": factor, "bytes_per_launch": float(np.mean(ker)) * 1024.0 / factor}
+    out["kernel"] = kernel_key
+    out["hbm_bytes_per_launch"] = int(round(out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"]))
+    out["algorithmic_bytes_per_launch"] = alg_bytes
+    out["traffic_over_algorithmic"] = out["hbm_bytes_per_launch"] / alg_bytes
+    return out
 
 
 def cpu_baseline(Ws, xs, min_seconds: float):
@@ -112,7 +154,20 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--extras", action="store_true", help="also time decode, the batch sweep and raw BF16")
     ap.add_argument("--rotate-gb", type=float, default=1.1)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a 1 GiB elementwise copy first (scale for FETCH_SIZE / WRITE_SIZE counter runs)")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "BENCH_JSON"),
+                    help="turn two rocprofv3 --pmc counter_collection.csv files (and the JSON line bench.py "
+                         "printed in one of those runs) into the traffic summary, print it and exit")
     args = ap.parse_args()
+
+    if args.summarize_counters:
+        fetch_csv, write_csv, bench_json = args.summarize_counters
+        with open(bench_json) as f:
+            line = [l for l in f if l.startswith("{")][-1]
+        alg = json.loads(line)["roofline"]["algorithmic_bytes_per_launch"]
+        print(json.dumps(summarize_counters(fetch_csv, write_csv, KERNEL.split("::")[1].split("<")[0], alg), indent=1))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the fused decode-GEMV has no cross-GPU step in this build "
@@ -141,13 +196,16 @@ def main():
     log("coded layer: %d bytes (%.4f bits/weight, %d escapes), %d rotation copies"
         % (layer_blob_bytes, 8.0 * layer_blob_bytes / n_weights, sum(b.n_esc for b in blobs), copies))
 
-    step = lambda i: lbf.gemv(rot[i % copies], xd, lbf.LBF_F32, outs=ys)
-    ms_step, ms_launch, ms_launch_med = time_launches(torch, step, args.steps, args.warmup)
+    if args.copy_calibration:
+        copy_calibration(torch)
+    calls = [lbf.prepare(r, xd, lbf.LBF_F32, outs=ys) for r in rot]
+    step = lambda i: calls[i % copies]()
+    ms_step = time_region(torch, step, args.steps, args.warmup)
     alg = sum(algorithmic_bytes(b, 1, 4) for b in blobs)
-    achieved = alg / (ms_launch * 1e-3) / 1e9
+    achieved = alg / (ms_step * 1e-3) / 1e9
     value = 2.0 * n_weights / (ms_step * 1e-3) / 1e9
-    log("step %.2f us, launch mean %.2f us (median %.2f): %.1f GB/s BF16-equiv, %.1f GB/s algorithmic (%.1f %% of 8 TB/s)"
-        % (ms_step * 1e3, ms_launch * 1e3, ms_launch_med * 1e3, value, achieved, 100 * achieved / HBM_PEAK_GBS))
+    log("launch mean %.2f us: %.1f GB/s BF16-equiv, %.1f GB/s algorithmic (%.1f %% of 8 TB/s)"
+        % (ms_step * 1e3, value, achieved, 100 * achieved / HBM_PEAK_GBS))
 
     traffic = None
     if os.path.exists(COUNTERS):
@@ -174,8 +232,8 @@ def main():
                    "bits_per_weight": round(8.0 * layer_blob_bytes / n_weights, 4), "rotation_copies": copies},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "k_gemv<1,8>", "algorithmic_bytes_per_launch": alg,
-                     "launch_ms_mean": round(ms_launch, 5), "launch_ms_median": round(ms_launch_med, 5)},
+                     "kernel": KERNEL, "algorithmic_bytes_per_launch": alg,
+                     "launch_ms_mean": round(ms_step, 5)},
     }
 
     if args.extras:
@@ -188,41 +246,45 @@ def main():
 
 
 def extras(torch, lbf, synth, Ws, blobs, rot, copies, args):
+    """Context lines beside the headline: standalone decode of the layer, the
+    uncompressed BF16 layer through torch's F.linear, and a batch sweep of the
+    fused product on gate_proj alone."""
     res = {}
-    # standalone decode of the layer: reads the planes, writes 2 bytes per weight
     outs = [torch.empty((b.rows, b.cols), dtype=torch.bfloat16, device="cuda") for b in blobs]
 
     def dec(i):
         for b, o in zip(rot[i % copies], outs):
             lbf.decode(b, out=o)
 
-    ms, _, _ = time_launches(torch, dec, 20, 3)
+    ms = time_region(torch, dec, 20, 3)
     n = sum(W.size for W in Ws)
     alg = sum(algorithmic_bytes(b, 0, 0) for b in blobs) + 2 * n
     res["decode_layer"] = {"us": round(ms * 1e3, 2), "bf16_equiv_GBs": round(2 * n / (ms * 1e-3) / 1e9, 1),
                            "hbm_GBs": round(alg / (ms * 1e-3) / 1e9, 1)}
-    # raw BF16 lane: torch F.linear over the same layer, uncompressed weights
+    del outs
     wd = [dev(torch, W) for W in Ws]
     xd = [dev(torch, synth.layer_x(m)) for m in range(len(Ws))]
-    wrot = [wd] + [[w.clone() for w in wd] for _ in range(1)]
+    wrot = [wd] + [[w.clone() for w in wd] for _ in range(3)]
 
     def raw(i):
-        for w, x in zip(wrot[i % 2], xd):
+        for w, x in zip(wrot[i % 4], xd):
             torch.nn.functional.linear(x, w)
 
-    ms, _, _ = time_launches(torch, raw, 20, 3)
-    res["raw_bf16_linear_layer"] = {"us": round(ms * 1e3, 2), "GBs": round(2 * n / (ms * 1e-3) / 1e9, 1)}
-    # gate_proj batch sweep
+    ms = time_region(torch, raw, 20, 3)
+    res["raw_bf16_linear_layer"] = {"us": round(ms * 1e3, 2), "GBs": round(2 * n / (ms * 1e-3) / 1e9, 1),
+                                    "hbm_frac": round(2 * n / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del wd, wrot
+    torch.cuda.empty_cache()
     g = synth.GATE
     sweep = {}
     for batch in (1, 2, 4, 8):
         x = dev(torch, synth.gate_batch_x(batch))
         y = torch.empty((batch, blobs[g].rows), dtype=torch.bfloat16, device="cuda")
-        f = lambda i: lbf.gemv(rot[i % copies][g], x, lbf.LBF_BF16, outs=y)
-        ms_s, ms_l, _ = time_launches(torch, f, 30, 5)
+        calls = [lbf.prepare(r[g], x, lbf.LBF_BF16, outs=y) for r in rot]
+        ms = time_region(torch, lambda i: calls[i % copies](), 30, 5)
         alg = algorithmic_bytes(blobs[g], batch, 2)
-        sweep[str(batch)] = {"us": round(ms_l * 1e3, 2), "bf16_equiv_GBs": round(2 * Ws[g].size / (ms_l * 1e-3) / 1e9, 1),
-                             "hbm_frac": round(alg / (ms_l * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        sweep[str(batch)] = {"us": round(ms * 1e3, 2), "bf16_equiv_GBs": round(2 * Ws[g].size / (ms * 1e-3) / 1e9, 1),
+                             "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     res["gate_proj_sweep"] = sweep
     return res
 

@@ -200,25 +200,53 @@ def decode(blob: Blob, out=None, stream=None):
     return out
 
 
+class Prepared:
+    """One fused product with its arguments marshalled once: each call is a
+    single lbf_gemv / lbf_gemm call on the stream captured at preparation.
+    Holds references to every tensor it points at."""
+
+    def __init__(self, fn, what, blobs: Sequence[Blob], xs, y_dtype, outs, stream):
+        torch = _torch()
+        n = len(blobs)
+        if len(xs) != n:
+            raise ValueError("one x per blob")
+        batch = int(xs[0].shape[0])
+        xs = [x.contiguous() for x in xs]
+        for x, b in zip(xs, blobs):
+            if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[0] != batch or x.shape[1] != b.cols:
+                raise ValueError("x must be bfloat16 [batch, cols] with the same batch for every group")
+        tdt = torch.float32 if y_dtype == LBF_F32 else torch.bfloat16
+        if outs is None:
+            outs = [torch.empty((batch, b.rows), dtype=tdt, device=b.data.device) for b in blobs]
+        for y, b in zip(outs, blobs):
+            if y.dtype != tdt or not y.is_contiguous() or y.numel() != batch * b.rows:
+                raise ValueError("each output must be a contiguous %s tensor of batch * rows elements" % tdt)
+        self._keep = (list(blobs), xs, outs)
+        self.outs = outs
+        self._fn, self._what = fn, what
+        self._args = ((Desc * n)(*[b.desc for b in blobs]), (ctypes.c_void_p * n)(*[_ptr(b.data) for b in blobs]), n,
+                      (ctypes.c_void_p * n)(*[_ptr(x) for x in xs]), batch,
+                      (ctypes.c_void_p * n)(*[_ptr(y) for y in outs]), y_dtype, _stream(stream))
+
+    def __call__(self):
+        _check(self._fn(*self._args), self._what)
+        return self.outs
+
+
 def _product(fn, what, blobs: Sequence[Blob], xs, y_dtype, outs, stream):
-    torch = _torch()
-    n = len(blobs)
-    if len(xs) != n:
-        raise ValueError("one x per blob")
-    batch = int(xs[0].shape[0])
-    descs = (Desc * n)(*[b.desc for b in blobs])
-    pb = (ctypes.c_void_p * n)(*[_ptr(b.data) for b in blobs])
-    xs = [x.contiguous() for x in xs]
-    for x, b in zip(xs, blobs):
-        if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[0] != batch or x.shape[1] != b.cols:
-            raise ValueError("x must be bfloat16 [batch, cols] with the same batch for every group")
-    px = (ctypes.c_void_p * n)(*[_ptr(x) for x in xs])
-    tdt = torch.float32 if y_dtype == LBF_F32 else torch.bfloat16
-    if outs is None:
-        outs = [torch.empty((batch, b.rows), dtype=tdt, device=b.data.device) for b in blobs]
-    py = (ctypes.c_void_p * n)(*[_ptr(y) for y in outs])
-    _check(fn(descs, pb, n, px, batch, py, y_dtype, _stream(stream)), what)
-    return outs
+    return Prepared(fn, what, blobs, xs, y_dtype, outs, stream)()
+
+
+def prepare(blobs, xs, y_dtype: int = LBF_F32, outs=None, stream=None) -> Prepared:
+    """Marshal a grouped product once (gemv for batch 1..8, gemm above); the
+    returned object launches it when called."""
+    if isinstance(blobs, Blob):
+        blobs, xs = [blobs], [xs]
+        outs = None if outs is None else [outs]
+    b = int(xs[0].shape[0])
+    L = lib()
+    fn, what = (L.lbf_gemv, "lbf_gemv") if b <= 8 else (L.lbf_gemm, "lbf_gemm")
+    return Prepared(fn, what, blobs, xs, y_dtype, outs, stream)
 
 
 def gemv(blobs, xs, y_dtype: int = LBF_F32, outs=None, stream=None):
