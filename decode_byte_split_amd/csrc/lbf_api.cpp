@@ -238,6 +238,9 @@ static int product(bool mfma, const lbf_desc* descs, const void* const* d_blobs,
   std::vector<GemvGroup> groups;
   const int rc = build_groups(descs, d_blobs, n_groups, d_x, d_y, groups);
   if (rc) return rc;
+  if (mfma)
+    for (const GemvGroup& G : groups)
+      if (G.cols / LBF_TILE > kGemmMaxTiles) return LBF_E_UNSUPPORTED;
   for (int g0 = 0; g0 < n_groups; g0 += LBF_MAX_GROUPS) {
     const int cnt = std::min(LBF_MAX_GROUPS, n_groups - g0);
     const hipError_t e = mfma ? launch_gemm(groups.data() + g0, cnt, batch, y_dtype, s)

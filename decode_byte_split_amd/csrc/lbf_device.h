@@ -2,8 +2,8 @@
 // nibble-code expansion, exponent lookup, BF16 reassembly, escape placement
 // and wave-level integer prefix sums.
 //
-// Format (see include/lbf.h): per weight one raw byte (sign << 7 | mantissa)
-// and one 4-bit code; code c < 15 stands for exponent lut[c], code 15 takes
+// Format (see include/lbf.h): per weight one raw byte (mantissa << 1 | sign
+// of the pair partner) and one 4-bit code; code c < 15 stands for exponent lut[c], code 15 takes
 // the next byte of the tile's escape slice.  The pages this follows:
 // "Lossless LLM Weight Compression vs 8-bit GGUF" (wavect.io), sections
 // "What does 'lossless' mean for LLM weights?" (exact rebuild in registers
@@ -184,5 +184,35 @@ __device__ __forceinline__ u32x4 load_nt(const u32x4* p) { return __builtin_nont
 __device__ __forceinline__ u32x2 load_nt(const u32x2* p) { return __builtin_nontemporal_load(p); }
 
 __device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Plane addresses of a format-v1 blob with n_tiles tiles (header 256 bytes,
+// raw and nibble planes back to back, index, escapes at the next 256 boundary).
+struct Planes {
+  const uint8_t *raw, *nib, *esc;
+  const uint32_t* idx;
+};
+__device__ __forceinline__ Planes planes_of(const uint8_t* blob, uint64_t n_tiles) {
+  Planes P;
+  P.raw = blob + 256;
+  P.nib = P.raw + n_tiles * kTile;
+  P.idx = reinterpret_cast<const uint32_t*>(P.nib + n_tiles * (kTile / 2));
+  P.esc = blob + ((256 + n_tiles * (kTile + kTile / 2) + 4 * (n_tiles + 1) + 255) & ~uint64_t(255));
+  return P;
+}
+
+// Raw buffer resource over [base, base + bytes): loads at or past the end
+// return 0 and stores there are dropped, without touching memory.
+constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer access on gfx9
+constexpr int kNonTemporal = 2;         // cache policy: streaming
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays NaN (quiet, sign kept).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
 
 }  // namespace lbf

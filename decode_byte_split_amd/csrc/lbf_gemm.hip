@@ -1,11 +1,325 @@
-// lbf_gemm.hip — fused decode + matrix product on bf16 MFMA for batch >= 9.
+// lbf_gemm.hip — fused decode + matrix product on bf16 MFMA for batch 9..256.
+//
+// Y[b, r] = sum_k W[r, k] X[b, k] with W decoded straight into the A operand
+// of v_mfma_f32_16x16x32_bf16 (fp32 accumulation); nothing decoded touches
+// memory.  (Coded weights stay in GPU memory and are rebuilt exactly in
+// registers right before the multiply: "Lossless LLM Weight Compression vs
+// 8-bit GGUF", section "What does 'lossless' mean for LLM weights?"; a fused
+// decompression-GEMM is the prior art named in "How does this compare with
+// prior lossless systems?".)
+//
+// At these batch sizes the product is still bound by reading the coded
+// weights (2B flops per ~1.5 bytes), so the kernel is laid out like a stream:
+//  - a workgroup is 4 waves; each wave owns one block of 16 rows for the
+//    whole K and keeps the batch (up to 64 columns, 4 blocks of 16) in fp32
+//    accumulators;
+//  - MFMA operand layout (16x16x32): lane l holds A[l % 16][8 (l / 16) + s]
+//    and B[8 (l / 16) + s][l % 16], s = 0..7, and D[4 (l / 16) + s][l % 16],
+//    s = 0..3.  The sum over k does not care which physical column sits in
+//    which k slot, so each lane loads the coded chunk it needs directly: lane
+//    (i, q) = (l % 16, l / 16) of step k takes the 16-weight chunk
+//    16 (k % 4) + 4 j + q (j = 0..3) of tile k / 4 of row i — per load
+//    instruction 64 contiguous raw bytes of each of the 16 rows — and the x
+//    operand is read from LDS with the same column order;
+//  - a wave's 16 rows are 16 T consecutive tiles, so its tile index words and
+//    its whole escape slice are contiguous: both are staged in LDS once, and
+//    every tile's escape count and first escape come from there.  A tile
+//    whose escapes all carry one exponent (0, 1, or 2 equal ones: nearly all
+//    of them for trained weights) puts that exponent into the lane's own LUT
+//    slot 15 and needs no ranking; otherwise the lane ranks its escapes
+//    across the 4 lanes of its row with ds_bpermute and patches them from LDS;
+//  - x is staged per step (256 columns of every batch row) into LDS, padded
+//    so the 16-byte operand reads are conflict-free, double-buffered with one
+//    barrier per step;  the coded chunks run through a ring of three register
+//    slots (two steps in flight), every load issued unconditionally (invalid
+//    ones go out of the buffer range and return 0).
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
 
 #include "lbf_device.h"
 #include "lbf_internal.h"
 
 namespace lbf {
 
-hipError_t launch_gemm(const GemvGroup*, int, int, int, hipStream_t) { return hipErrorNotSupported; }
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr int kGemmWaves = 4;
+constexpr int kGemmRows = 16 * kGemmWaves;     // rows per workgroup
+constexpr int kGemmBatch = 64;                 // batch columns per launch
+constexpr int kStepK = 256;                    // columns per pipeline step
+constexpr int kXStride = kStepK * 2 + 16;      // LDS bytes per staged x row
+constexpr uint32_t kEscCap = 2048;             // escape bytes per wave held in LDS
+constexpr uint32_t kOOB = 0x80000000u;         // a buffer offset past every range used here (all < 2^31)
+
+struct GemmLaunch {
+  GemvGroup g[LBF_MAX_GROUPS];
+  uint32_t wg_begin[LBF_MAX_GROUPS + 1];  // first workgroup of each group
+  uint32_t idx_bytes;                     // LDS bytes per wave for index words
+  int n_groups, batch, y_bf16;
+};
+
+struct GSlot {
+  u32x4 raw[4];
+  u32x2 nib[4];
+};
+
+template <int NB>
+__global__ __launch_bounds__(kGemmWaves * kWave) void k_gemm(GemmLaunch L) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const uint32_t wave = uniform(threadIdx.x >> 6);
+  const int lane = lane_id();
+  const uint32_t li = (uint32_t)lane & 15u, lq = (uint32_t)lane >> 4;
+
+  uint32_t g = 0;
+  while (g + 1 < (uint32_t)L.n_groups && L.wg_begin[g + 1] <= blockIdx.x) g++;
+  const GemvGroup& G = L.g[g];
+  const uint32_t T = G.cols >> 10;
+  const uint64_t n_tiles = (uint64_t)G.rows * T;
+  const Planes P = planes_of(G.blob, n_tiles);
+  const uint32_t r0 = (blockIdx.x - L.wg_begin[g]) * kGemmRows + wave * 16u;
+  const uint32_t rows_here = r0 < G.rows ? min(16u, G.rows - r0) : 0u;
+  const uint32_t tiles_here = rows_here * T;
+  const uint64_t t_first = (uint64_t)r0 * T;
+
+  uint8_t* xs = smem;  // [2][NB * 16][kXStride]
+  uint8_t* wl = smem + 2 * NB * 16 * kXStride + wave * (L.idx_bytes + kEscCap);
+  uint32_t* idx_l = reinterpret_cast<uint32_t*>(wl);
+  uint8_t* esc_l = wl + L.idx_bytes;
+
+  const uint32_t n_steps = 4 * T;
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(P.raw + t_first * kTile, tiles_here * kTile);
+  const __amdgpu_buffer_rsrc_t rn = make_rsrc(P.nib + t_first * (kTile / 2), tiles_here * (kTile / 2));
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(G.x, (uint32_t)L.batch * G.cols * 2);
+
+  // coded chunks of step k: lane (li, lq), chunk j -> tile k / 4 of row li,
+  // 16-weight chunk 16 (k % 4) + 4 j + lq
+  auto load_step = [&](GSlot& S, uint32_t k) {
+    const bool ok = k < n_steps;
+    const uint32_t tile = li * T + (k >> 2);
+    const uint32_t ch0 = 16u * (k & 3u) + lq;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const uint32_t ch = ch0 + 4u * j;
+      const uint32_t orw = ok ? tile * kTile + ch * 16u : kOOB;
+      const uint32_t onb = ok ? tile * (kTile / 2) + ch * 8u : kOOB;
+      S.raw[j] = __builtin_amdgcn_raw_buffer_load_b128(rr, orw, 0, kNonTemporal);
+      S.nib[j] = __builtin_amdgcn_raw_buffer_load_b64(rn, onb, 0, kNonTemporal);
+    }
+  };
+  // x columns [256 k, 256 k + 256) of batch rows 0 .. 16 NB - 1: piece
+  // p = 256 m + threadIdx.x is row p / 32, bytes 16 (p % 32) of the step
+  u32x4 xr[NB * 2];
+  auto load_x = [&](uint32_t k) {
+    const bool ok = k < n_steps;
+#pragma unroll
+    for (int m = 0; m < NB * 2; m++) {
+      const uint32_t p = 256u * m + threadIdx.x;
+      const uint32_t o = ok ? (p >> 5) * G.cols * 2 + k * (kStepK * 2) + (p & 31u) * 16u : kOOB;
+      xr[m] = __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, kNonTemporal);
+    }
+  };
+  auto store_x = [&](uint32_t buf) {
+    uint8_t* d = xs + buf * (NB * 16 * kXStride);
+#pragma unroll
+    for (int m = 0; m < NB * 2; m++) {
+      const uint32_t p = 256u * m + threadIdx.x;
+      *reinterpret_cast<u32x4*>(d + (p >> 5) * kXStride + (p & 31u) * 16u) = xr[m];
+    }
+  };
+
+  GSlot s0, s1, s2;
+  load_step(s0, 0);
+  load_step(s1, 1);
+  load_x(0);
+
+  // this wave's index words idx[t_first .. t_first + tiles_here] and escape
+  // bytes, clamped to the stream so a corrupt index stays in bounds
+  uint32_t e_lo = 0, e_hi = 0, a0 = 0;
+  bool dense = false;
+  if (rows_here) {
+    for (uint32_t w = (uint32_t)lane; w <= tiles_here; w += kWave) idx_l[w] = min(P.idx[t_first + w], G.n_esc);
+    wave_lds_sync();
+    e_lo = idx_l[0];
+    e_hi = max(idx_l[tiles_here], e_lo);
+    a0 = e_lo & ~3u;
+    dense = e_hi - a0 > kEscCap;
+    if (!dense) {
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(P.esc + a0);
+      const uint32_t nw = (e_hi - a0 + 3) >> 2;
+      for (uint32_t w = (uint32_t)lane; w < nw; w += kWave) reinterpret_cast<uint32_t*>(esc_l)[w] = src[w];
+    }
+  }
+  store_x(0);
+  __syncthreads();
+
+  f32x4 acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; nb++) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // per tile: first escape (absolute), count, the lane's LUT word 3 and
+  // whether any row of the wave needs ranked escapes
+  uint32_t t_ia = 0, t_cnt = 0, t3 = G.lut[3], run = 0;
+  bool any_slow = false, fast = true;
+  auto esc_at = [&](uint32_t pos) -> uint32_t {  // pos absolute, in [e_lo, e_hi)
+    return dense ? (uint32_t)P.esc[pos] : (uint32_t)esc_l[pos - a0];
+  };
+
+  auto step = [&](GSlot& cur, GSlot& nx2, uint32_t k) {
+    load_step(nx2, k + 2);
+    load_x(k + 1);
+    if ((k & 3u) == 0) {
+      const uint32_t c = k >> 2;
+      uint32_t ia = e_lo, ib = e_lo;
+      if (li < rows_here) {
+        ia = min(max(idx_l[li * T + c], e_lo), e_hi);
+        ib = min(max(idx_l[li * T + c + 1], ia), e_hi);
+      }
+      t_ia = ia;
+      t_cnt = ib - ia;
+      const uint32_t e1 = t_cnt ? esc_at(ia) : 0u;
+      const uint32_t e2 = t_cnt > 1 ? esc_at(ia + 1) : e1;
+      fast = t_cnt == 0 || (t_cnt <= 2 && e1 == e2);
+      t3 = fast ? ((G.lut[3] & 0x00FFFFFFu) | (e1 << 24)) : G.lut[3];
+      any_slow = __builtin_amdgcn_ballot_w64(!fast) != 0;
+      run = 0;
+    }
+    const Lut lut{G.lut[0], G.lut[1], G.lut[2], t3};
+    const uint8_t* xb = xs + (k & 1u) * (NB * 16 * kXStride) + li * kXStride + lq * 32u;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      uint32_t E[4];
+      exponents16<false>(cur.nib[j], lut, 0u, E);
+      if (any_slow) {
+        uint64_t m0 = fast ? 0 : escape_mask8(cur.nib[j].x);
+        uint64_t m1 = fast ? 0 : escape_mask8(cur.nib[j].y);
+        const uint32_t cl = (uint32_t)(__builtin_popcountll(m0) + __builtin_popcountll(m1));
+        uint32_t pre = 0, tot = 0;
+#pragma unroll
+        for (uint32_t q = 0; q < 4; q++) {
+          const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((li + 16u * q) * 4u), (int)cl);
+          pre += q < lq ? v : 0u;
+          tot += v;
+        }
+        uint32_t pos = run + pre;
+        run += tot;
+        while (m0) {
+          const uint32_t w = (uint32_t)__builtin_ctzll(m0) >> 3;
+          patch_exponent(E, w, pos < t_cnt ? esc_at(t_ia + pos) : 0u);
+          m0 &= m0 - 1;
+          pos++;
+        }
+        while (m1) {
+          const uint32_t w = 8u + ((uint32_t)__builtin_ctzll(m1) >> 3);
+          patch_exponent(E, w, pos < t_cnt ? esc_at(t_ia + pos) : 0u);
+          m1 &= m1 - 1;
+          pos++;
+        }
+      }
+      uint32_t w[8];
+      assemble16(cur.raw[j], E, w);
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{w[4 * h], w[4 * h + 1], w[4 * h + 2], w[4 * h + 3]});
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++) {
+          const u32x4 xv = *reinterpret_cast<const u32x4*>(xb + nb * 16 * kXStride + j * 128 + h * 16);
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, xv), acc[nb], 0, 0, 0);
+        }
+      }
+    }
+    store_x((k + 1) & 1u);
+    __syncthreads();
+  };
+
+  for (uint32_t k = 0; k < n_steps; k += 3) {
+    step(s0, s2, k);
+    if (k + 1 < n_steps) step(s1, s0, k + 1);
+    if (k + 2 < n_steps) step(s2, s1, k + 2);
+  }
+
+  // lane (li, lq) of block nb holds Y[nb*16 + li][r0 + 4 lq + s], s = 0..3;
+  // values and offsets are formed first, the stores follow in straight-line
+  // code (one branch on the output type, outside the loops)
+  const uint32_t eb = L.y_bf16 ? 2u : 4u;
+  const __amdgpu_buffer_rsrc_t ry = make_rsrc(G.y, (uint32_t)L.batch * G.rows * eb);
+  uint32_t off[NB][4], val[NB][4];
+#pragma unroll
+  for (int nb = 0; nb < NB; nb++) {
+    const uint32_t b = nb * 16u + li;
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+      const uint32_t r = r0 + 4u * lq + s;
+      off[nb][s] = (b < (uint32_t)L.batch && r < G.rows) ? (b * G.rows + r) * eb : kOOB;
+      const float v = acc[nb][s];  // element copy first: a bit_cast of acc[nb][s] itself reads element 0
+      val[nb][s] = __builtin_bit_cast(uint32_t, v);
+    }
+  }
+  if (L.y_bf16) {
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+      for (int s = 0; s < 4; s++)
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(__builtin_bit_cast(float, val[nb][s])), ry, off[nb][s], 0, 0);
+  } else {
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+      for (int s = 0; s < 4; s++) __builtin_amdgcn_raw_buffer_store_b32(val[nb][s], ry, off[nb][s], 0, 0);
+  }
+}
+
+// Largest dynamic LDS size each kernel instance was opened up to.
+static std::atomic<int> g_lds_set[4];
+
+template <int NB>
+static hipError_t run_gemm(const GemmLaunch& L, uint32_t grid, hipStream_t s) {
+  const int lds = 2 * NB * 16 * kXStride + kGemmWaves * (int)(L.idx_bytes + kEscCap);
+  if (g_lds_set[NB - 1].load(std::memory_order_relaxed) < lds) {
+    const hipError_t e =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<NB>), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    g_lds_set[NB - 1].store(lds, std::memory_order_relaxed);
+  }
+  hipLaunchKernelGGL((k_gemm<NB>), dim3(grid), dim3(kGemmWaves * kWave), lds, s, L);
+  return hipGetLastError();
+}
+
+// Batch columns go in slabs of up to 64 (each slab re-reads the coded
+// weights); a slab of m columns runs ceil(m / 16) MFMA column blocks.
+hipError_t launch_gemm(const GemvGroup* groups, int n_groups, int batch, int y_dtype, hipStream_t s) {
+  const uint32_t eb = y_dtype == LBF_BF16 ? 2u : 4u;
+  for (int b0 = 0; b0 < batch; b0 += kGemmBatch) {
+    const int nb = std::min(kGemmBatch, batch - b0);
+    GemmLaunch L;
+    L.n_groups = n_groups;
+    L.batch = nb;
+    L.y_bf16 = y_dtype == LBF_BF16;
+    uint32_t wg = 0, t_max = 1;
+    for (int g = 0; g < n_groups; g++) {
+      GemvGroup G = groups[g];
+      if ((G.cols >> 10) > kGemmMaxTiles) return hipErrorNotSupported;
+      G.x += (size_t)b0 * G.cols;
+      G.y = static_cast<uint8_t*>(G.y) + (size_t)b0 * G.rows * eb;
+      L.g[g] = G;
+      L.wg_begin[g] = wg;
+      wg += (G.rows + kGemmRows - 1) / kGemmRows;
+      t_max = std::max(t_max, G.cols >> 10);
+    }
+    L.wg_begin[n_groups] = wg;
+    L.idx_bytes = (4 * (16 * t_max + 1) + 15) & ~15u;
+    hipError_t e;
+    switch ((nb + 15) / 16) {
+      case 1: e = run_gemm<1>(L, wg, s); break;
+      case 2: e = run_gemm<2>(L, wg, s); break;
+      case 3: e = run_gemm<3>(L, wg, s); break;
+      default: e = run_gemm<4>(L, wg, s); break;
+    }
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
 
 }  // namespace lbf

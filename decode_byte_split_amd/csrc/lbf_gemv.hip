@@ -60,12 +60,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (r0 + r1) + (r2 + r3);
 }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);  // quiet NaN, sign kept
-  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-}
-
 template <int B>
 __device__ __forceinline__ void dot16(const uint32_t w[8], const uint32_t (*xr)[8], float acc[B][2]) {
 #pragma unroll
@@ -94,13 +88,6 @@ struct RowBuf {
 // memory access) and need no per-row vector address arithmetic, so the
 // compiler counts outstanding loads exactly and keeps the next row in flight
 // while the current one is decoded.
-constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer access on gfx9
-constexpr int kNonTemporal = 2;         // cache policy: streaming
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
-}
-
 template <int SMAX>
 __device__ __forceinline__ void load_row(RowBuf<SMAX>& R, const uint8_t* raw_p, const uint8_t* nib_p,
                                          const uint32_t* idx_p, uint64_t t0, uint32_t S, int lane) {
@@ -633,19 +620,8 @@ struct Pos {
   bool valid;
 };
 
-struct GroupPtrs {
-  const uint8_t *raw, *nib, *esc;
-  const uint32_t* idx;
-};
-
-__device__ __forceinline__ GroupPtrs ptrs_of(const GemvGroup& G) {
-  const uint64_t n_tiles = (uint64_t)G.rows * (G.cols >> 10);
-  GroupPtrs P;
-  P.raw = G.blob + LBF_HEADER_BYTES;
-  P.nib = P.raw + n_tiles * kTile;
-  P.idx = reinterpret_cast<const uint32_t*>(P.nib + n_tiles * (kTile / 2));
-  P.esc = G.blob + ((LBF_HEADER_BYTES + n_tiles * (kTile + kTile / 2) + 4 * (n_tiles + 1) + 255) & ~uint64_t(255));
-  return P;
+__device__ __forceinline__ Planes ptrs_of(const GemvGroup& G) {
+  return planes_of(G.blob, (uint64_t)G.rows * (G.cols >> 10));
 }
 
 __device__ __forceinline__ Pos row_pos(const RingLaunch& L, uint32_t q) {
@@ -665,7 +641,7 @@ __device__ __forceinline__ Pos row_pos(const RingLaunch& L, uint32_t q) {
 __device__ __forceinline__ uint64_t tile_of(const Pos& p) { return (uint64_t)p.r * p.T + p.c; }
 
 __device__ __forceinline__ void load_idx(Slot& s, const RingLaunch& L, const Pos& p, int lane) {
-  const GroupPtrs P = ptrs_of(L.g[p.g]);
+  const Planes P = ptrs_of(L.g[p.g]);
   const __amdgpu_buffer_rsrc_t r = make_rsrc(P.idx + tile_of(p), p.valid ? (p.S + 1) * 4 : 0u);
   s.idxv = __builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)lane * 4, 0, 0);
 }
@@ -674,7 +650,7 @@ __device__ __forceinline__ void load_idx(Slot& s, const RingLaunch& L, const Pos
 __device__ __forceinline__ void load_data(Slot& s, const RingLaunch& L, const Pos& p, uint32_t& e_first,
                                           uint32_t& e_cnt, int lane) {
   const GemvGroup& G = L.g[p.g];
-  const GroupPtrs P = ptrs_of(G);
+  const Planes P = ptrs_of(G);
   const uint32_t hi = min((uint32_t)__builtin_amdgcn_readlane((int)s.idxv, (int)p.S), G.n_esc);
   e_first = min((uint32_t)__builtin_amdgcn_readlane((int)s.idxv, 0), hi);
   e_cnt = p.valid ? hi - e_first : 0u;
@@ -800,7 +776,7 @@ __global__ __launch_bounds__(kRingWaves * kWave) void k_gemv_ring(RingLaunch L) 
     load_idx(nx2, L, p2, lane);
     load_data(nx1, L, p1, f1, n1, lane);
     const GemvGroup& G = L.g[p0.g];
-    const GroupPtrs P = ptrs_of(G);
+    const Planes P = ptrs_of(G);
     const uint8_t* x_g = smem + L.x_off[p0.g];
     slot_lds[lane] = (uint8_t)cur.escv;  // the chunk's escapes, for the patch path
     wave_lds_sync();

@@ -47,6 +47,10 @@ struct GemvGroup {
 hipError_t launch_gemv(const GemvGroup* groups, int n_groups, int batch, int y_dtype, hipStream_t s);
 hipError_t launch_gemm(const GemvGroup* groups, int n_groups, int batch, int y_dtype, hipStream_t s);
 
+// lbf_gemm stages each wave's tile index words (16 rows x cols / 1024 tiles)
+// in LDS; rows longer than this many tiles are not supported.
+constexpr uint32_t kGemmMaxTiles = 64;
+
 // Workspace layout of lbf_encode: hist[256] u32, then tile counts u32[n_tiles].
 constexpr uint64_t kWorkHistBytes = 1024;
 

@@ -153,7 +153,12 @@ int lbf_gemv(const lbf_desc* descs, const void* const* d_blobs, int n_groups, co
 /*
  * lbf_gemm — the same product for batch >= 9, on bf16 MFMA (matrix cores)
  * with fp32 accumulation; the decoded weights go straight into the MFMA
- * operand registers.  Arguments as lbf_gemv; batch 9..256.
+ * operand registers and are never written to memory.  (Same page, section
+ * "How does this compare with prior lossless systems?": a fused
+ * decompression-GEMM.)  Arguments and layouts as lbf_gemv; batch 9..256
+ * (LBF_E_INVAL otherwise).  Requires cols_g % 1024 == 0 (LBF_E_SHAPE) and
+ * cols_g <= 65536 (LBF_E_UNSUPPORTED).  Batches above 64 run as several
+ * launches of up to 64 columns, each reading the coded weights once.
  */
 int lbf_gemm(const lbf_desc* descs, const void* const* d_blobs, int n_groups, const void* const* d_x,
              int batch, void* const* d_y, int y_dtype, hipStream_t s);

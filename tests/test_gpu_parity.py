@@ -14,32 +14,14 @@ import pytest
 
 from oracle import oracle as O
 from decode_byte_split_amd import synth
+from gpu_util import check_product, dev, host, make_env, say
 
 pytestmark = pytest.mark.gpu
 
 
-def say(msg):
-    sys.stdout.write("[gpu-parity] %s\n" % msg)
-    sys.stdout.flush()
-
-
 @pytest.fixture(scope="module")
 def env():
-    import torch
-    from decode_byte_split_amd import lbf
-
-    assert torch.cuda.is_available(), "GPU tests need a GPU"
-    lbf.lib()
-    return torch, lbf
-
-
-def dev(torch, a: np.ndarray):
-    """uint16 bf16 patterns (numpy) -> torch.bfloat16 on the GPU."""
-    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
-
-
-def host(t) -> np.ndarray:
-    return t.view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+    return make_env()
 
 
 def tensors():
@@ -113,21 +95,6 @@ def test_decode_leaves_neighbours_untouched(env):
     h = buf.cpu().numpy()
     assert (h[:guard] == -12345).all() and (h[guard + n:] == -12345).all()
     assert np.array_equal(h[guard:guard + n].view(np.uint16).reshape(7, 333), W)
-
-
-def check_product(y_gpu, y_ref, a_ref, bf16_out):
-    y = y_gpu.float().cpu().numpy().astype(np.float64)
-    fin = np.isfinite(y_ref)
-    # non-finite reference entries: same class on the GPU
-    assert np.array_equal(np.isnan(y[~fin]), np.isnan(y_ref[~fin]))
-    inf = np.isinf(y_ref)
-    assert np.array_equal(y[inf], y_ref[inf])
-    tol = 1e-3 * a_ref[fin]
-    if bf16_out:
-        tol = tol + 2.0 ** -8 * np.abs(y_ref[fin])
-    err = np.abs(y[fin] - y_ref[fin])
-    worst = np.max(err - tol) if err.size else -1
-    assert np.all(err <= tol), "max excess %g" % worst
 
 
 @pytest.mark.parametrize("batch", [1, 2, 3, 4, 5, 8])

@@ -117,6 +117,9 @@ def test_calls_validate_before_touching_the_gpu():
     assert L.lbf_gemv(good, p, 1, p, 9, p, 0, None) == lbf.LBF_E_INVAL  # batch 9 is not a GEMV
     assert L.lbf_gemv(good, p, 1, p, 1, p, 7, None) == lbf.LBF_E_INVAL  # unknown output type
     assert L.lbf_gemm(good, p, 1, p, 8, p, 0, None) == lbf.LBF_E_INVAL
+    assert L.lbf_gemm(good, p, 1, p, 257, p, 0, None) == lbf.LBF_E_INVAL
+    wide = _oracle_desc(np.zeros((1, 65536 + 1024), dtype=np.uint16))[0]  # 65 tiles per row
+    assert L.lbf_gemm((lbf.Desc * 1)(wide), p, 1, p, 16, p, 0, None) == lbf.LBF_E_UNSUPPORTED
     misaligned = (ctypes.c_void_p * 1)(256 + 8)
     assert L.lbf_gemv(good, misaligned, 1, p, 1, p, 0, None) == lbf.LBF_E_ALIGN
     small = _oracle_desc(np.zeros((3, 5), dtype=np.uint16))[0]
