@@ -277,14 +277,21 @@ def extras(torch, lbf, synth, Ws, blobs, rot, copies, args):
     torch.cuda.empty_cache()
     g = synth.GATE
     sweep = {}
-    for batch in (1, 2, 4, 8):
+    wg = [dev(torch, Ws[g])] + [dev(torch, Ws[g]) for _ in range(3)]
+    for batch in (1, 2, 4, 8, 16, 32, 64):
         x = dev(torch, synth.gate_batch_x(batch))
         y = torch.empty((batch, blobs[g].rows), dtype=torch.bfloat16, device="cuda")
         calls = [lbf.prepare(r[g], x, lbf.LBF_BF16, outs=y) for r in rot]
         ms = time_region(torch, lambda i: calls[i % copies](), 30, 5)
         alg = algorithmic_bytes(blobs[g], batch, 2)
-        sweep[str(batch)] = {"us": round(ms * 1e3, 2), "bf16_equiv_GBs": round(2 * Ws[g].size / (ms * 1e-3) / 1e9, 1),
-                             "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        flops = 2.0 * batch * Ws[g].size
+        ms_raw = time_region(torch, lambda i: torch.nn.functional.linear(x, wg[i % 4]), 30, 5)
+        sweep[str(batch)] = {"path": "gemv" if batch <= 8 else "gemm_mfma", "us": round(ms * 1e3, 2),
+                             "bf16_equiv_GBs": round(2 * Ws[g].size / (ms * 1e-3) / 1e9, 1),
+                             "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                             "mfma_frac_of_2.5PF": round(flops / (ms * 1e-3) / 2.5e15, 4) if batch > 8 else None,
+                             "raw_bf16_linear_us": round(ms_raw * 1e3, 2)}
+    del wg
     res["gate_proj_sweep"] = sweep
     return res
 

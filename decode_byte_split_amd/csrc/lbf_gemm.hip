@@ -30,13 +30,15 @@
 //    across the 4 lanes of its row with ds_bpermute and patches them from LDS;
 //  - x is staged per step (256 columns of every batch row) into LDS, padded
 //    so the 16-byte operand reads are conflict-free, double-buffered with one
-//    barrier per step;  the coded chunks run through a ring of three register
-//    slots (two steps in flight), every load issued unconditionally (invalid
-//    ones go out of the buffer range and return 0).
+//    barrier per step, and loaded two steps ahead through two register sets;
+//    the coded chunks run through a ring of four register slots (three steps
+//    in flight); every load is issued unconditionally (invalid ones go out of
+//    the buffer range and return 0).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "lbf_device.h"
 #include "lbf_internal.h"
@@ -105,35 +107,43 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void k_gemm(GemmLaunch L) {
       const uint32_t ch = ch0 + 4u * j;
       const uint32_t orw = ok ? tile * kTile + ch * 16u : kOOB;
       const uint32_t onb = ok ? tile * (kTile / 2) + ch * 8u : kOOB;
-      S.raw[j] = __builtin_amdgcn_raw_buffer_load_b128(rr, orw, 0, kNonTemporal);
-      S.nib[j] = __builtin_amdgcn_raw_buffer_load_b64(rn, onb, 0, kNonTemporal);
+      // default cache policy: a row's 128-byte lines are read by two or four
+      // consecutive load instructions
+      S.raw[j] = __builtin_amdgcn_raw_buffer_load_b128(rr, orw, 0, 0);
+      S.nib[j] = __builtin_amdgcn_raw_buffer_load_b64(rn, onb, 0, 0);
     }
   };
   // x columns [256 k, 256 k + 256) of batch rows 0 .. 16 NB - 1: piece
   // p = 256 m + threadIdx.x is row p / 32, bytes 16 (p % 32) of the step
-  u32x4 xr[NB * 2];
-  auto load_x = [&](uint32_t k) {
+  struct XRegs {
+    u32x4 v[NB * 2];
+  };
+  auto load_x = [&](XRegs& xr, uint32_t k) {
     const bool ok = k < n_steps;
 #pragma unroll
     for (int m = 0; m < NB * 2; m++) {
       const uint32_t p = 256u * m + threadIdx.x;
       const uint32_t o = ok ? (p >> 5) * G.cols * 2 + k * (kStepK * 2) + (p & 31u) * 16u : kOOB;
-      xr[m] = __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, kNonTemporal);
+      xr.v[m] = __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, kNonTemporal);
     }
   };
-  auto store_x = [&](uint32_t buf) {
+  auto store_x = [&](const XRegs& xr, uint32_t buf) {
     uint8_t* d = xs + buf * (NB * 16 * kXStride);
 #pragma unroll
     for (int m = 0; m < NB * 2; m++) {
       const uint32_t p = 256u * m + threadIdx.x;
-      *reinterpret_cast<u32x4*>(d + (p >> 5) * kXStride + (p & 31u) * 16u) = xr[m];
+      *reinterpret_cast<u32x4*>(d + (p >> 5) * kXStride + (p & 31u) * 16u) = xr.v[m];
     }
   };
 
-  GSlot s0, s1, s2;
+  // issue order (loads retire in order): x 2 steps ahead, coded data 3
+  GSlot s0, s1, s2, s3;
+  XRegs xa, xb;
+  load_x(xa, 0);
   load_step(s0, 0);
+  load_x(xb, 1);
   load_step(s1, 1);
-  load_x(0);
+  load_step(s2, 2);
 
   // this wave's index words idx[t_first .. t_first + tiles_here] and escape
   // bytes, clamped to the stream so a corrupt index stays in bounds
@@ -152,7 +162,7 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void k_gemm(GemmLaunch L) {
       for (uint32_t w = (uint32_t)lane; w < nw; w += kWave) reinterpret_cast<uint32_t*>(esc_l)[w] = src[w];
     }
   }
-  store_x(0);
+  store_x(xa, 0);
   __syncthreads();
 
   f32x4 acc[NB];
@@ -163,82 +173,105 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void k_gemm(GemmLaunch L) {
   // whether any row of the wave needs ranked escapes
   uint32_t t_ia = 0, t_cnt = 0, t3 = G.lut[3], run = 0;
   bool any_slow = false, fast = true;
-  auto esc_at = [&](uint32_t pos) -> uint32_t {  // pos absolute, in [e_lo, e_hi)
-    return dense ? (uint32_t)P.esc[pos] : (uint32_t)esc_l[pos - a0];
-  };
+  // The main loop, instantiated twice: waves whose escape slice fits in LDS
+  // read escapes there only; the rest ("dense" slices) read them from
+  // memory.  Keeping the two apart leaves the common loop free of loads
+  // whose completion the compiler cannot count.  Both run the same barriers.
+  auto main_loop = [&](auto dense_tag) {
+    constexpr bool DENSE = decltype(dense_tag)::value;
+    auto esc_at = [&](uint32_t pos) -> uint32_t {  // pos absolute, in [e_lo, e_hi)
+      if constexpr (DENSE)
+        return (uint32_t)P.esc[pos];
+      else
+        return (uint32_t)esc_l[pos - a0];
+    };
 
-  auto step = [&](GSlot& cur, GSlot& nx2, uint32_t k) {
-    load_step(nx2, k + 2);
-    load_x(k + 1);
-    if ((k & 3u) == 0) {
-      const uint32_t c = k >> 2;
-      uint32_t ia = e_lo, ib = e_lo;
-      if (li < rows_here) {
-        ia = min(max(idx_l[li * T + c], e_lo), e_hi);
-        ib = min(max(idx_l[li * T + c + 1], ia), e_hi);
+    // step k: x of step k + 2 and coded data of step k + 3 are issued, step k
+    // is computed from slot `cur` and x buffer k % 2, and x of step k + 1
+    // (issued a step earlier) goes to x buffer (k + 1) % 2.  A tile starts
+    // every 4 steps (TILE_START).
+    auto step = [&](GSlot& cur, GSlot& nx3, XRegs& x_in, const XRegs& x_out, uint32_t k, auto tile_start) {
+      load_x(x_in, k + 2);
+      load_step(nx3, k + 3);
+      if constexpr (decltype(tile_start)::value) {
+        const uint32_t c = k >> 2;
+        uint32_t ia = e_lo, ib = e_lo;
+        if (li < rows_here) {
+          ia = min(max(idx_l[li * T + c], e_lo), e_hi);
+          ib = min(max(idx_l[li * T + c + 1], ia), e_hi);
+        }
+        t_ia = ia;
+        t_cnt = ib - ia;
+        const uint32_t e1 = t_cnt ? esc_at(ia) : 0u;
+        const uint32_t e2 = t_cnt > 1 ? esc_at(ia + 1) : e1;
+        fast = t_cnt == 0 || (t_cnt <= 2 && e1 == e2);
+        t3 = fast ? ((G.lut[3] & 0x00FFFFFFu) | (e1 << 24)) : G.lut[3];
+        any_slow = __builtin_amdgcn_ballot_w64(!fast) != 0;
+        run = 0;
       }
-      t_ia = ia;
-      t_cnt = ib - ia;
-      const uint32_t e1 = t_cnt ? esc_at(ia) : 0u;
-      const uint32_t e2 = t_cnt > 1 ? esc_at(ia + 1) : e1;
-      fast = t_cnt == 0 || (t_cnt <= 2 && e1 == e2);
-      t3 = fast ? ((G.lut[3] & 0x00FFFFFFu) | (e1 << 24)) : G.lut[3];
-      any_slow = __builtin_amdgcn_ballot_w64(!fast) != 0;
-      run = 0;
-    }
-    const Lut lut{G.lut[0], G.lut[1], G.lut[2], t3};
-    const uint8_t* xb = xs + (k & 1u) * (NB * 16 * kXStride) + li * kXStride + lq * 32u;
+      const Lut lut{G.lut[0], G.lut[1], G.lut[2], t3};
+      const uint8_t* xb = xs + (k & 1u) * (NB * 16 * kXStride) + li * kXStride + lq * 32u;
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      uint32_t E[4];
-      exponents16<false>(cur.nib[j], lut, 0u, E);
-      if (any_slow) {
-        uint64_t m0 = fast ? 0 : escape_mask8(cur.nib[j].x);
-        uint64_t m1 = fast ? 0 : escape_mask8(cur.nib[j].y);
-        const uint32_t cl = (uint32_t)(__builtin_popcountll(m0) + __builtin_popcountll(m1));
-        uint32_t pre = 0, tot = 0;
+      for (int j = 0; j < 4; j++) {
+        uint32_t E[4];
+        exponents16<false>(cur.nib[j], lut, 0u, E);
+        if (any_slow) {
+          uint64_t m0 = fast ? 0 : escape_mask8(cur.nib[j].x);
+          uint64_t m1 = fast ? 0 : escape_mask8(cur.nib[j].y);
+          const uint32_t cl = (uint32_t)(__builtin_popcountll(m0) + __builtin_popcountll(m1));
+          // most chunks of a ranked tile hold none of its escapes
+          if (__builtin_amdgcn_ballot_w64(cl != 0) != 0) {
+            uint32_t pre = 0, tot = 0;
 #pragma unroll
-        for (uint32_t q = 0; q < 4; q++) {
-          const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((li + 16u * q) * 4u), (int)cl);
-          pre += q < lq ? v : 0u;
-          tot += v;
+            for (uint32_t q = 0; q < 4; q++) {
+              const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((li + 16u * q) * 4u), (int)cl);
+              pre += q < lq ? v : 0u;
+              tot += v;
+            }
+            uint32_t pos = run + pre;
+            run += tot;
+            while (m0) {
+              const uint32_t w = (uint32_t)__builtin_ctzll(m0) >> 3;
+              patch_exponent(E, w, pos < t_cnt ? esc_at(t_ia + pos) : 0u);
+              m0 &= m0 - 1;
+              pos++;
+            }
+            while (m1) {
+              const uint32_t w = 8u + ((uint32_t)__builtin_ctzll(m1) >> 3);
+              patch_exponent(E, w, pos < t_cnt ? esc_at(t_ia + pos) : 0u);
+              m1 &= m1 - 1;
+              pos++;
+            }
+          }
         }
-        uint32_t pos = run + pre;
-        run += tot;
-        while (m0) {
-          const uint32_t w = (uint32_t)__builtin_ctzll(m0) >> 3;
-          patch_exponent(E, w, pos < t_cnt ? esc_at(t_ia + pos) : 0u);
-          m0 &= m0 - 1;
-          pos++;
-        }
-        while (m1) {
-          const uint32_t w = 8u + ((uint32_t)__builtin_ctzll(m1) >> 3);
-          patch_exponent(E, w, pos < t_cnt ? esc_at(t_ia + pos) : 0u);
-          m1 &= m1 - 1;
-          pos++;
-        }
-      }
-      uint32_t w[8];
-      assemble16(cur.raw[j], E, w);
+        uint32_t w[8];
+        assemble16(cur.raw[j], E, w);
 #pragma unroll
-      for (int h = 0; h < 2; h++) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{w[4 * h], w[4 * h + 1], w[4 * h + 2], w[4 * h + 3]});
+        for (int h = 0; h < 2; h++) {
+          const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{w[4 * h], w[4 * h + 1], w[4 * h + 2], w[4 * h + 3]});
 #pragma unroll
-        for (int nb = 0; nb < NB; nb++) {
-          const u32x4 xv = *reinterpret_cast<const u32x4*>(xb + nb * 16 * kXStride + j * 128 + h * 16);
-          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, xv), acc[nb], 0, 0, 0);
+          for (int nb = 0; nb < NB; nb++) {
+            const u32x4 xv = *reinterpret_cast<const u32x4*>(xb + nb * 16 * kXStride + j * 128 + h * 16);
+            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, xv), acc[nb], 0, 0, 0);
+          }
         }
       }
-    }
-    store_x((k + 1) & 1u);
-    __syncthreads();
-  };
+      store_x(x_out, (k + 1) & 1u);
+      __syncthreads();
+    };
 
-  for (uint32_t k = 0; k < n_steps; k += 3) {
-    step(s0, s2, k);
-    if (k + 1 < n_steps) step(s1, s0, k + 1);
-    if (k + 2 < n_steps) step(s2, s1, k + 2);
-  }
+    // n_steps is a multiple of 4: one iteration is one tile
+    for (uint32_t k = 0; k < n_steps; k += 4) {
+      step(s0, s3, xa, xb, k, std::true_type{});
+      step(s1, s0, xb, xa, k + 1, std::false_type{});
+      step(s2, s1, xa, xb, k + 2, std::false_type{});
+      step(s3, s2, xb, xa, k + 3, std::false_type{});
+    }
+  };
+  if (dense)
+    main_loop(std::true_type{});
+  else
+    main_loop(std::false_type{});
 
   // lane (li, lq) of block nb holds Y[nb*16 + li][r0 + 4 lq + s], s = 0..3;
   // values and offsets are formed first, the stores follow in straight-line
