@@ -68,10 +68,12 @@ struct GSlot {
   u32x2 nib[4];
 };
 
-template <int NB>
-__global__ __launch_bounds__(kGemmWaves * kWave) void k_gemm(GemmLaunch L) {
+template <int NB, int S>
+__global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const uint32_t wave = uniform(threadIdx.x >> 6);
+  const uint32_t rb = wave & 3u;  // row block of this wave
+  const uint32_t kh = wave >> 2;  // its share of K: tiles kh, kh + S, kh + 2 S, ...
   const int lane = lane_id();
   const uint32_t li = (uint32_t)lane & 15u, lq = (uint32_t)lane >> 4;
 
@@ -81,58 +83,71 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void k_gemm(GemmLaunch L) {
   const uint32_t T = G.cols >> 10;
   const uint64_t n_tiles = (uint64_t)G.rows * T;
   const Planes P = planes_of(G.blob, n_tiles);
-  const uint32_t r0 = (blockIdx.x - L.wg_begin[g]) * kGemmRows + wave * 16u;
+  const uint32_t r0 = (blockIdx.x - L.wg_begin[g]) * kGemmRows + rb * 16u;
   const uint32_t rows_here = r0 < G.rows ? min(16u, G.rows - r0) : 0u;
   const uint32_t tiles_here = rows_here * T;
   const uint64_t t_first = (uint64_t)r0 * T;
 
-  uint8_t* xs = smem;  // [2][NB * 16][kXStride]
-  uint8_t* wl = smem + 2 * NB * 16 * kXStride + wave * (L.idx_bytes + kEscCap);
+  constexpr uint32_t kXBuf = NB * 16 * kXStride;  // one K part's x of one step
+  uint8_t* xs = smem;                             // [2 buffers][S parts][NB * 16 rows][kXStride]
+  uint8_t* wl = smem + 2 * S * kXBuf + rb * (L.idx_bytes + kEscCap);  // shared by the row block's waves
   uint32_t* idx_l = reinterpret_cast<uint32_t*>(wl);
   uint8_t* esc_l = wl + L.idx_bytes;
 
-  const uint32_t n_steps = 4 * T;
+  // step k: round k / 4 (tiles (k / 4) S .. (k / 4) S + S - 1, one per K
+  // part), columns 256 (k % 4) .. + 256 of each of them
+  const uint32_t n_steps = 4 * ((T + S - 1) / S);
   const __amdgpu_buffer_rsrc_t rr = make_rsrc(P.raw + t_first * kTile, tiles_here * kTile);
   const __amdgpu_buffer_rsrc_t rn = make_rsrc(P.nib + t_first * (kTile / 2), tiles_here * (kTile / 2));
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(G.x, (uint32_t)L.batch * G.cols * 2);
 
-  // coded chunks of step k: lane (li, lq), chunk j -> tile k / 4 of row li,
-  // 16-weight chunk 16 (k % 4) + 4 j + lq
-  auto load_step = [&](GSlot& S, uint32_t k) {
-    const bool ok = k < n_steps;
-    const uint32_t tile = li * T + (k >> 2);
-    const uint32_t ch0 = 16u * (k & 3u) + lq;
+  // coded chunks of step k: lane (li, lq), chunk j -> tile c = (k / 4) S + kh
+  // of row li, 16-weight chunk 16 (k % 4) + 4 j + lq.  The lane part of the
+  // offset is fixed, the step part is uniform (scalar offset) and j goes in
+  // the instruction's immediate; a step past the end gets a lane offset past
+  // the range, and so do rows past the tensor, so every such load returns 0
+  // whether or not the range check counts the scalar offset.
+  const uint32_t vo_raw = li * T * kTile + lq * 16u;
+  const uint32_t vo_nib = li * T * (kTile / 2) + lq * 8u;
+  auto load_step = [&](GSlot& Sl, uint32_t k) {
+    const uint32_t c = (k >> 2) * S + kh;
+    const bool ok = k < n_steps && c < T;  // uniform
+    const uint32_t vr = ok ? vo_raw : kOOB, vn = ok ? vo_nib : kOOB;
+    const uint32_t sr = ok ? c * kTile + (k & 3u) * 256u : 0u;
+    const uint32_t sn = ok ? c * (kTile / 2) + (k & 3u) * 128u : 0u;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      const uint32_t ch = ch0 + 4u * j;
-      const uint32_t orw = ok ? tile * kTile + ch * 16u : kOOB;
-      const uint32_t onb = ok ? tile * (kTile / 2) + ch * 8u : kOOB;
       // default cache policy: a row's 128-byte lines are read by two or four
       // consecutive load instructions
-      S.raw[j] = __builtin_amdgcn_raw_buffer_load_b128(rr, orw, 0, 0);
-      S.nib[j] = __builtin_amdgcn_raw_buffer_load_b64(rn, onb, 0, 0);
+      Sl.raw[j] = __builtin_amdgcn_raw_buffer_load_b128(rr, vr + 64u * j, sr, 0);
+      Sl.nib[j] = __builtin_amdgcn_raw_buffer_load_b64(rn, vn + 32u * j, sn, 0);
     }
   };
-  // x columns [256 k, 256 k + 256) of batch rows 0 .. 16 NB - 1: piece
-  // p = 256 m + threadIdx.x is row p / 32, bytes 16 (p % 32) of the step
+  // x of step k for every K part: piece p = 256 S m + threadIdx.x is part
+  // h = p / (512 NB) (the same for a whole wave), batch row (p / 32) % (16 NB),
+  // bytes 16 (p % 32) of the part's 256 columns; rows past the batch are past
+  // the range
   struct XRegs {
     u32x4 v[NB * 2];
   };
   auto load_x = [&](XRegs& xr, uint32_t k) {
-    const bool ok = k < n_steps;
 #pragma unroll
     for (int m = 0; m < NB * 2; m++) {
-      const uint32_t p = 256u * m + threadIdx.x;
-      const uint32_t o = ok ? (p >> 5) * G.cols * 2 + k * (kStepK * 2) + (p & 31u) * 16u : kOOB;
-      xr.v[m] = __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, kNonTemporal);
+      const uint32_t p = 256u * S * m + threadIdx.x;
+      const uint32_t h = uniform(p / (512u * NB)), row = (p >> 5) % (16u * NB);
+      const uint32_t c = (k >> 2) * S + h;
+      const bool ok = k < n_steps && c < T;
+      const uint32_t vo = ok ? row * G.cols * 2 + (p & 31u) * 16u : kOOB;
+      const uint32_t so = ok ? (c * kTile + (k & 3u) * kStepK) * 2 : 0u;
+      xr.v[m] = __builtin_amdgcn_raw_buffer_load_b128(rx, vo, so, kNonTemporal);
     }
   };
   auto store_x = [&](const XRegs& xr, uint32_t buf) {
-    uint8_t* d = xs + buf * (NB * 16 * kXStride);
 #pragma unroll
     for (int m = 0; m < NB * 2; m++) {
-      const uint32_t p = 256u * m + threadIdx.x;
-      *reinterpret_cast<u32x4*>(d + (p >> 5) * kXStride + (p & 31u) * 16u) = xr.v[m];
+      const uint32_t p = 256u * S * m + threadIdx.x;
+      const uint32_t h = p / (512u * NB), row = (p >> 5) % (16u * NB);
+      *reinterpret_cast<u32x4*>(xs + (buf * S + h) * kXBuf + row * kXStride + (p & 31u) * 16u) = xr.v[m];
     }
   };
 
@@ -145,18 +160,18 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void k_gemm(GemmLaunch L) {
   load_step(s1, 1);
   load_step(s2, 2);
 
-  // this wave's index words idx[t_first .. t_first + tiles_here] and escape
-  // bytes, clamped to the stream so a corrupt index stays in bounds
+  // the row block's index words idx[t_first .. t_first + tiles_here] and
+  // escape bytes (staged by its first wave), clamped to the stream so a
+  // corrupt index stays in bounds
   uint32_t e_lo = 0, e_hi = 0, a0 = 0;
   bool dense = false;
-  if (rows_here) {
+  if (rows_here && kh == 0) {
     for (uint32_t w = (uint32_t)lane; w <= tiles_here; w += kWave) idx_l[w] = min(P.idx[t_first + w], G.n_esc);
     wave_lds_sync();
     e_lo = idx_l[0];
     e_hi = max(idx_l[tiles_here], e_lo);
     a0 = e_lo & ~3u;
-    dense = e_hi - a0 > kEscCap;
-    if (!dense) {
+    if (e_hi - a0 <= kEscCap) {
       const uint32_t* src = reinterpret_cast<const uint32_t*>(P.esc + a0);
       const uint32_t nw = (e_hi - a0 + 3) >> 2;
       for (uint32_t w = (uint32_t)lane; w < nw; w += kWave) reinterpret_cast<uint32_t*>(esc_l)[w] = src[w];
@@ -164,6 +179,12 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void k_gemm(GemmLaunch L) {
   }
   store_x(xa, 0);
   __syncthreads();
+  if (rows_here) {
+    e_lo = idx_l[0];
+    e_hi = max(idx_l[tiles_here], e_lo);
+    a0 = e_lo & ~3u;
+    dense = e_hi - a0 > kEscCap;
+  }
 
   f32x4 acc[NB];
 #pragma unroll
@@ -194,9 +215,9 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void k_gemm(GemmLaunch L) {
       load_x(x_in, k + 2);
       load_step(nx3, k + 3);
       if constexpr (decltype(tile_start)::value) {
-        const uint32_t c = k >> 2;
+        const uint32_t c = (k >> 2) * S + kh;
         uint32_t ia = e_lo, ib = e_lo;
-        if (li < rows_here) {
+        if (li < rows_here && c < T) {
           ia = min(max(idx_l[li * T + c], e_lo), e_hi);
           ib = min(max(idx_l[li * T + c + 1], ia), e_hi);
         }
@@ -210,7 +231,7 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void k_gemm(GemmLaunch L) {
         run = 0;
       }
       const Lut lut{G.lut[0], G.lut[1], G.lut[2], t3};
-      const uint8_t* xb = xs + (k & 1u) * (NB * 16 * kXStride) + li * kXStride + lq * 32u;
+      const uint8_t* xb = xs + ((k & 1u) * S + kh) * kXBuf + li * kXStride + lq * 32u;
 #pragma unroll
       for (int j = 0; j < 4; j++) {
         uint32_t E[4];
@@ -273,6 +294,23 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void k_gemm(GemmLaunch L) {
   else
     main_loop(std::false_type{});
 
+  // K parts: the row block's later waves hand their sums to its first wave
+  // through LDS (the x buffers are free after the last barrier), which adds
+  // them in part order
+  if constexpr (S > 1) {
+    f32x4* red = reinterpret_cast<f32x4*>(smem);
+    if (kh > 0) {
+#pragma unroll
+      for (int nb = 0; nb < NB; nb++) red[(((kh - 1) * 4 + rb) * NB + nb) * kWave + lane] = acc[nb];
+    }
+    __syncthreads();
+    if (kh > 0) return;
+#pragma unroll
+    for (uint32_t h = 1; h < (uint32_t)S; h++)
+#pragma unroll
+      for (int nb = 0; nb < NB; nb++) acc[nb] += red[(((h - 1) * 4 + rb) * NB + nb) * kWave + lane];
+  }
+
   // lane (li, lq) of block nb holds Y[nb*16 + li][r0 + 4 lq + s], s = 0..3;
   // values and offsets are formed first, the stores follow in straight-line
   // code (one branch on the output type, outside the loops)
@@ -305,18 +343,19 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void k_gemm(GemmLaunch L) {
 }
 
 // Largest dynamic LDS size each kernel instance was opened up to.
-static std::atomic<int> g_lds_set[4];
+static std::atomic<int> g_lds_set[4][2];
 
-template <int NB>
+template <int NB, int S>
 static hipError_t run_gemm(const GemmLaunch& L, uint32_t grid, hipStream_t s) {
-  const int lds = 2 * NB * 16 * kXStride + kGemmWaves * (int)(L.idx_bytes + kEscCap);
-  if (g_lds_set[NB - 1].load(std::memory_order_relaxed) < lds) {
-    const hipError_t e =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<NB>), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  const int lds = 2 * S * NB * 16 * kXStride + kGemmWaves * (int)(L.idx_bytes + kEscCap);
+  std::atomic<int>& set = g_lds_set[NB - 1][S - 1];
+  if (set.load(std::memory_order_relaxed) < lds) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<NB, S>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
-    g_lds_set[NB - 1].store(lds, std::memory_order_relaxed);
+    set.store(lds, std::memory_order_relaxed);
   }
-  hipLaunchKernelGGL((k_gemm<NB>), dim3(grid), dim3(kGemmWaves * kWave), lds, s, L);
+  hipLaunchKernelGGL((k_gemm<NB, S>), dim3(grid), dim3(kGemmWaves * S * kWave), lds, s, L);
   return hipGetLastError();
 }
 
@@ -330,7 +369,7 @@ hipError_t launch_gemm(const GemvGroup* groups, int n_groups, int batch, int y_d
     L.n_groups = n_groups;
     L.batch = nb;
     L.y_bf16 = y_dtype == LBF_BF16;
-    uint32_t wg = 0, t_max = 1;
+    uint32_t wg = 0, t_max = 1, t_min = kGemmMaxTiles;
     for (int g = 0; g < n_groups; g++) {
       GemvGroup G = groups[g];
       if ((G.cols >> 10) > kGemmMaxTiles) return hipErrorNotSupported;
@@ -340,15 +379,19 @@ hipError_t launch_gemm(const GemvGroup* groups, int n_groups, int batch, int y_d
       L.wg_begin[g] = wg;
       wg += (G.rows + kGemmRows - 1) / kGemmRows;
       t_max = std::max(t_max, G.cols >> 10);
+      t_min = std::min(t_min, G.cols >> 10);
     }
     L.wg_begin[n_groups] = wg;
     L.idx_bytes = (4 * (16 * t_max + 1) + 15) & ~15u;
+    // up to 16 columns, rows of two or more tiles split K over two waves per
+    // row block (8 waves a workgroup, two per SIMD, no register spills)
+    const bool split = t_min >= 2;
     hipError_t e;
     switch ((nb + 15) / 16) {
-      case 1: e = run_gemm<1>(L, wg, s); break;
-      case 2: e = run_gemm<2>(L, wg, s); break;
-      case 3: e = run_gemm<3>(L, wg, s); break;
-      default: e = run_gemm<4>(L, wg, s); break;
+      case 1: e = split ? run_gemm<1, 2>(L, wg, s) : run_gemm<1, 1>(L, wg, s); break;
+      case 2: e = run_gemm<2, 1>(L, wg, s); break;
+      case 3: e = run_gemm<3, 1>(L, wg, s); break;
+      default: e = run_gemm<4, 1>(L, wg, s); break;
     }
     if (e != hipSuccess) return e;
   }
