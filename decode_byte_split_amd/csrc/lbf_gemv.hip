@@ -7,25 +7,24 @@
 // Compression vs 8-bit GGUF", section "What does 'lossless' mean for LLM
 // weights?".  Weight bandwidth is the bound (same page, section "Lossless
 // compression or Q8 GGUF: which should you deploy?", on fleets whose
-// bottleneck is weight bandwidth), so the kernel is built for HBM streaming:
+// bottleneck is weight bandwidth), so both kernels here are HBM streams:
 //
-//  * persistent workgroups (as many as fit on the chip), each taking one
+//  * k_gemv_ring (batch 1..4, x of every tensor of the call fits in 96 KiB of
+//    LDS): one 1024-thread workgroup per CU, rows dealt to CUs, waves take
+//    rows from an LDS counter and stream them through a three-slot register
+//    ring (details at the kernel);
+//  * k_gemv (everything else): persistent workgroups, each taking one
 //    contiguous, cost-balanced range of work units across the launch's
-//    weight tensors ("groups"); a unit is `phases` consecutive rows of one
-//    tensor, all K;
-//  * K-stationary waves: each of the 4 waves owns a fixed slice of whole
-//    1024-weight tiles (1, 2 or 4 slices per row) and one row of every unit
-//    (the row phase), keeps the matching x values in VGPRs and walks rows;
-//  * per tile and lane one 16-byte raw load and one 8-byte nibble load, both
-//    non-temporal and coalesced; the loads for the next row are issued before
-//    the current row is decoded (two row buffers, ping-pong);
-//  * the escape bytes of a workgroup's whole range of one tensor are one
-//    contiguous slice of the escape stream: they are preloaded into LDS once,
-//    so a tile with escapes costs no extra memory round trip; the tile index
-//    is read with scalar loads;
-//  * each row's lane partials are summed across the wave with DPP and lane
-//    reads in a fixed order, K slices are combined in LDS in slice order: no
-//    floating-point atomics, bitwise-reproducible output.
+//    tensors; a unit is `phases` consecutive rows of one tensor, all K; each
+//    of the 4 waves owns a fixed slice of whole tiles (1, 2 or 4 slices per
+//    row), keeps the matching x in VGPRs and walks rows, loads for the next
+//    row in flight (two row buffers); the escape bytes of a workgroup's range
+//    of one tensor are one contiguous slice, preloaded into LDS once.
+//
+// Both read every tile with one 16-byte raw load and one 8-byte nibble load
+// per lane (non-temporal, coalesced), sum each row's lane partials across the
+// wave with DPP and lane reads in a fixed order and combine K slices in LDS in
+// slice order: no floating-point atomics, bitwise-reproducible output.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -358,229 +357,6 @@ static hipError_t run(GemvLaunch& L, hipStream_t s) {
   return hipGetLastError();
 }
 
-// ---- Row-streaming variant (batch 1..4, x staged in LDS) -------------------
-//
-// One 1024-thread workgroup per CU.  Every wave decodes whole rows (in
-// chunks of up to 4 tiles, the next chunk in flight while one is decoded)
-// and takes its next row from a counter in LDS, so the 16 waves of a CU
-// balance among themselves whatever their scheduling priority; workgroups
-// get equal-cost contiguous row ranges.  x for the current tensor is staged
-// in LDS (each lane's 16 values split in two 16-byte halves stored in
-// separate 1 KiB arrays, so the reads are conflict-free).
-constexpr int kRowWaves = 16;
-constexpr int kRowChunk = 4;
-constexpr uint32_t kRowEscShared = 16384;
-constexpr uint32_t kRowXMax = 98304;  // LDS bytes for x: B * K * 2
-
-struct RowLaunch {
-  GemvGroup g[LBF_MAX_GROUPS];
-  uint64_t total_cost;
-  int n_groups;
-  int y_bf16;
-  uint32_t x_bytes;
-};
-
-template <int B, bool CONTIG, bool PRELOAD>
-__device__ __forceinline__ void chunk_dot(const RowBuf<kRowChunk>& R, uint32_t S, uint32_t c, uint32_t T,
-                                          const uint8_t* x_sh, const SegCtx& C, float acc[B][2], int lane) {
-  uint32_t first[kRowChunk], cnt[kRowChunk], e1[kRowChunk], e2[kRowChunk];
-  chunk_escapes<kRowChunk, PRELOAD>(R.ixv, S, C, first, cnt, e1, e2);
-#pragma unroll
-  for (int j = 0; j < kRowChunk; j++) {
-    if ((uint32_t)j < S) {
-      uint32_t xr[B][8];
-#pragma unroll
-      for (int b = 0; b < B; b++) {
-        const uint8_t* xs = x_sh + (size_t)((b * T + c + j) * 2) * kTile + lane * 16;
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(xs);
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(xs + kTile);
-        xr[b][0] = a0.x; xr[b][1] = a0.y; xr[b][2] = a0.z; xr[b][3] = a0.w;
-        xr[b][4] = a1.x; xr[b][5] = a1.y; xr[b][6] = a1.z; xr[b][7] = a1.w;
-      }
-      uint32_t E[4];
-      tile_exponents<CONTIG, PRELOAD>(R.nib[j], first[j], cnt[j], e1[j], e2[j], C, E);
-      uint32_t w[8];
-      assemble16(R.raw[j], E, w);
-      dot16<B>(w, xr, acc);
-    }
-  }
-}
-
-template <int B, bool CONTIG, bool PRELOAD>
-__device__ __forceinline__ void stream_rows(const GemvGroup& G, uint32_t u_lo, uint32_t u_hi, bool y_bf16,
-                                            const uint8_t* raw_p, const uint8_t* nib_p, const uint32_t* idx_p,
-                                            const uint8_t* x_sh, const SegCtx& C, uint32_t* ctr, int lane) {
-  const uint32_t T = G.cols >> 10;
-  auto pull = [&]() -> uint32_t {
-    uint32_t v = 0;
-    if (lane == 0) v = atomicAdd(ctr, 1u);
-    return u_lo + uniform(v);
-  };
-  uint32_t r = pull();
-  if (r >= u_hi) return;
-  uint32_t rn = pull();
-  uint32_t c = 0;
-  RowBuf<kRowChunk> A, Bf;
-  load_row<kRowChunk>(A, raw_p, nib_p, idx_p, (uint64_t)r * T, min((uint32_t)kRowChunk, T), lane);
-  float acc[B][2];
-#pragma unroll
-  for (int b = 0; b < B; b++) acc[b][0] = acc[b][1] = 0.f;
-  // one step: prefetch the chunk after (r, c) into `nxt`, decode `cur`;
-  // returns false when the wave's stream has ended
-  auto step = [&](RowBuf<kRowChunk>& cur, RowBuf<kRowChunk>& nxt) -> bool {
-    const bool row_end = c + kRowChunk >= T;
-    const uint32_t r2 = row_end ? rn : r, c2 = row_end ? 0u : c + kRowChunk;
-    const bool more = r2 < u_hi;
-    const uint32_t lr = more ? r2 : r, lc = more ? c2 : c;
-    load_row<kRowChunk>(nxt, raw_p, nib_p, idx_p, (uint64_t)lr * T + lc, min((uint32_t)kRowChunk, T - lc), lane);
-    chunk_dot<B, CONTIG, PRELOAD>(cur, min((uint32_t)kRowChunk, T - c), c, T, x_sh, C, acc, lane);
-    if (row_end) {
-#pragma unroll
-      for (int b = 0; b < B; b++) {
-        const float v = wave_sum(acc[b][0] + acc[b][1]);
-        acc[b][0] = acc[b][1] = 0.f;
-        if (lane == 0) {
-          const size_t o = (size_t)b * G.rows + r;
-          if (y_bf16)
-            static_cast<uint16_t*>(G.y)[o] = f32_to_bf16_rne(v);
-          else
-            static_cast<float*>(G.y)[o] = v;
-        }
-      }
-      if (more) rn = pull();
-    }
-    r = r2;
-    c = c2;
-    return more;
-  };
-  while (step(A, Bf) && step(Bf, A)) {
-  }
-}
-
-template <int B>
-__global__ __launch_bounds__(kRowWaves * kWave) void k_gemv_rows(RowLaunch L) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* x_sh = smem;
-  uint8_t* esc_sh = smem + L.x_bytes;
-  uint8_t* stage = esc_sh + kRowEscShared;
-  uint32_t* ctr = reinterpret_cast<uint32_t*>(stage + kRowWaves * kTile);
-  const uint32_t wave = uniform(threadIdx.x >> 6);
-  const int lane = lane_id();
-  const uint64_t c_lo = L.total_cost * blockIdx.x / gridDim.x;
-  const uint64_t c_hi = L.total_cost * (blockIdx.x + 1) / gridDim.x;
-  for (int gi = 0; gi < L.n_groups; gi++) {
-    const GemvGroup& G = L.g[gi];
-    const uint64_t g_lo = G.cost_begin, g_hi = G.cost_begin + (uint64_t)G.n_units * G.unit_cost;
-    if (g_hi <= c_lo) continue;
-    if (g_lo >= c_hi) break;
-    const uint32_t u_lo = c_lo > g_lo ? (uint32_t)((c_lo - g_lo + G.unit_cost - 1) / G.unit_cost) : 0u;
-    const uint32_t u_hi = (uint32_t)min((uint64_t)G.n_units, (c_hi - g_lo + G.unit_cost - 1) / G.unit_cost);
-    if (u_lo >= u_hi) continue;
-    // segment: rows [u_lo, u_hi) of tensor gi
-    const uint32_t T = G.cols >> 10;
-    const uint64_t n_tiles = (uint64_t)G.rows * T;
-    const uint8_t* raw_p = G.blob + LBF_HEADER_BYTES;
-    const uint8_t* nib_p = raw_p + n_tiles * kTile;
-    const uint32_t* idx_p = reinterpret_cast<const uint32_t*>(nib_p + n_tiles * (kTile / 2));
-    const uint8_t* esc_p =
-        G.blob + ((LBF_HEADER_BYTES + n_tiles * (kTile + kTile / 2) + 4 * (n_tiles + 1) + 255) & ~uint64_t(255));
-    const uint32_t seg_hi = idx_p[(uint64_t)u_hi * T];
-    const uint32_t seg_lo = idx_p[(uint64_t)u_lo * T];
-    __syncthreads();  // the previous segment is done with x_sh, esc_sh and the counter
-    // x -> LDS: element (b, t, lane, half) = 16 bytes at ((b*T + t)*2 + half)*1024 + lane*16
-    const uint32_t nx = (uint32_t)B * T * kWave * 2;
-    for (uint32_t i = threadIdx.x; i < nx; i += kRowWaves * kWave) {
-      const uint32_t half = i & 1u, ln = (i >> 1) & 63u, bt = i >> 7;
-      const u32x4 v = reinterpret_cast<const u32x4*>(G.x)[(size_t)bt * 128 + ln * 2 + half];
-      *reinterpret_cast<u32x4*>(x_sh + (size_t)(bt * 2 + half) * kTile + ln * 16) = v;
-    }
-    SegCtx C;
-    C.esc_p = esc_p;
-    C.esc_sh = esc_sh;
-    C.esc_wave = stage + wave * kTile;
-    C.lut = Lut{G.lut[0], G.lut[1], G.lut[2], G.lut[3]};
-    C.base4 = G.base4;
-    C.e_hi = min(seg_hi, G.n_esc);
-    C.e_lo = min(seg_lo, C.e_hi);
-    const bool preload = C.e_hi - C.e_lo <= kRowEscShared;
-    if (preload) {
-      for (uint32_t p = threadIdx.x; p < C.e_hi - C.e_lo; p += kRowWaves * kWave) esc_sh[p] = esc_p[C.e_lo + p];
-    } else {  // dense escapes: per-tile staging, bounded by the stream itself
-      C.e_lo = 0;
-      C.e_hi = G.n_esc;
-    }
-    if (threadIdx.x == 0) *ctr = 0u;
-    __syncthreads();
-    const bool contig = G.flags & 1u;
-    if (preload) {
-      if (contig)
-        stream_rows<B, true, true>(G, u_lo, u_hi, L.y_bf16, raw_p, nib_p, idx_p, x_sh, C, ctr, lane);
-      else
-        stream_rows<B, false, true>(G, u_lo, u_hi, L.y_bf16, raw_p, nib_p, idx_p, x_sh, C, ctr, lane);
-    } else {
-      if (contig)
-        stream_rows<B, true, false>(G, u_lo, u_hi, L.y_bf16, raw_p, nib_p, idx_p, x_sh, C, ctr, lane);
-      else
-        stream_rows<B, false, false>(G, u_lo, u_hi, L.y_bf16, raw_p, nib_p, idx_p, x_sh, C, ctr, lane);
-    }
-  }
-}
-
-template <int B>
-static hipError_t run_rows_kernel(RowLaunch& L, hipStream_t s) {
-  static int cus = 0;
-  const uint32_t lds = L.x_bytes + kRowEscShared + kRowWaves * kTile + 16;
-  if (!cus) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return hipErrorUnknown;
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_rows<B>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             (int)(kRowXMax + kRowEscShared + kRowWaves * kTile + 16));
-    if (e != hipSuccess) return e;
-  }
-  uint64_t units = 0;
-  for (int g = 0; g < L.n_groups; g++) units += L.g[g].n_units;
-  const uint64_t grid = std::min<uint64_t>((uint64_t)cus, units);
-  hipLaunchKernelGGL((k_gemv_rows<B>), dim3((unsigned)grid), dim3(kRowWaves * kWave), lds, s, L);
-  return hipGetLastError();
-}
-
-static bool rows_fit(const GemvGroup* groups, int n_groups, int batch) {
-  if (batch > 4) return false;
-  for (int g = 0; g < n_groups; g++)
-    if ((uint64_t)batch * groups[g].cols * 2 > kRowXMax) return false;
-  return true;
-}
-
-static hipError_t launch_rows(const GemvGroup* groups, int n_groups, int batch, int y_dtype, hipStream_t s) {
-  RowLaunch L;
-  L.n_groups = n_groups;
-  L.y_bf16 = y_dtype == LBF_BF16;
-  uint64_t cost = 0;
-  uint32_t x_bytes = 0;
-  for (int g = 0; g < n_groups; g++) {
-    GemvGroup G = groups[g];
-    const uint32_t T = G.cols >> 10;
-    G.n_units = G.rows;  // a unit is one row
-    const uint64_t n_tiles = (uint64_t)G.rows * T;
-    const uint32_t esc_per_tile = (uint32_t)std::min<uint64_t>(1024, (G.n_esc + n_tiles - 1) / n_tiles);
-    G.unit_cost = T * (16u + esc_per_tile / 8u);
-    G.cost_begin = cost;
-    cost += (uint64_t)G.n_units * G.unit_cost;
-    x_bytes = std::max<uint32_t>(x_bytes, (uint32_t)batch * G.cols * 2);
-    L.g[g] = G;
-  }
-  L.total_cost = cost;
-  L.x_bytes = x_bytes;
-  switch (batch) {
-    case 1: return run_rows_kernel<1>(L, s);
-    case 2: return run_rows_kernel<2>(L, s);
-    case 3: return run_rows_kernel<3>(L, s);
-    default: return run_rows_kernel<4>(L, s);
-  }
-}
-
 // ---- Ring GEMV (x of every tensor fits in LDS) ------------------------------
 //
 // The fastest form, used for batch 1..4 when x of every tensor of the call
@@ -597,6 +373,7 @@ static hipError_t launch_rows(const GemvGroup* groups, int n_groups, int batch, 
 // (a disabled one gets a zero-length buffer range) and the ring is unrolled
 // by three, so the compiler counts outstanding loads exactly.
 constexpr int kRingWaves = 16;
+constexpr int kRingChunk = 4;  // tiles per chunk (at most; the last of a row may be shorter)
 constexpr uint32_t kRingXMax = 98304;
 
 struct RingLaunch {
@@ -608,8 +385,8 @@ struct RingLaunch {
 };
 
 struct Slot {
-  u32x4 raw[kRowChunk];
-  u32x2 nib[kRowChunk];
+  u32x4 raw[kRingChunk];
+  u32x2 nib[kRingChunk];
   uint32_t idxv;  // lane j: idx[t0 + j], j <= S
   uint32_t escv;  // lane p: escape p of the chunk's slice, p < 64
 };
@@ -634,7 +411,7 @@ __device__ __forceinline__ Pos row_pos(const RingLaunch& L, uint32_t q) {
   p.r = qq - (uint32_t)L.g[g].cost_begin;
   p.T = L.g[g].cols >> 10;
   p.c = 0;
-  p.S = p.valid ? min((uint32_t)kRowChunk, p.T) : 0u;
+  p.S = p.valid ? min((uint32_t)kRingChunk, p.T) : 0u;
   return p;
 }
 
@@ -660,7 +437,7 @@ __device__ __forceinline__ void load_data(Slot& s, const RingLaunch& L, const Po
   const __amdgpu_buffer_rsrc_t rr = make_rsrc(P.raw + t0 * kTile, p.S * kTile);
   const __amdgpu_buffer_rsrc_t rn = make_rsrc(P.nib + t0 * (kTile / 2), p.S * (kTile / 2));
 #pragma unroll
-  for (int j = 0; j < kRowChunk; j++) {
+  for (int j = 0; j < kRingChunk; j++) {
     s.raw[j] = __builtin_amdgcn_raw_buffer_load_b128(rr, (uint32_t)lane * 16 + j * kTile, 0, kNonTemporal);
     s.nib[j] = __builtin_amdgcn_raw_buffer_load_b64(rn, (uint32_t)lane * 8 + j * (kTile / 2), 0, kNonTemporal);
   }
@@ -728,14 +505,18 @@ __global__ __launch_bounds__(kRingWaves * kWave) void k_gemv_ring(RingLaunch L) 
       if (lane == 0) v = atomicAdd(lctr, 1u);
       k = uniform(v);
     }
-    const uint64_t q = blockIdx.x + (uint64_t)k * gridDim.x;
+    // workgroups go round-robin over the 8 XCDs: give each XCD a contiguous
+    // block of gridDim.x / 8 consecutive rows per round
+    const uint32_t b = blockIdx.x, per = gridDim.x >> 3;
+    const uint32_t cu = (gridDim.x & 7u) ? b : (b & 7u) * per + (b >> 3);
+    const uint64_t q = cu + (uint64_t)k * gridDim.x;
     return row_pos(L, q < L.n_rows ? (uint32_t)q : L.n_rows);
   };
   auto advance = [&](const Pos& p) -> Pos {
-    if (p.valid && p.c + kRowChunk < p.T) {
+    if (p.valid && p.c + kRingChunk < p.T) {
       Pos n = p;
-      n.c = p.c + kRowChunk;
-      n.S = min((uint32_t)kRowChunk, p.T - n.c);
+      n.c = p.c + kRingChunk;
+      n.S = min((uint32_t)kRingChunk, p.T - n.c);
       return n;
     }
     if (!p.valid) return p;
@@ -781,7 +562,7 @@ __global__ __launch_bounds__(kRingWaves * kWave) void k_gemv_ring(RingLaunch L) 
     slot_lds[lane] = (uint8_t)cur.escv;  // the chunk's escapes, for the patch path
     wave_lds_sync();
 #pragma unroll
-    for (int j = 0; j < kRowChunk; j++) {
+    for (int j = 0; j < kRingChunk; j++) {
       if ((uint32_t)j < p0.S) {
         uint32_t xr[B][8];
 #pragma unroll
@@ -802,7 +583,7 @@ __global__ __launch_bounds__(kRingWaves * kWave) void k_gemv_ring(RingLaunch L) 
       }
     }
     // row end: the sums of row p0.r are stored by lane 0 (range 0 otherwise)
-    const bool row_end = p0.valid && p0.c + kRowChunk >= p0.T;
+    const bool row_end = p0.valid && p0.c + kRingChunk >= p0.T;
     float v[B];
 #pragma unroll
     for (int bb = 0; bb < B; bb++) v[bb] = 0.f;
@@ -902,7 +683,6 @@ hipError_t launch_gemv(const GemvGroup* groups, int n_groups, int batch, int y_d
   bool used = false;
   const hipError_t e = launch_ring(groups, n_groups, batch, y_dtype, used, s);
   if (used || e != hipSuccess) return e;
-  if (rows_fit(groups, n_groups, batch)) return launch_rows(groups, n_groups, batch, y_dtype, s);
   static const int smax_of[9] = {0, 4, 4, 2, 2, 1, 1, 1, 1};
   const uint32_t smax = (uint32_t)smax_of[batch];
   GemvLaunch L;
