@@ -5,7 +5,7 @@ tensors (q, k, v, o, gate, up, down; 218,103,808 BF16 weights), batch 1, fp32
 output.  Inputs are synthetic and seeded (decode_byte_split_amd.synth), coded
 on the GPU and resident in HBM before timing.  Steps rotate over several
 copies of the coded layer so the working set (> 1 GB) cannot sit in the
-256 MB Infinity Cache.
+256 MB Infinity Cache and the timing averages over many placements in memory.
 
 Printed: one JSON line with the metric (BF16-equivalent weight GB/s), the
 roofline of the GEMV kernel (algorithmic bytes per launch / mean launch time
@@ -148,12 +148,12 @@ def cpu_baseline(Ws, xs, min_seconds: float):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--extras", action="store_true", help="also time decode, the batch sweep and raw BF16")
-    ap.add_argument("--rotate-gb", type=float, default=1.1)
+    ap.add_argument("--rotate-gb", type=float, default=4.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB elementwise copy first (scale for FETCH_SIZE / WRITE_SIZE counter runs)")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "BENCH_JSON"),

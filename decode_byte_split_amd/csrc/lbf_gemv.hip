@@ -9,8 +9,9 @@
 // compression or Q8 GGUF: which should you deploy?", on fleets whose
 // bottleneck is weight bandwidth), so both kernels here are HBM streams:
 //
-//  * k_gemv_ring (batch 1..4, x of every tensor of the call fits in 96 KiB of
-//    LDS): one 1024-thread workgroup per CU, rows dealt to CUs, waves take
+//  * k_gemv_ring (x of every tensor of the call fits in 96 KiB of LDS): one
+//    workgroup per CU (16 waves for batch 1..4, 8 for 5..8), rows dealt to
+//    CUs, waves take
 //    rows from an LDS counter and stream them through a three-slot register
 //    ring (details at the kernel);
 //  * k_gemv (everything else): persistent workgroups, each taking one
@@ -28,6 +29,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "lbf_device.h"
 #include "lbf_internal.h"
@@ -372,7 +374,7 @@ static hipError_t run(GemvLaunch& L, hipStream_t s) {
 // index needs nothing).  Every memory operation is issued unconditionally
 // (a disabled one gets a zero-length buffer range) and the ring is unrolled
 // by three, so the compiler counts outstanding loads exactly.
-constexpr int kRingWaves = 16;
+constexpr int kRingWaves = 16;  // waves per workgroup for batch 1..4 (4 per SIMD); 8 for batch 5..8
 constexpr int kRingChunk = 4;  // tiles per chunk (at most; the last of a row may be shorter)
 constexpr uint32_t kRingXMax = 98304;
 
@@ -485,13 +487,13 @@ __device__ __forceinline__ void ring_exponents(u32x2 nib, const GemvGroup& G, ui
   }
 }
 
-template <int B>
-__global__ __launch_bounds__(kRingWaves * kWave) void k_gemv_ring(RingLaunch L) {
+template <int B, int W>
+__global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const uint32_t wave = uniform(threadIdx.x >> 6);
   const int lane = lane_id();
   uint8_t* slot_lds = smem + kRingXMax + wave * kTile;
-  uint32_t* lctr = reinterpret_cast<uint32_t*>(smem + kRingXMax + kRingWaves * kTile);
+  uint32_t* lctr = reinterpret_cast<uint32_t*>(smem + kRingXMax + W * kTile);
 
   // rows of this CU: blockIdx.x + k * gridDim.x; the wave's first two come
   // from k = wave, wave + 16, the rest from the LDS counter (starts at 32)
@@ -499,7 +501,7 @@ __global__ __launch_bounds__(kRingWaves * kWave) void k_gemv_ring(RingLaunch L) 
   auto next_row = [&]() -> Pos {
     uint32_t k;
     if (k_static < 2) {
-      k = wave + kRingWaves * k_static++;
+      k = wave + W * k_static++;
     } else {
       uint32_t v = 0;
       if (lane == 0) v = atomicAdd(lctr, 1u);
@@ -537,13 +539,13 @@ __global__ __launch_bounds__(kRingWaves * kWave) void k_gemv_ring(RingLaunch L) 
     const uint32_t T = G.cols >> 10;
     uint8_t* xd = smem + L.x_off[L.xsrc_group[k]];
     const uint32_t nx = (uint32_t)B * T * kWave * 2;
-    for (uint32_t i = threadIdx.x; i < nx; i += kRingWaves * kWave) {
+    for (uint32_t i = threadIdx.x; i < nx; i += W * kWave) {
       const uint32_t half = i & 1u, ln = (i >> 1) & 63u, bt = i >> 7;
       const u32x4 v = reinterpret_cast<const u32x4*>(G.x)[(size_t)bt * 128 + ln * 2 + half];
       *reinterpret_cast<u32x4*>(xd + (size_t)(bt * 2 + half) * kTile + ln * 16) = v;
     }
   }
-  if (threadIdx.x == 0) *lctr = 2u * kRingWaves;
+  if (threadIdx.x == 0) *lctr = 2u * W;
   __syncthreads();
 
   float acc[B][2];
@@ -616,20 +618,24 @@ __global__ __launch_bounds__(kRingWaves * kWave) void k_gemv_ring(RingLaunch L) 
     }
 }
 
+// Batch 1..4: 16 waves a workgroup (4 per SIMD, <= 128 VGPRs each); batch
+// 5..8 needs more registers for x and the sums: 8 waves (2 per SIMD).
 template <int B>
 static hipError_t run_ring_kernel(RingLaunch& L, hipStream_t s) {
-  static int cus = 0;
-  const uint32_t lds = kRingXMax + kRingWaves * kTile + 16;
-  if (!cus) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return hipErrorUnknown;
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_ring<B>),
+  constexpr int W = B <= 4 ? kRingWaves : kRingWaves / 2;
+  static std::atomic<int> ready{0};  // attribute set for this instance (per process)
+  const uint32_t lds = kRingXMax + W * kTile + 16;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return hipErrorUnknown;
+  if (!ready.load(std::memory_order_acquire)) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_ring<B, W>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
+    ready.store(1, std::memory_order_release);
   }
   const uint32_t grid = (uint32_t)std::min<uint64_t>((uint64_t)cus, L.n_rows);
-  hipLaunchKernelGGL((k_gemv_ring<B>), dim3(grid), dim3(kRingWaves * kWave), lds, s, L);
+  hipLaunchKernelGGL((k_gemv_ring<B, W>), dim3(grid), dim3(W * kWave), lds, s, L);
   return hipGetLastError();
 }
 
@@ -637,7 +643,6 @@ static hipError_t run_ring_kernel(RingLaunch& L, hipStream_t s) {
 static hipError_t launch_ring(const GemvGroup* groups, int n_groups, int batch, int y_dtype, bool& used,
                               hipStream_t s) {
   used = false;
-  if (batch > 4) return hipSuccess;
   RingLaunch L;
   uint32_t x_bytes = 0;
   L.n_xsrc = 0;
@@ -675,7 +680,11 @@ static hipError_t launch_ring(const GemvGroup* groups, int n_groups, int batch, 
     case 1: return run_ring_kernel<1>(L, s);
     case 2: return run_ring_kernel<2>(L, s);
     case 3: return run_ring_kernel<3>(L, s);
-    default: return run_ring_kernel<4>(L, s);
+    case 4: return run_ring_kernel<4>(L, s);
+    case 5: return run_ring_kernel<5>(L, s);
+    case 6: return run_ring_kernel<6>(L, s);
+    case 7: return run_ring_kernel<7>(L, s);
+    default: return run_ring_kernel<8>(L, s);
   }
 }
 
