@@ -4,7 +4,7 @@ One step = one grouped lbf_gemv launch over the layer's seven coded weight
 tensors (q, k, v, o, gate, up, down; 218,103,808 BF16 weights), batch 1, fp32
 output.  Inputs are synthetic and seeded (decode_byte_split_amd.synth), coded
 on the GPU and resident in HBM before timing.  Steps rotate over several
-copies of the coded layer so the working set (> 1 GB) cannot sit in the
+copies of the coded layer (4 GB) so the working set cannot sit in the
 256 MB Infinity Cache and the timing averages over many placements in memory.
 
 Printed: one JSON line with the metric (BF16-equivalent weight GB/s), the
@@ -152,7 +152,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--extras", action="store_true", help="also time decode, the batch sweep and raw BF16")
+    ap.add_argument("--extras", action="store_true", help="also time decode, the batch sweep, the experts, "
+                    "raw BF16 and a copy ceiling")
+    ap.add_argument("--model-sweep", action="store_true",
+                    help="also code the full 32-layer weight set and time GEMV and decode sweeps over it (minutes)")
     ap.add_argument("--rotate-gb", type=float, default=4.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB elementwise copy first (scale for FETCH_SIZE / WRITE_SIZE counter runs)")
@@ -238,6 +241,10 @@ def main():
 
     if args.extras:
         out["extra"] = extras(torch, lbf, synth, Ws, blobs, rot, copies, args)
+    if args.model_sweep:
+        del rot, calls
+        torch.cuda.empty_cache()
+        out.setdefault("extra", {})["model_sweep"] = model_sweep(torch, lbf, synth)
 
     if not args.no_cpu:
         log("timing the CPU oracle (~%.0f s)" % args.cpu_seconds)
@@ -293,7 +300,78 @@ def extras(torch, lbf, synth, Ws, blobs, rot, copies, args):
                              "raw_bf16_linear_us": round(ms_raw * 1e3, 2)}
     del wg
     res["gate_proj_sweep"] = sweep
+    # the 64-expert set (1536 x 4096 each, escape-rate stress) grouped at batch 4
+    Wx = [synth.expert_tensor(e) for e in range(64)]
+    ex = [lbf.encode(dev(torch, W)) for W in Wx]
+    exr = [ex] + [[lbf.Blob(b.desc, b.data.clone()) for b in ex] for _ in range(3)]
+    xe = [dev(torch, synth.expert_x(e)) for e in range(64)]
+    ye = [torch.empty((4, b.rows), dtype=torch.float32, device="cuda") for b in ex]
+    ecalls = [lbf.prepare(r, xe, lbf.LBF_F32, outs=ye) for r in exr]
+    ms = time_region(torch, lambda i: ecalls[i % 4](), 20, 3)
+    alg = sum(algorithmic_bytes(b, 4, 4) for b in ex)
+    n_e = sum(W.size for W in Wx)
+    res["experts64_b4"] = {"us": round(ms * 1e3, 2), "bf16_equiv_GBs": round(2 * n_e / (ms * 1e-3) / 1e9, 1),
+                           "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                           "coded_bytes": sum(b.nbytes for b in ex), "escapes": sum(b.n_esc for b in ex)}
+    del ex, exr, ecalls, Wx
+    torch.cuda.empty_cache()
+    # mixed read + write ceiling: an elementwise copy of 1 GiB (read and written)
+    src = torch.ones(COPY_ELEMS, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    ms = time_region(torch, lambda i: torch.neg(src, out=dst), 10, 2)
+    res["copy_1GiB_ceiling"] = {"us": round(ms * 1e3, 2), "GBs_read_plus_write": round(8 * COPY_ELEMS / (ms * 1e-3) / 1e9, 1)}
+    del src, dst
+    torch.cuda.empty_cache()
     return res
+
+
+def model_sweep(torch, lbf, synth):
+    """The full 32-layer 8B-shaped weight set (224 tensors, 6.98e9 weights):
+    coded tensor by tensor on the GPU, then a fused batch-1 GEMV sweep (one
+    grouped launch per layer, each tensor with its own x) and a standalone
+    decode sweep over every tensor."""
+    t0 = time.time()
+    layers, xs = [], []
+    for L in range(32):
+        blobs = []
+        for m in range(len(synth.LAYER)):
+            W = synth.model_tensor(L, m)
+            blobs.append(lbf.encode(dev(torch, W)))
+            del W
+        layers.append(blobs)
+        xs.append([dev(torch, synth.model_x(L, m)) for m in range(len(synth.LAYER))])
+        if L % 8 == 7:
+            torch.cuda.synchronize()
+            log("model sweep: %d layers coded (%.0f s)" % (L + 1, time.time() - t0))
+    n = sum(r * c for _, r, c in synth.LAYER) * 32
+    coded = sum(b.nbytes for bl in layers for b in bl)
+    ys = [[torch.empty((1, b.rows), dtype=torch.float32, device="cuda") for b in bl] for bl in layers]
+    calls = [lbf.prepare(bl, x, lbf.LBF_F32, outs=y) for bl, x, y in zip(layers, xs, ys)]
+
+    def sweep(i):
+        for c in calls:
+            c()
+
+    ms = time_region(torch, sweep, 5, 2)
+    alg = sum(algorithmic_bytes(b, 1, 4) for bl in layers for b in bl)
+    outs = {}
+    for bl in layers[:1]:
+        for b in bl:
+            outs[(b.rows, b.cols)] = torch.empty((b.rows, b.cols), dtype=torch.bfloat16, device="cuda")
+
+    def dec(i):
+        for bl in layers:
+            for b in bl:
+                lbf.decode(b, out=outs[(b.rows, b.cols)])
+
+    ms_d = time_region(torch, dec, 3, 1)
+    return {"workload": "llama8b_32_layers", "tensors": 32 * len(synth.LAYER), "weights": n, "coded_bytes": coded,
+            "bits_per_weight": round(8.0 * coded / n, 4), "reduction_vs_bf16": round(1 - coded / (2.0 * n), 5),
+            "gemv_sweep_us": round(ms * 1e3, 1), "gemv_bf16_equiv_GBs": round(2 * n / (ms * 1e-3) / 1e9, 1),
+            "gemv_hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "decode_sweep_us": round(ms_d * 1e3, 1),
+            "decode_hbm_GBs": round((sum(algorithmic_bytes(b, 0, 0) for bl in layers for b in bl) + 2 * n)
+                                    / (ms_d * 1e-3) / 1e9, 1)}
 
 
 if __name__ == "__main__":

@@ -173,6 +173,28 @@ def test_gemv_layer_grouped_full(env):
         assert np.array_equal(host(lbf.decode(b)), W)
 
 
+@pytest.mark.parametrize("layer", [0, 31])
+def test_gemv_model_layer_sampled(env, layer):
+    """A layer of the full 32-layer weight set (per-tensor sigma ~ U(0.01, 0.05)):
+    GPU blobs equal the oracle's for k and v, the grouped batch-1 GEMV matches
+    the oracle on row ranges at the start, middle and end of every tensor."""
+    torch, lbf = env
+    t0 = time.time()
+    Ws = [synth.model_tensor(layer, m) for m in range(len(synth.LAYER))]
+    xs = [synth.model_x(layer, m) for m in range(len(synth.LAYER))]
+    say("model layer %d generated in %.1fs" % (layer, time.time() - t0))
+    blobs = [lbf.encode(dev(torch, W)) for W in Ws]
+    for m in (1, 2):
+        assert np.array_equal(blobs[m].data.cpu().numpy(), O.encode(Ws[m])), m
+    ys = lbf.gemv(blobs, [dev(torch, x) for x in xs], lbf.LBF_F32)
+    torch.cuda.synchronize()
+    for W, x, y in zip(Ws, xs, ys):
+        R = W.shape[0]
+        for r0 in (0, R // 2 - 64, R - 128):
+            y_ref, a_ref = O.matvec(W, x, rows=(r0, r0 + 128))
+            check_product(y[:, r0:r0 + 128], y_ref, a_ref, False)
+
+
 def test_gemv_gate_batch_sweep(env):
     torch, lbf = env
     W = synth.layer_tensor(synth.GATE)
