@@ -31,7 +31,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 METRIC = "fused decode-GEMV BF16-equiv weight GB/s + % HBM roofline, 8B-shaped layer"
 COUNTERS = os.path.join(ROOT, "profiles", "gemv_ring_layer_b1_counters.json")
-KERNEL = "lbf::k_gemv_ring<1>"
+KERNEL = "lbf::k_gemv_ring<1, 16>"
 KERNEL_SOURCES = ("decode_byte_split_amd/csrc/lbf_gemv.hip", "decode_byte_split_amd/csrc/lbf_device.h")
 
 
@@ -154,6 +154,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--extras", action="store_true", help="also time decode, the batch sweep, the experts, "
                     "raw BF16 and a copy ceiling")
+    ap.add_argument("--gate-batch", type=int, default=0, metavar="B",
+                    help="time only the gate_proj product (14336 x 4096) at batch B (GEMV for B <= 8, MFMA GEMM "
+                         "above) and print its own line; for profiling")
     ap.add_argument("--model-sweep", action="store_true",
                     help="also code the full 32-layer weight set and time GEMV and decode sweeps over it (minutes)")
     ap.add_argument("--rotate-gb", type=float, default=4.0)
@@ -171,6 +174,9 @@ def main():
         alg = json.loads(line)["roofline"]["algorithmic_bytes_per_launch"]
         print(json.dumps(summarize_counters(fetch_csv, write_csv, KERNEL.split("::")[1].split("<")[0], alg), indent=1))
         return
+
+    if args.gate_batch:
+        return gate_batch(args)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the fused decode-GEMV has no cross-GPU step in this build "
@@ -323,6 +329,38 @@ def extras(torch, lbf, synth, Ws, blobs, rot, copies, args):
     del src, dst
     torch.cuda.empty_cache()
     return res
+
+
+def gate_batch(args):
+    """gate_proj (14336 x 4096) at one batch size, bf16 output: the fused
+    product alone, rotated over 4 GB of coded copies, HIP-event timed."""
+    import torch
+
+    from decode_byte_split_amd import lbf, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    B = args.gate_batch
+    W = synth.layer_tensor(synth.GATE)
+    blob = lbf.encode(dev(torch, W))
+    copies = max(1, int(np.ceil(args.rotate_gb * 1e9 / blob.nbytes)))
+    rot = [blob] + [lbf.Blob(blob.desc, blob.data.clone()) for _ in range(copies - 1)]
+    x = dev(torch, synth.gate_batch_x(B))
+    y = torch.empty((B, blob.rows), dtype=torch.bfloat16, device="cuda")
+    calls = [lbf.prepare(r, x, lbf.LBF_BF16, outs=y) for r in rot]
+    ms = time_region(torch, lambda i: calls[i % copies](), args.steps, args.warmup)
+    alg = algorithmic_bytes(blob, B, 2)
+    flops = 2.0 * B * W.size
+    out = {"metric": "fused decode product BF16-equiv weight GB/s, gate_proj", "value": round(2 * W.size / (ms * 1e-3) / 1e9, 1),
+           "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "gate_proj_14336x4096", "batch": B, "y_dtype": "bf16",
+                      "path": "gemv" if B <= 8 else "gemm_mfma_16x16x32_bf16", "rotation_copies": copies},
+           "roofline": {"bound": "hbm", "achieved": round(alg / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "algorithmic_bytes_per_launch": alg},
+           "mfma": {"tflops": round(flops / (ms * 1e-3) / 1e12, 2), "frac_of_2.5PF_bf16": round(flops / (ms * 1e-3) / 2.5e15, 4)}
+           if B > 8 else None}
+    print(json.dumps(out))
 
 
 def model_sweep(torch, lbf, synth):
