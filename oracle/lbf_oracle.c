@@ -303,6 +303,76 @@ int lbfo_decode(const uint8_t* blob, uint64_t blob_len, uint16_t* out, uint64_t 
   return 0;
 }
 
+/* ---- verification without decoding -------------------------------------
+ * Checks a blob against the 96 descriptor bytes the caller trusts (corruption
+ * must be detected and refused: "Lossless LLM Weight Compression vs 8-bit
+ * GGUF", sections "Is the GLM-5.2 result production-ready?" and "Questions to
+ * ask a vendor or research team").  Each failed check sets one bit:
+ *    1  header: bytes [0,96) differ from desc96, or [96,256) are not zero
+ *    2  index: idx[0] != 0, idx decreases, or idx[n_t] != n_esc
+ *    4  count: a tile holds a number of code-15 nibbles other than
+ *       idx[t+1] - idx[t]
+ *    8  code: a nibble of a real weight holds an unused code (n_codes..14)
+ *   16  escape: an escape byte equals a coded exponent (escapes are, by
+ *       definition, the exponents outside the table)
+ *   32  padding: a byte the format defines as zero is not (raw and code bits of
+ *       padding weights past n; the gap after the index; bytes after the
+ *       escape stream up to blob_bytes)
+ * The raw sign/mantissa bytes of real weights carry no redundancy: only a
+ * hash of the blob (lbfo_crc32) catches changes there.
+ * desc96 must describe a layout that fits blob_len (else the result is 1).
+ */
+unsigned lbfo_verify(const uint8_t* blob, uint64_t blob_len, const uint8_t desc96[96]) {
+  unsigned bad = 0;
+  uint64_t rows = get_u64(desc96 + 8), cols = get_u64(desc96 + 16), n_esc = get_u64(desc96 + 24);
+  unsigned n_codes = desc96[88];
+  const uint8_t* lut = desc96 + 72;
+  if (n_codes > 15 || (cols != 0 && rows > UINT64_MAX / cols) || rows * cols >= (1ull << 32)) return 1;
+  layout_t L = layout_for(rows, cols, n_esc);
+  if (blob_len < L.blob_bytes) return 1;
+
+  if (memcmp(blob, desc96, 96) != 0) bad |= 1u;
+  for (uint64_t i = 96; i < HEADER; i++)
+    if (blob[i] != 0) bad |= 1u;
+
+  const uint8_t* raw = blob + L.off_raw;
+  const uint8_t* nib = blob + L.off_nib;
+  const uint8_t* idx = blob + L.off_idx;
+  const uint8_t* esc = blob + L.off_esc;
+  if (get_u32(idx) != 0 || get_u32(idx + 4u * L.n_tiles) != n_esc) bad |= 2u;
+  for (uint64_t t = 0; t < L.n_tiles; t++) {
+    uint32_t a = get_u32(idx + 4u * t), b = get_u32(idx + 4u * (t + 1));
+    if (b < a) bad |= 2u;
+    uint64_t fifteens = 0;
+    for (uint64_t i = t * TILE; i < (t + 1) * TILE; i++) {
+      unsigned code = (nib[code_byte(i)] >> code_shift(i)) & 15u;
+      if (i >= L.n) {
+        if (code != 0) bad |= 32u;
+        continue;
+      }
+      if (code == 15u)
+        fifteens++;
+      else if (code >= n_codes)
+        bad |= 8u;
+    }
+    if (b >= a && fifteens != (uint64_t)(b - a)) bad |= 4u;
+    if (b < a && fifteens != 0) bad |= 4u;
+  }
+  /* padding weights: mantissa bits 0; the sign bit of byte i is weight i^1's,
+     so byte n (n odd) may carry the sign of weight n - 1 */
+  for (uint64_t i = L.n; i < L.n_tiles * TILE; i++) {
+    uint8_t allowed = (i == L.n && (L.n & 1u)) ? 1u : 0u;
+    if (raw[i] & (uint8_t)~allowed) bad |= 32u;
+  }
+  for (uint64_t j = 0; j < n_esc; j++)
+    if (code_of(esc[j], lut, n_codes) != 15u) bad |= 16u;
+  for (uint64_t i = L.off_idx + 4u * (L.n_tiles + 1); i < L.off_esc; i++)
+    if (blob[i] != 0) bad |= 32u;
+  for (uint64_t i = L.off_esc + n_esc; i < L.blob_bytes; i++)
+    if (blob[i] != 0) bad |= 32u;
+  return bad;
+}
+
 /* ---- y = W x in float64 ------------------------------------------------
  * y[b*rows + r] = sum_k W[r,k] * x[b,k], summed in k order in double;
  * a[b*rows + r] = sum_k |W[r,k]| * |x[b,k]|, the scale the error bound uses.

@@ -64,6 +64,8 @@ def lib():
         L.lbfo_entropy16.argtypes = [_u16p, _u64]
         L.lbfo_entropy_exponent.restype = ctypes.c_double
         L.lbfo_entropy_exponent.argtypes = [_u16p, _u64]
+        L.lbfo_verify.restype = ctypes.c_uint
+        L.lbfo_verify.argtypes = [_u8p, _u64, _u8p]
         _lib = L
     return _lib
 
@@ -166,6 +168,17 @@ def decode(blob: np.ndarray) -> np.ndarray:
     if rc != 0:
         raise ValueError("oracle decode failed (%d)" % rc)
     return out
+
+
+VERIFY_HEADER, VERIFY_INDEX, VERIFY_COUNT, VERIFY_CODE, VERIFY_ESCAPE, VERIFY_PADDING = 1, 2, 4, 8, 16, 32
+
+
+def verify(blob: np.ndarray, desc96: np.ndarray | bytes | None = None) -> int:
+    """Bit mask of failed structural checks of ``blob`` against the 96
+    descriptor bytes ``desc96`` (default: the blob's own first 96 bytes)."""
+    blob = np.ascontiguousarray(blob, dtype=np.uint8)
+    d = blob[:96].copy() if desc96 is None else np.frombuffer(bytes(desc96), dtype=np.uint8).copy()
+    return int(lib().lbfo_verify(_p(blob, _u8p), blob.size, _p(d, _u8p)))
 
 
 def matvec(W: np.ndarray, x: np.ndarray, rows: tuple[int, int] | None = None):

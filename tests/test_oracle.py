@@ -101,6 +101,63 @@ def test_escape_ties_golden():
     assert np.array_equal(O.decode(blob), W)
 
 
+# ---- structural verification (corruption must be detected, fail closed) ----------
+# Expected flags are worked out from the goldens' hand-derived layouts:
+# 1 header, 2 index, 4 code-15 count, 8 unused code, 16 escape is a coded
+# exponent, 32 nonzero padding.
+
+def _corrupt(blob, pos, value=None, xor=None):
+    b = blob.copy()
+    if value is not None:
+        b[pos] = value
+    else:
+        b[pos] ^= xor
+    return b
+
+
+def test_verify_tiny_six_corruptions():
+    g = golden("tiny_six.json")
+    W = np.array(g["bits"], dtype=np.uint16).reshape(g["rows"], g["cols"])
+    blob = O.encode(W)
+    d = blob[:96].copy()
+    on, orw, oi = g["off_nib"], g["off_raw"], g["off_idx"]
+    assert O.verify(blob, d) == 0
+    assert O.verify(_corrupt(blob, on, 0x23), d) == O.VERIFY_CODE       # weight 0: code 3 >= n_codes
+    assert O.verify(_corrupt(blob, on, 0x2F), d) == O.VERIFY_COUNT      # weight 0: code 15, no escape indexed
+    assert O.verify(_corrupt(blob, on + 2, xor=0x10), d) == O.VERIFY_PADDING  # padding weight 6 gets code 1
+    assert O.verify(_corrupt(blob, orw + 6, 1), d) == O.VERIFY_PADDING  # n = 6 even: byte 6 must stay 0
+    assert O.verify(_corrupt(blob, orw + 7, 0x80), d) == O.VERIFY_PADDING
+    assert O.verify(_corrupt(blob, oi + 4, 1), d) == O.VERIFY_INDEX | O.VERIFY_COUNT  # idx[1] = 1 != n_esc
+    assert O.verify(_corrupt(blob, oi + 8, 7), d) == O.VERIFY_PADDING   # gap after the index
+    assert O.verify(_corrupt(blob, 100, 1), d) == O.VERIFY_HEADER
+    assert O.verify(_corrupt(blob, 8, xor=1), d) == O.VERIFY_HEADER     # rows differ from the trusted descriptor
+    flipped = _corrupt(blob, orw, xor=0x02)                             # a mantissa bit of a real weight:
+    assert O.verify(flipped, d) == 0                                    # no structural trace ...
+    assert O.crc32(flipped) != O.crc32(blob)                            # ... the blob hash catches it
+
+
+def test_verify_escape_ties_corruptions():
+    g = golden("escape_ties.json")
+    blob = O.encode(_escape_ties_tensor(g))
+    d = blob[:96].copy()
+    oe, oi, on = g["off_esc"], g["off_idx"], g["off_nib"]
+    assert O.verify(blob, d) == 0
+    assert O.verify(_corrupt(blob, oe, 101), d) == O.VERIFY_ESCAPE      # 101 has code 0
+    assert O.verify(_corrupt(blob, oe, 99), d) == 0                     # another uncoded exponent: hash only
+    assert O.verify(_corrupt(blob, oe + g["n_esc"], 5), d) == O.VERIFY_PADDING
+    assert O.verify(_corrupt(blob, oi + 4, 6), d) == O.VERIFY_COUNT     # idx = 0, 6, 12: tiles hold 5 and 7
+    assert O.verify(_corrupt(blob, oi + 4, 13), d) == O.VERIFY_INDEX | O.VERIFY_COUNT  # idx decreases
+    assert O.verify(_corrupt(blob, on, 0x9F), d) == O.VERIFY_COUNT      # weight 0 becomes a sixth escape in tile 0
+
+
+@pytest.mark.parametrize("shape", [(0, 7), (1, 1), (3, 5), (5, 4097), (256, 256)])
+def test_verify_accepts_encoder_output(shape):
+    rows, cols = shape
+    W = synth.all_patterns(rows, cols) if shape == (256, 256) else \
+        synth.gaussian(np.random.default_rng([9, rows, cols]), rows, cols, 0.02, 0.01, 100.0)
+    assert O.verify(O.encode(W)) == 0
+
+
 # ---- the round trip is the identity (lossless means bit-exact) -----------------
 
 def test_roundtrip_all_65536_patterns():
