@@ -231,6 +231,22 @@ int lbf_decode(const lbf_desc* desc, const void* d_blob, void* d_w_out, hipStrea
   return LBF_OK;
 }
 
+int lbf_verify(const lbf_desc* desc, const void* d_blob, uint32_t* d_flags, hipStream_t s) {
+  const int rc = check(desc);
+  if (rc) return rc;
+  if (!d_blob || !d_flags) return LBF_E_INVAL;
+  if (!aligned(d_blob, 256) || !aligned(d_flags, 4)) return LBF_E_ALIGN;
+  if (launch_verify(*desc, static_cast<const uint8_t*>(d_blob), d_flags, s) != hipSuccess) return LBF_E_HIP;
+  return LBF_OK;
+}
+
+int lbf_crc32(const void* d_data, uint64_t n, uint32_t* d_crc, hipStream_t s) {
+  if ((n && !d_data) || !d_crc) return LBF_E_INVAL;
+  if (!aligned(d_data, 16) || !aligned(d_crc, 4)) return LBF_E_ALIGN;
+  if (launch_crc32(static_cast<const uint8_t*>(d_data), n, d_crc, s) != hipSuccess) return LBF_E_HIP;
+  return LBF_OK;
+}
+
 static int product(bool mfma, const lbf_desc* descs, const void* const* d_blobs, int n_groups,
                    const void* const* d_x, int batch, void* const* d_y, int y_dtype, hipStream_t s) {
   if (y_dtype != LBF_F32 && y_dtype != LBF_BF16) return LBF_E_INVAL;

@@ -27,6 +27,8 @@ KLut klut_of(const lbf_desc& d);
 // Launchers (defined next to their kernels).  All enqueue on `s` and return
 // the launch status.
 hipError_t launch_decode(const lbf_desc& d, const uint8_t* blob, uint16_t* out, hipStream_t s);
+hipError_t launch_verify(const lbf_desc& d, const uint8_t* blob, uint32_t* flags, hipStream_t s);
+hipError_t launch_crc32(const uint8_t* data, uint64_t n, uint32_t* crc, hipStream_t s);
 
 hipError_t launch_hist(const uint16_t* w, uint64_t n, uint32_t* hist, hipStream_t s);
 hipError_t launch_pack(const uint16_t* w, const lbf_desc& d, uint8_t* blob, uint32_t* tile_cnt, hipStream_t s);

@@ -94,6 +94,10 @@ def lib():
         L.lbf_encode.argtypes = [vp, u64, u64, vp, u64, vp, u64, dp, vp]
         L.lbf_decode.restype = i32
         L.lbf_decode.argtypes = [dp, vp, vp, vp]
+        L.lbf_verify.restype = i32
+        L.lbf_verify.argtypes = [dp, vp, vp, vp]
+        L.lbf_crc32.restype = i32
+        L.lbf_crc32.argtypes = [vp, u64, vp, vp]
         for name in ("lbf_gemv", "lbf_gemm"):
             f = getattr(L, name)
             f.restype = i32
@@ -102,8 +106,8 @@ def lib():
     return _lib
 
 
-EXPORTS = ("lbf_strerror", "lbf_encode_work_bytes", "lbf_desc_check", "lbf_encode", "lbf_decode", "lbf_gemv",
-           "lbf_gemm")
+EXPORTS = ("lbf_strerror", "lbf_encode_work_bytes", "lbf_desc_check", "lbf_encode", "lbf_decode", "lbf_verify",
+           "lbf_crc32", "lbf_gemv", "lbf_gemm")
 
 
 def strerror(status: int) -> str:
@@ -198,6 +202,31 @@ def decode(blob: Blob, out=None, stream=None):
         out = torch.empty((blob.rows, blob.cols), dtype=torch.bfloat16, device=blob.data.device)
     _check(lib().lbf_decode(ctypes.byref(blob.desc), _ptr(blob.data), _ptr(out), _stream(stream)), "lbf_decode")
     return out
+
+
+VERIFY_HEADER, VERIFY_INDEX, VERIFY_COUNT, VERIFY_CODE, VERIFY_ESCAPE, VERIFY_PADDING = 1, 2, 4, 8, 16, 32
+
+
+def verify(blob: Blob, desc: Desc | None = None, stream=None) -> int:
+    """Structural check of a device blob against ``desc`` (default: its own
+    descriptor) on the GPU; returns the failed-check mask (0: all pass).
+    Waits for the stream."""
+    torch = _torch()
+    flags = torch.empty(1, dtype=torch.int32, device=blob.data.device)
+    d = blob.desc if desc is None else desc
+    _check(lib().lbf_verify(ctypes.byref(d), _ptr(blob.data), _ptr(flags), _stream(stream)), "lbf_verify")
+    return int(flags.item()) & 0xFFFFFFFF
+
+
+def crc32(t, stream=None) -> int:
+    """CRC-32 (zlib's) of a contiguous device tensor's bytes, on the GPU.
+    Waits for the stream."""
+    torch = _torch()
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("crc32 takes a contiguous tensor on the GPU")
+    out = torch.empty(1, dtype=torch.int32, device=t.device)
+    _check(lib().lbf_crc32(_ptr(t), t.numel() * t.element_size(), _ptr(out), _stream(stream)), "lbf_crc32")
+    return int(out.item()) & 0xFFFFFFFF
 
 
 class Prepared:

@@ -163,6 +163,41 @@ int lbf_gemv(const lbf_desc* descs, const void* const* d_blobs, int n_groups, co
 int lbf_gemm(const lbf_desc* descs, const void* const* d_blobs, int n_groups, const void* const* d_x,
              int batch, void* const* d_y, int y_dtype, hipStream_t s);
 
+/* Checks of lbf_verify; its result is the OR of the failed ones (0: all pass). */
+enum {
+  LBF_VERIFY_HEADER = 1,  /* device bytes [0,96) differ from *desc, or [96,256) are not zero */
+  LBF_VERIFY_INDEX = 2,   /* idx[0] != 0, idx decreases, or idx[n_tiles] != n_esc */
+  LBF_VERIFY_COUNT = 4,   /* a tile holds a number of code-15 nibbles other than idx[t+1] - idx[t] */
+  LBF_VERIFY_CODE = 8,    /* a real weight holds an unused code (n_codes .. 14) */
+  LBF_VERIFY_ESCAPE = 16, /* an escape byte is one of the coded exponents */
+  LBF_VERIFY_PADDING = 32 /* a byte the format pads with zero is not zero */
+};
+
+/*
+ * lbf_verify — structural check of a device blob against the host descriptor
+ * the caller trusts, on the GPU, without decoding.  Corrupt weights must be
+ * detected and refused (same page, sections "Is the GLM-5.2 result
+ * production-ready?" and "Questions to ask a vendor or research team").
+ *   desc      host descriptor (checked with lbf_desc_check: LBF_E_DESC)
+ *   d_blob    device, 256-byte aligned, desc->blob_bytes long
+ *   d_flags   device uint32, 4-byte aligned: overwritten with the OR of the
+ *             failed LBF_VERIFY_* checks once the stream reaches it
+ * Not covered: the sign and mantissa bits of real weights and escaped
+ * exponents changed into other uncoded ones carry no redundancy; compare
+ * lbf_crc32 of the blob with a stored hash to cover every byte.
+ */
+int lbf_verify(const lbf_desc* desc, const void* d_blob, uint32_t* d_flags, hipStream_t s);
+
+/*
+ * lbf_crc32 — CRC-32 of n bytes of device memory (IEEE 802.3 polynomial,
+ * reflected, initial value and final xor 0xFFFFFFFF: zlib's crc32), on the
+ * GPU.  Lets a stored hash of a blob be checked where the blob lives.
+ *   d_data    device, 16-byte aligned (any n, including 0)
+ *   d_crc     device uint32, 4-byte aligned: overwritten with the CRC once the
+ *             stream reaches it
+ */
+int lbf_crc32(const void* d_data, uint64_t n, uint32_t* d_crc, hipStream_t s);
+
 #ifdef __cplusplus
 }
 #endif

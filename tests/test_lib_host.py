@@ -125,3 +125,10 @@ def test_calls_validate_before_touching_the_gpu():
     small = _oracle_desc(np.zeros((3, 5), dtype=np.uint16))[0]
     assert L.lbf_gemv((lbf.Desc * 1)(small), p, 1, p, 1, p, 0, None) == lbf.LBF_E_SHAPE  # cols % 1024
     assert L.lbf_encode(256, 1 << 20, 1 << 20, 256, 1 << 30, None, 0, ctypes.byref(lbf.Desc()), None) == lbf.LBF_E_SHAPE
+    assert L.lbf_verify(ctypes.byref(bad), 256, 256, None) == lbf.LBF_E_DESC
+    assert L.lbf_verify(ctypes.byref(d), 256 + 16, 256, None) == lbf.LBF_E_ALIGN
+    assert L.lbf_verify(ctypes.byref(d), 256, 258, None) == lbf.LBF_E_ALIGN
+    assert L.lbf_verify(ctypes.byref(d), None, 256, None) == lbf.LBF_E_INVAL
+    assert L.lbf_crc32(256 + 4, 100, 256, None) == lbf.LBF_E_ALIGN
+    assert L.lbf_crc32(None, 100, 256, None) == lbf.LBF_E_INVAL
+    assert L.lbf_crc32(256, 100, None, None) == lbf.LBF_E_INVAL
