@@ -98,3 +98,29 @@ def test_crc32_of_blob_equals_oracle(env):
     for name, blob in BLOBS.items():
         t = torch.from_numpy(blob).cuda()
         assert lbf.crc32(t) == O.crc32(blob), name
+
+
+def test_artifact_layer_loads_verified_and_decodes_exactly(env, tmp_path):
+    """The 8B-shaped layer, coded on the GPU, through an artifact file: loaded
+    with host and GPU checks, every tensor decodes to its source bits; a
+    corrupted copy of the file is refused."""
+    torch, lbf = env
+    from decode_byte_split_amd import artifact as A
+
+    names = [m[0] for m in synth.LAYER]
+    blobs = {name: lbf.encode(dev(torch, synth.layer_tensor(m))) for m, name in enumerate(names)}
+    path = str(tmp_path / "layer.lbfa")
+    A.save(path, blobs)
+    rep = A.size_report(path)
+    say("layer artifact: %d bytes, %.4f bits/weight, %.3f %% smaller than BF16"
+        % (rep["file_bytes"], rep["bits_per_weight"], 100 * rep["reduction_vs_bf16"]))
+    assert rep["reduction_vs_bf16"] > 0.24
+    ok = A.check_against(path, lambda name: synth.layer_tensor(names.index(name)))
+    assert all(ok.values()) and len(ok) == len(names)
+    e = A.read_manifest(path)[0]
+    raw = bytearray(open(path, "rb").read())
+    raw[e.offset + 5000] ^= 0x01
+    bad = str(tmp_path / "bad.lbfa")
+    open(bad, "wb").write(bytes(raw))
+    with pytest.raises(A.ArtifactError):
+        A.load(bad, [e.name])
