@@ -275,6 +275,28 @@ def extras(torch, lbf, synth, Ws, blobs, rot, copies, args):
     res["decode_layer"] = {"us": round(ms * 1e3, 2), "bf16_equiv_GBs": round(2 * n / (ms * 1e-3) / 1e9, 1),
                            "hbm_GBs": round(alg / (ms * 1e-3) / 1e9, 1)}
     del outs
+    # integrity checks of the resident layer: structural verification of every
+    # blob (reads the nibble plane, index, escapes, header and padding) and
+    # CRC-32 of every whole blob
+    flags = torch.empty((len(blobs), 1), dtype=torch.int32, device="cuda")
+
+    def ver(i):
+        for j, b in enumerate(rot[i % copies]):
+            lbf.verify_into(b, flags[j])
+
+    ms = time_region(torch, ver, 20, 3)
+    assert int(flags.abs().sum()) == 0, "a resident blob failed verification"
+    vb = sum(b.nbytes - b.rows * b.cols for b in blobs)  # everything but the raw plane
+    res["verify_layer"] = {"us": round(ms * 1e3, 2), "GBs": round(vb / (ms * 1e-3) / 1e9, 1),
+                           "bytes_read": vb}
+
+    def crc(i):
+        for j, b in enumerate(rot[i % copies]):
+            lbf.crc32_into(b.data, flags[j])
+
+    ms = time_region(torch, crc, 20, 3)
+    cb = sum(b.nbytes for b in blobs)
+    res["crc32_layer"] = {"us": round(ms * 1e3, 2), "GBs": round(cb / (ms * 1e-3) / 1e9, 1), "bytes_read": cb}
     wd = [dev(torch, W) for W in Ws]
     xd = [dev(torch, synth.layer_x(m)) for m in range(len(Ws))]
     wrot = [wd] + [[w.clone() for w in wd] for _ in range(3)]

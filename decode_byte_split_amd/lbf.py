@@ -207,15 +207,30 @@ def decode(blob: Blob, out=None, stream=None):
 VERIFY_HEADER, VERIFY_INDEX, VERIFY_COUNT, VERIFY_CODE, VERIFY_ESCAPE, VERIFY_PADDING = 1, 2, 4, 8, 16, 32
 
 
+def verify_into(blob: Blob, flags, desc: Desc | None = None, stream=None) -> None:
+    """Enqueue the structural check of a device blob against ``desc`` (default:
+    its own descriptor); the failed-check mask lands in ``flags`` (a one-element
+    int32 or uint32 device tensor) when the stream reaches it.  Does not wait."""
+    d = blob.desc if desc is None else desc
+    _check(lib().lbf_verify(ctypes.byref(d), _ptr(blob.data), _ptr(flags), _stream(stream)), "lbf_verify")
+
+
 def verify(blob: Blob, desc: Desc | None = None, stream=None) -> int:
     """Structural check of a device blob against ``desc`` (default: its own
     descriptor) on the GPU; returns the failed-check mask (0: all pass).
     Waits for the stream."""
     torch = _torch()
     flags = torch.empty(1, dtype=torch.int32, device=blob.data.device)
-    d = blob.desc if desc is None else desc
-    _check(lib().lbf_verify(ctypes.byref(d), _ptr(blob.data), _ptr(flags), _stream(stream)), "lbf_verify")
+    verify_into(blob, flags, desc, stream)
     return int(flags.item()) & 0xFFFFFFFF
+
+
+def crc32_into(t, out, stream=None) -> None:
+    """Enqueue zlib's CRC-32 of a contiguous device tensor's bytes into ``out``
+    (a one-element int32 or uint32 device tensor).  Does not wait."""
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("crc32 takes a contiguous tensor on the GPU")
+    _check(lib().lbf_crc32(_ptr(t), t.numel() * t.element_size(), _ptr(out), _stream(stream)), "lbf_crc32")
 
 
 def crc32(t, stream=None) -> int:
@@ -225,7 +240,7 @@ def crc32(t, stream=None) -> int:
     if not t.is_cuda or not t.is_contiguous():
         raise ValueError("crc32 takes a contiguous tensor on the GPU")
     out = torch.empty(1, dtype=torch.int32, device=t.device)
-    _check(lib().lbf_crc32(_ptr(t), t.numel() * t.element_size(), _ptr(out), _stream(stream)), "lbf_crc32")
+    crc32_into(t, out, stream)
     return int(out.item()) & 0xFFFFFFFF
 
 
