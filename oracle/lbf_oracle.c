@@ -452,3 +452,309 @@ double lbfo_entropy_exponent(const uint16_t* w, uint64_t n) {
   }
   return h;
 }
+
+/* ---- the entropy-coded variant (K15H) ----------------------------------
+ * The English page's larger "K15" reduction belongs to an entropy-coded form
+ * of the same split (opening section), and DFloat11 entropy-codes the
+ * exponent while sign and mantissa stay raw (meowlab page, section 二).  Here
+ * the 4-bit K15 code of every weight (codes 0..14 for the table's exponents,
+ * 15 for an escape, exactly as above) is Huffman-coded; the raw plane, the
+ * escape index and the escape stream are those of format v1.
+ * Readings taken where the pages are silent (each is listed in the design doc):
+ *  - symbol counts are over the n real weights (not the tile padding);
+ *  - code lengths come from Huffman's procedure run with two queues: the used
+ *    symbols sorted by count, then by symbol, and the merged nodes in the
+ *    order they are made; each step merges the two lightest queue fronts, the
+ *    leaf queue winning a tie.  A lone used symbol gets length 1.  With at
+ *    most 16 symbols no length exceeds 15;
+ *  - codes are canonical as RFC 1951 section 3.2.2 defines them: shorter
+ *    codes first, equal lengths in symbol order, consecutive values;
+ *  - a code is written most significant bit first into a bit stream whose
+ *    bit k is bit k % 32 of 32-bit word k / 32 (little-endian words);
+ *  - each 1024-weight tile is its own stream of whole words, its codes in
+ *    element order, unused bits zero; woff[t] is the first word of tile t,
+ *    woff[n_t] the total word count.
+ * Blob layout (K15H), every plane starting at a multiple of 256:
+ *   [0,256)      header, 128 meaningful bytes, then zeros:
+ *                0 u32 magic 0x4846424C ("LBFH") | 4 u16 version 1 |
+ *                6 u16 tile_log2 10 | 8 u64 rows | 16 u64 cols | 24 u64 n_esc |
+ *                32 u64 off_raw | 40 u64 off_bits | 48 u64 off_woff |
+ *                56 u64 off_idx | 64 u64 off_esc | 72 u64 blob_bytes |
+ *                80 u64 stream_words | 88 u8 lut[16] | 104 u8 n_codes |
+ *                105 u8 max_len | 106..107 zero | 108 u8 len[16] |
+ *                124 u32 CRC-32 of bytes [0,124)
+ *   off_raw      raw plane, as format v1 (n_t * 1024 bytes)
+ *   off_bits     code stream, stream_words 32-bit words
+ *   off_woff     uint32 woff[n_t + 1]
+ *   off_idx      uint32 idx[n_t + 1], as format v1
+ *   off_esc      escape stream, as format v1
+ */
+
+/* Huffman code lengths of 16 symbols from their counts (two-queue form). */
+void lbfo_huffman_lengths(const uint64_t count[16], uint8_t len[16]) {
+  int leaf_sym[16], m = 0;
+  uint64_t weight[31];
+  int parent[31];
+  memset(len, 0, 16);
+  for (int s = 0; s < 16; s++)
+    if (count[s] > 0) leaf_sym[m++] = s;
+  if (m == 0) return;
+  if (m == 1) {
+    len[leaf_sym[0]] = 1;
+    return;
+  }
+  /* leaves sorted by (count, symbol): insertion sort, stable on symbol */
+  for (int i = 1; i < m; i++) {
+    int s = leaf_sym[i], j = i - 1;
+    while (j >= 0 && count[leaf_sym[j]] > count[s]) {
+      leaf_sym[j + 1] = leaf_sym[j];
+      j--;
+    }
+    leaf_sym[j + 1] = s;
+  }
+  for (int i = 0; i < m; i++) {
+    weight[i] = count[leaf_sym[i]];
+    parent[i] = -1;
+  }
+  int next_leaf = 0, next_node = m, made = m;
+  for (int step = 0; step < m - 1; step++) {
+    int pick[2];
+    for (int k = 0; k < 2; k++) {
+      int leaf_ok = next_leaf < m, node_ok = next_node < made;
+      if (leaf_ok && (!node_ok || weight[next_leaf] <= weight[next_node]))
+        pick[k] = next_leaf++;
+      else
+        pick[k] = next_node++;
+    }
+    weight[made] = weight[pick[0]] + weight[pick[1]];
+    parent[made] = -1;
+    parent[pick[0]] = parent[pick[1]] = made;
+    made++;
+  }
+  for (int i = 0; i < m; i++) {
+    int depth = 0;
+    for (int k = i; parent[k] >= 0; k = parent[k]) depth++;
+    len[leaf_sym[i]] = (uint8_t)depth;
+  }
+}
+
+/* Canonical code values from lengths (RFC 1951, section 3.2.2). */
+void lbfo_canonical_codes(const uint8_t len[16], uint16_t code[16]) {
+  unsigned bl_count[16] = {0}, next_code[16] = {0};
+  for (int s = 0; s < 16; s++)
+    if (len[s]) bl_count[len[s]]++;
+  unsigned c = 0;
+  for (int bits = 1; bits < 16; bits++) {
+    c = (c + bl_count[bits - 1]) << 1;
+    next_code[bits] = c;
+  }
+  for (int s = 0; s < 16; s++) code[s] = len[s] ? (uint16_t)next_code[len[s]]++ : 0;
+}
+
+typedef struct {
+  uint64_t n, n_tiles, n_esc, stream_words;
+  uint64_t off_raw, off_bits, off_woff, off_idx, off_esc, blob_bytes;
+} hlayout_t;
+
+static hlayout_t hlayout_for(uint64_t rows, uint64_t cols, uint64_t n_esc, uint64_t stream_words) {
+  hlayout_t L;
+  L.n = rows * cols;
+  L.n_tiles = (L.n + TILE - 1) / TILE;
+  L.n_esc = n_esc;
+  L.stream_words = stream_words;
+  L.off_raw = HEADER;
+  L.off_bits = round_up_256(L.off_raw + L.n_tiles * TILE);
+  L.off_woff = round_up_256(L.off_bits + 4u * stream_words);
+  L.off_idx = round_up_256(L.off_woff + 4u * (L.n_tiles + 1));
+  L.off_esc = round_up_256(L.off_idx + 4u * (L.n_tiles + 1));
+  L.blob_bytes = round_up_256(L.off_esc + n_esc);
+  return L;
+}
+
+/* The K15 code of every real weight, read from a format-v1 blob. */
+static unsigned v1_code(const uint8_t* nib, uint64_t i) { return (nib[code_byte(i)] >> code_shift(i)) & 15u; }
+
+/* Everything the K15H encoder decides before writing: the v1 plan, the code
+ * counts, the code lengths, the stream size and the blob size. */
+int lbfo_hplan(const uint16_t* w, uint64_t rows, uint64_t cols, uint64_t code_count[16], uint8_t len[16],
+               uint64_t* stream_words, uint64_t* blob_bytes) {
+  uint8_t lut[16], n_codes;
+  uint64_t n_esc, v1_bytes;
+  if (lbfo_plan(w, rows, cols, lut, &n_codes, &n_esc, &v1_bytes) != 0) return -1;
+  uint64_t n = rows * cols;
+  memset(code_count, 0, 16 * sizeof(uint64_t));
+  for (uint64_t i = 0; i < n; i++) code_count[code_of(exponent_of(w[i]), lut, n_codes)]++;
+  lbfo_huffman_lengths(code_count, len);
+  uint64_t words = 0;
+  for (uint64_t t = 0; t * TILE < n; t++) {
+    uint64_t bits = 0, end = (t + 1) * TILE < n ? (t + 1) * TILE : n;
+    for (uint64_t i = t * TILE; i < end; i++) bits += len[code_of(exponent_of(w[i]), lut, n_codes)];
+    words += (bits + 31) / 32;
+  }
+  *stream_words = words;
+  *blob_bytes = hlayout_for(rows, cols, n_esc, words).blob_bytes;
+  return 0;
+}
+
+/* Write the K15H blob of w: the v1 blob first (raw plane, codes, index,
+ * escapes), then its codes re-written as Huffman codes tile by tile. */
+int lbfo_hencode(const uint16_t* w, uint64_t rows, uint64_t cols, uint8_t* blob, uint64_t blob_cap) {
+  uint64_t code_count[16], words, bytes, v1_bytes, n_esc;
+  uint8_t len[16], lut[16], n_codes;
+  uint16_t code[16];
+  if (lbfo_hplan(w, rows, cols, code_count, len, &words, &bytes) != 0) return -1;
+  if (blob_cap < bytes) return -2;
+  if (lbfo_plan(w, rows, cols, lut, &n_codes, &n_esc, &v1_bytes) != 0) return -1;
+  uint8_t* v1 = (uint8_t*)malloc(v1_bytes);
+  if (!v1) return -3;
+  if (lbfo_encode(w, rows, cols, v1, v1_bytes) != 0) {
+    free(v1);
+    return -4;
+  }
+  layout_t V = layout_for(rows, cols, n_esc);
+  hlayout_t L = hlayout_for(rows, cols, n_esc, words);
+  lbfo_canonical_codes(len, code);
+  unsigned max_len = 0;
+  for (int s = 0; s < 16; s++)
+    if (len[s] > max_len) max_len = len[s];
+
+  memset(blob, 0, bytes);
+  put_u32(blob + 0, 0x4846424Cu);
+  put_u16(blob + 4, 1);
+  put_u16(blob + 6, 10);
+  put_u64(blob + 8, rows);
+  put_u64(blob + 16, cols);
+  put_u64(blob + 24, n_esc);
+  put_u64(blob + 32, L.off_raw);
+  put_u64(blob + 40, L.off_bits);
+  put_u64(blob + 48, L.off_woff);
+  put_u64(blob + 56, L.off_idx);
+  put_u64(blob + 64, L.off_esc);
+  put_u64(blob + 72, L.blob_bytes);
+  put_u64(blob + 80, words);
+  memcpy(blob + 88, lut, 16);
+  blob[104] = n_codes;
+  blob[105] = (uint8_t)max_len;
+  memcpy(blob + 108, len, 16);
+  put_u32(blob + 124, lbfo_crc32(blob, 124));
+
+  memcpy(blob + L.off_raw, v1 + V.off_raw, L.n_tiles * TILE);
+  memcpy(blob + L.off_idx, v1 + V.off_idx, 4u * (L.n_tiles + 1));
+  memcpy(blob + L.off_esc, v1 + V.off_esc, n_esc);
+
+  uint8_t* bits = blob + L.off_bits;
+  uint8_t* woff = blob + L.off_woff;
+  uint64_t word = 0; /* first word of the current tile */
+  for (uint64_t t = 0; t < L.n_tiles; t++) {
+    put_u32(woff + 4u * t, (uint32_t)word);
+    uint64_t k = 0; /* bit position inside the tile's stream */
+    uint64_t end = (t + 1) * TILE < L.n ? (t + 1) * TILE : L.n;
+    for (uint64_t i = t * TILE; i < end; i++) {
+      unsigned s = v1_code(v1 + V.off_nib, i);
+      for (int b = len[s] - 1; b >= 0; b--, k++) { /* most significant bit first */
+        if ((code[s] >> b) & 1u) {
+          uint64_t at = 4u * (word + k / 32) + (k % 32) / 8; /* byte of the little-endian word */
+          bits[at] |= (uint8_t)(1u << (k % 8));
+        }
+      }
+    }
+    word += (k + 31) / 32;
+  }
+  put_u32(woff + 4u * L.n_tiles, (uint32_t)word);
+  free(v1);
+  return word == words ? 0 : -5;
+}
+
+/* Read and check a K15H header: magic, version, CRC, shape, table, lengths
+ * (a complete prefix code when two or more symbols are used) and layout. */
+int lbfo_hread_header(const uint8_t* blob, uint64_t blob_len, uint64_t* rows, uint64_t* cols, uint64_t* n_esc,
+                      uint64_t* stream_words, uint8_t lut[16], uint8_t* n_codes, uint8_t len[16]) {
+  if (blob_len < HEADER) return -1;
+  if (get_u32(blob) != 0x4846424Cu) return -1;
+  if (blob[4] != 1 || blob[5] != 0 || blob[6] != 10 || blob[7] != 0) return -1;
+  if (get_u32(blob + 124) != lbfo_crc32(blob, 124)) return -1;
+  *rows = get_u64(blob + 8);
+  *cols = get_u64(blob + 16);
+  *n_esc = get_u64(blob + 24);
+  *stream_words = get_u64(blob + 80);
+  memcpy(lut, blob + 88, 16);
+  *n_codes = blob[104];
+  memcpy(len, blob + 108, 16);
+  if (*n_codes > 15) return -1;
+  if (*cols != 0 && *rows > UINT64_MAX / *cols) return -1;
+  if (*rows * *cols >= (1ull << 32)) return -1;
+  unsigned used = 0, max_len = 0;
+  double kraft = 0.0;
+  for (int s = 0; s < 16; s++) {
+    if (len[s] > 15) return -1;
+    if (!len[s]) continue;
+    used++;
+    kraft += ldexp(1.0, -(int)len[s]);
+    if (len[s] > max_len) max_len = len[s];
+  }
+  if (blob[105] != max_len) return -1;
+  if (used >= 2 && kraft != 1.0) return -1;
+  if (used == 1 && max_len != 1) return -1;
+  hlayout_t L = hlayout_for(*rows, *cols, *n_esc, *stream_words);
+  if (get_u64(blob + 32) != L.off_raw || get_u64(blob + 40) != L.off_bits || get_u64(blob + 48) != L.off_woff ||
+      get_u64(blob + 56) != L.off_idx || get_u64(blob + 64) != L.off_esc || get_u64(blob + 72) != L.blob_bytes ||
+      blob_len < L.blob_bytes)
+    return -1;
+  return 0;
+}
+
+/* Decode a K15H blob: per tile, read codes bit by bit (a code is complete
+ * when its value and length match a symbol's canonical code), then rebuild
+ * each weight from its raw byte and its exponent as format v1 does. */
+int lbfo_hdecode(const uint8_t* blob, uint64_t blob_len, uint16_t* out, uint64_t out_len) {
+  uint64_t rows, cols, n_esc, words;
+  uint8_t lut[16], n_codes, len[16];
+  uint16_t code[16];
+  if (lbfo_hread_header(blob, blob_len, &rows, &cols, &n_esc, &words, lut, &n_codes, len) != 0) return -1;
+  hlayout_t L = hlayout_for(rows, cols, n_esc, words);
+  if (out_len < L.n) return -2;
+  lbfo_canonical_codes(len, code);
+  const uint8_t* raw = blob + L.off_raw;
+  const uint8_t* bits = blob + L.off_bits;
+  const uint8_t* woff = blob + L.off_woff;
+  const uint8_t* idx = blob + L.off_idx;
+  const uint8_t* esc = blob + L.off_esc;
+  if (get_u32(woff) != 0 || get_u32(woff + 4u * L.n_tiles) != words) return -3;
+  if (get_u32(idx) != 0 || get_u32(idx + 4u * L.n_tiles) != n_esc) return -3;
+
+  for (uint64_t t = 0; t < L.n_tiles; t++) {
+    uint64_t w0 = get_u32(woff + 4u * t), w1 = get_u32(woff + 4u * (t + 1));
+    uint64_t first = get_u32(idx + 4u * t), last = get_u32(idx + 4u * (t + 1));
+    if (w1 < w0 || w1 > words || last < first || last > n_esc) return -3;
+    uint64_t k = 0, limit = 32u * (w1 - w0), seen = 0;
+    uint64_t end = (t + 1) * TILE < L.n ? (t + 1) * TILE : L.n;
+    for (uint64_t i = t * TILE; i < end; i++) {
+      unsigned value = 0, s = 16;
+      for (unsigned l = 1; l <= 15 && s == 16; l++) {
+        if (k >= limit) return -3;
+        uint64_t at = 4u * (w0 + k / 32) + (k % 32) / 8;
+        value = (value << 1) | ((bits[at] >> (k % 8)) & 1u);
+        k++;
+        for (unsigned c = 0; c < 16; c++)
+          if (len[c] == l && code[c] == value) s = c;
+      }
+      if (s == 16) return -3;
+      unsigned e;
+      if (s == 15u) {
+        if (first + seen >= last) return -3;
+        e = esc[first + seen++];
+      } else {
+        if (s >= n_codes) return -3;
+        e = lut[s];
+      }
+      unsigned sg = raw[i ^ 1u] & 1u, m = raw[i] >> 1;
+      out[i] = (uint16_t)((sg << 15) | (e << 7) | m);
+    }
+    if (first + seen != last) return -3;
+    for (; k < limit; k++) { /* bits after the tile's last code are zero */
+      uint64_t at = 4u * (w0 + k / 32) + (k % 32) / 8;
+      if ((bits[at] >> (k % 8)) & 1u) return -3;
+    }
+  }
+  return 0;
+}

@@ -66,6 +66,18 @@ def lib():
         L.lbfo_entropy_exponent.argtypes = [_u16p, _u64]
         L.lbfo_verify.restype = ctypes.c_uint
         L.lbfo_verify.argtypes = [_u8p, _u64, _u8p]
+        L.lbfo_huffman_lengths.restype = None
+        L.lbfo_huffman_lengths.argtypes = [_u64p, _u8p]
+        L.lbfo_canonical_codes.restype = None
+        L.lbfo_canonical_codes.argtypes = [_u8p, _u16p]
+        L.lbfo_hplan.restype = ctypes.c_int
+        L.lbfo_hplan.argtypes = [_u16p, _u64, _u64, _u64p, _u8p, _u64p, _u64p]
+        L.lbfo_hencode.restype = ctypes.c_int
+        L.lbfo_hencode.argtypes = [_u16p, _u64, _u64, _u8p, _u64]
+        L.lbfo_hread_header.restype = ctypes.c_int
+        L.lbfo_hread_header.argtypes = [_u8p, _u64, _u64p, _u64p, _u64p, _u64p, _u8p, _u8p, _u8p]
+        L.lbfo_hdecode.restype = ctypes.c_int
+        L.lbfo_hdecode.argtypes = [_u8p, _u64, _u16p, _u64]
         _lib = L
     return _lib
 
@@ -217,3 +229,92 @@ def entropy16(w: np.ndarray) -> float:
 def entropy_exponent(w: np.ndarray) -> float:
     w = _bf16(w).reshape(-1)
     return float(lib().lbfo_entropy_exponent(_p(w, _u16p), w.size))
+
+
+# ---- the entropy-coded variant (K15H) --------------------------------------
+
+
+def huffman_lengths(count) -> np.ndarray:
+    """Huffman code lengths (uint8[16]) of 16 symbols from their counts."""
+    c = np.ascontiguousarray(count, dtype=np.uint64)
+    assert c.size == 16
+    out = np.zeros(16, dtype=np.uint8)
+    lib().lbfo_huffman_lengths(_p(c, _u64p), _p(out, _u8p))
+    return out
+
+
+def canonical_codes(lengths) -> np.ndarray:
+    """Canonical code values (uint16[16]) for 16 code lengths (0 = unused)."""
+    ln = np.ascontiguousarray(lengths, dtype=np.uint8)
+    assert ln.size == 16
+    out = np.zeros(16, dtype=np.uint16)
+    lib().lbfo_canonical_codes(_p(ln, _u8p), _p(out, _u16p))
+    return out
+
+
+@dataclass
+class HPlan:
+    code_count: np.ndarray
+    lengths: np.ndarray
+    stream_words: int
+    blob_bytes: int
+
+
+def hplan(w: np.ndarray) -> HPlan:
+    w = _bf16(w)
+    rows, cols = w.shape
+    cc = np.zeros(16, dtype=np.uint64)
+    ln = np.zeros(16, dtype=np.uint8)
+    sw, bb = ctypes.c_uint64(0), ctypes.c_uint64(0)
+    rc = lib().lbfo_hplan(_p(w, _u16p), rows, cols, _p(cc, _u64p), _p(ln, _u8p), ctypes.byref(sw), ctypes.byref(bb))
+    if rc != 0:
+        raise ValueError("oracle hplan failed (%d)" % rc)
+    return HPlan(cc, ln, int(sw.value), int(bb.value))
+
+
+def hencode(w: np.ndarray) -> np.ndarray:
+    """Encode a 2-D uint16 (bf16 bits) array into a K15H blob (uint8)."""
+    w = _bf16(w)
+    if w.ndim != 2:
+        raise ValueError("hencode takes a 2-D [rows, cols] array")
+    rows, cols = w.shape
+    pl = hplan(w)
+    blob = np.zeros(pl.blob_bytes, dtype=np.uint8)
+    rc = lib().lbfo_hencode(_p(w, _u16p), rows, cols, _p(blob, _u8p), blob.size)
+    if rc != 0:
+        raise ValueError("oracle hencode failed (%d)" % rc)
+    return blob
+
+
+@dataclass
+class HHeader:
+    rows: int
+    cols: int
+    n_esc: int
+    stream_words: int
+    lut: np.ndarray
+    n_codes: int
+    lengths: np.ndarray
+
+
+def hread_header(blob: np.ndarray) -> HHeader:
+    blob = np.ascontiguousarray(blob, dtype=np.uint8)
+    r, c, e, sw = (ctypes.c_uint64(0) for _ in range(4))
+    lut = np.zeros(16, dtype=np.uint8)
+    ln = np.zeros(16, dtype=np.uint8)
+    nc = ctypes.c_uint8(0)
+    rc = lib().lbfo_hread_header(_p(blob, _u8p), blob.size, ctypes.byref(r), ctypes.byref(c), ctypes.byref(e),
+                                 ctypes.byref(sw), _p(lut, _u8p), ctypes.byref(nc), _p(ln, _u8p))
+    if rc != 0:
+        raise ValueError("oracle: bad K15H header (%d)" % rc)
+    return HHeader(int(r.value), int(c.value), int(e.value), int(sw.value), lut, int(nc.value), ln)
+
+
+def hdecode(blob: np.ndarray) -> np.ndarray:
+    blob = np.ascontiguousarray(blob, dtype=np.uint8)
+    h = hread_header(blob)
+    out = np.zeros((h.rows, h.cols), dtype=np.uint16)
+    rc = lib().lbfo_hdecode(_p(blob, _u8p), blob.size, _p(out, _u16p), out.size)
+    if rc != 0:
+        raise ValueError("oracle hdecode failed (%d)" % rc)
+    return out
