@@ -15,6 +15,11 @@ static_assert(sizeof(lbf_desc) == 96, "descriptor must be 96 bytes");
 static_assert(offsetof(lbf_desc, lut) == 72, "descriptor layout");
 static_assert(offsetof(lbf_desc, n_codes) == 88, "descriptor layout");
 static_assert(offsetof(lbf_desc, desc_crc) == 92, "descriptor layout");
+static_assert(sizeof(lbf_hdesc) == 128, "K15H descriptor must be 128 bytes");
+static_assert(offsetof(lbf_hdesc, lut) == 88, "K15H descriptor layout");
+static_assert(offsetof(lbf_hdesc, n_codes) == 104, "K15H descriptor layout");
+static_assert(offsetof(lbf_hdesc, len) == 108, "K15H descriptor layout");
+static_assert(offsetof(lbf_hdesc, desc_crc) == 124, "K15H descriptor layout");
 
 namespace lbf {
 
@@ -50,19 +55,21 @@ uint32_t crc32(const void* data, size_t len) {
   return c ^ 0xFFFFFFFFu;
 }
 
-KLut klut_of(const lbf_desc& d) {
+KLut klut_from(const uint8_t lut[16], int n_codes) {
   KLut k;
   for (int q = 0; q < 4; q++)
-    k.t[q] = d.lut[4 * q] | (d.lut[4 * q + 1] << 8) | (d.lut[4 * q + 2] << 16) | ((uint32_t)d.lut[4 * q + 3] << 24);
-  k.base4 = d.lut[0] * 0x01010101u;
-  k.contiguous = d.n_codes > 0;
-  for (int c = 0; c < d.n_codes; c++)
-    if (d.lut[c] != d.lut[0] + c) k.contiguous = 0;
+    k.t[q] = lut[4 * q] | (lut[4 * q + 1] << 8) | (lut[4 * q + 2] << 16) | ((uint32_t)lut[4 * q + 3] << 24);
+  k.base4 = lut[0] * 0x01010101u;
+  k.contiguous = n_codes > 0;
+  for (int c = 0; c < n_codes; c++)
+    if (lut[c] != lut[0] + c) k.contiguous = 0;
   // codes >= n_codes never occur, so lut[0] + c only has to be right below n_codes;
   // the byte-wise add must not carry: lut[0] + 15 <= 255
-  if (d.lut[0] > 240) k.contiguous = 0;
+  if (lut[0] > 240) k.contiguous = 0;
   return k;
 }
+
+KLut klut_of(const lbf_desc& d) { return klut_from(d.lut, d.n_codes); }
 
 static bool shape_ok(uint64_t rows, uint64_t cols) {
   if (cols != 0 && rows > UINT64_MAX / cols) return false;
@@ -88,6 +95,48 @@ static int check(const lbf_desc* d) {
   // fewer than 15 coded exponents means every exponent present got a code
   if (d->n_codes < 15 && d->n_esc != 0) return LBF_E_DESC;
   if (L.n > 0 && d->n_codes == 0) return LBF_E_DESC;
+  return LBF_OK;
+}
+
+// Code table rules shared by both descriptors.
+static bool table_ok(const uint8_t lut[16], int n_codes, uint64_t n, uint64_t n_esc) {
+  if (n_codes > 15) return false;
+  for (int c = 1; c < n_codes; c++)
+    if (lut[c] <= lut[c - 1]) return false;
+  for (int c = n_codes; c < 16; c++)
+    if (lut[c] != 0) return false;
+  // fewer than 15 coded exponents means every exponent present got a code
+  if (n_codes < 15 && n_esc != 0) return false;
+  if (n > 0 && n_codes == 0) return false;
+  return true;
+}
+
+static int hcheck(const lbf_hdesc* h) {
+  if (!h) return LBF_E_INVAL;
+  if (h->magic != LBF_HMAGIC || h->version != LBF_HVERSION || h->tile_log2 != LBF_TILE_LOG2) return LBF_E_DESC;
+  if (crc32(h, offsetof(lbf_hdesc, desc_crc)) != h->desc_crc) return LBF_E_DESC;
+  if (!shape_ok(h->rows, h->cols)) return LBF_E_DESC;
+  const HLayout L = hlayout_of(h->rows, h->cols, h->n_esc, h->stream_words);
+  if (h->n_esc > L.n || h->stream_words > L.n_tiles * LBF_HMAX_TILE_WORDS) return LBF_E_DESC;
+  if (h->off_raw != L.off_raw || h->off_bits != L.off_bits || h->off_woff != L.off_woff ||
+      h->off_idx != L.off_idx || h->off_esc != L.off_esc || h->blob_bytes != L.blob_bytes)
+    return LBF_E_DESC;
+  if (!table_ok(h->lut, h->n_codes, L.n, h->n_esc) || h->reserved[0] | h->reserved[1]) return LBF_E_DESC;
+  // lengths: exactly the codes that occur (the table's, and 15 when there are
+  // escapes) have one, forming a complete prefix code (one code: length 1)
+  uint32_t kraft = 0, used = 0, max_len = 0;
+  for (int c = 0; c < 16; c++) {
+    const bool occurs = c < h->n_codes || (c == 15 && h->n_esc > 0);
+    if (h->len[c] > 15 || (h->len[c] != 0) != occurs) return LBF_E_DESC;
+    if (!h->len[c]) continue;
+    used++;
+    kraft += 1u << (15 - h->len[c]);
+    max_len = std::max<uint32_t>(max_len, h->len[c]);
+  }
+  if (h->max_len != max_len) return LBF_E_DESC;
+  if (used >= 2 && kraft != (1u << 15)) return LBF_E_DESC;
+  if (used == 1 && max_len != 1) return LBF_E_DESC;
+  if (used == 0 && (L.n != 0 || h->stream_words != 0)) return LBF_E_DESC;
   return LBF_OK;
 }
 
@@ -215,6 +264,111 @@ int lbf_encode(const void* d_w, uint64_t rows, uint64_t cols, void* d_work, uint
   if (!aligned(d_blob, 256)) return LBF_E_ALIGN;
   if (blob_cap < desc->blob_bytes) return LBF_E_CAPACITY;
   if (launch_pack(static_cast<const uint16_t*>(d_w), *desc, static_cast<uint8_t*>(d_blob), tile_cnt, s) != hipSuccess)
+    return LBF_E_HIP;
+  return LBF_OK;
+}
+
+int lbf_hdesc_check(const lbf_hdesc* hdesc) { return hcheck(hdesc); }
+
+static uint64_t up256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
+
+uint64_t lbf_hencode_work_bytes(const lbf_desc* desc) {
+  if (check(desc)) return 0;
+  const Layout L = layout_of(desc->rows, desc->cols, desc->n_esc);
+  return 256 + up256(4 * L.n_tiles) + up256(4 * (L.n_tiles + 1));
+}
+
+int lbf_hencode(const lbf_desc* desc, const void* d_blob, void* d_work, uint64_t work_bytes, void* d_hblob,
+                uint64_t hblob_cap, lbf_hdesc* hdesc, hipStream_t s) {
+  const int rc = check(desc);
+  if (rc) return rc;
+  if (!hdesc || !d_work || !d_blob) return LBF_E_INVAL;
+  if (!aligned(d_blob, 256) || !aligned(d_work, 256)) return LBF_E_ALIGN;
+  if (work_bytes < lbf_hencode_work_bytes(desc)) return LBF_E_CAPACITY;
+  const Layout V = layout_of(desc->rows, desc->cols, desc->n_esc);
+  const uint8_t* blob = static_cast<const uint8_t*>(d_blob);
+  uint8_t* work = static_cast<uint8_t*>(d_work);
+  uint32_t* counts = reinterpret_cast<uint32_t*>(work);
+  uint32_t* words = reinterpret_cast<uint32_t*>(work + 256);
+  uint32_t* woff = reinterpret_cast<uint32_t*>(work + 256 + up256(4 * V.n_tiles));
+  if (!d_hblob) {  // phase 1
+    uint32_t cnt[16] = {0};
+    if (V.n) {
+      if (launch_hcount(*desc, blob, counts, s) != hipSuccess) return LBF_E_HIP;
+      if (hipMemcpyAsync(cnt, counts, sizeof cnt, hipMemcpyDeviceToHost, s) != hipSuccess) return LBF_E_HIP;
+      if (hipStreamSynchronize(s) != hipSuccess) return LBF_E_HIP;
+    }
+    uint64_t total = 0, c64[16];
+    for (int c = 0; c < 16; c++) total += c64[c] = cnt[c];
+    if (total != V.n) return LBF_E_HIP;  // the counts must account for every weight
+    if (cnt[15] != desc->n_esc) return LBF_E_DESC;
+    for (int c = desc->n_codes; c < 15; c++)
+      if (cnt[c]) return LBF_E_DESC;  // an unused code: not a valid v1 blob
+    uint8_t len[16];
+    huffman_lengths(c64, len);
+    uint32_t stream_words = 0;
+    if (launch_hwoff(*desc, blob, len, words, woff, s) != hipSuccess) return LBF_E_HIP;
+    if (hipMemcpyAsync(&stream_words, woff + V.n_tiles, 4, hipMemcpyDeviceToHost, s) != hipSuccess) return LBF_E_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return LBF_E_HIP;
+    const HLayout H = hlayout_of(desc->rows, desc->cols, desc->n_esc, stream_words);
+    std::memset(hdesc, 0, sizeof(*hdesc));
+    hdesc->magic = LBF_HMAGIC;
+    hdesc->version = LBF_HVERSION;
+    hdesc->tile_log2 = LBF_TILE_LOG2;
+    hdesc->rows = desc->rows;
+    hdesc->cols = desc->cols;
+    hdesc->n_esc = desc->n_esc;
+    hdesc->off_raw = H.off_raw;
+    hdesc->off_bits = H.off_bits;
+    hdesc->off_woff = H.off_woff;
+    hdesc->off_idx = H.off_idx;
+    hdesc->off_esc = H.off_esc;
+    hdesc->blob_bytes = H.blob_bytes;
+    hdesc->stream_words = stream_words;
+    std::memcpy(hdesc->lut, desc->lut, 16);
+    hdesc->n_codes = desc->n_codes;
+    for (int c = 0; c < 16; c++) {
+      hdesc->len[c] = len[c];
+      hdesc->max_len = std::max(hdesc->max_len, len[c]);
+    }
+    hdesc->desc_crc = crc32(hdesc, offsetof(lbf_hdesc, desc_crc));
+    return LBF_OK;
+  }
+  // phase 2
+  const int hrc = hcheck(hdesc);
+  if (hrc) return hrc;
+  if (hdesc->rows != desc->rows || hdesc->cols != desc->cols || hdesc->n_esc != desc->n_esc ||
+      hdesc->n_codes != desc->n_codes || std::memcmp(hdesc->lut, desc->lut, 16) != 0)
+    return LBF_E_DESC;
+  if (!aligned(d_hblob, 256)) return LBF_E_ALIGN;
+  if (hblob_cap < hdesc->blob_bytes) return LBF_E_CAPACITY;
+  const HLayout H = hlayout_of(hdesc->rows, hdesc->cols, hdesc->n_esc, hdesc->stream_words);
+  uint8_t* out = static_cast<uint8_t*>(d_hblob);
+  uint32_t* out_woff = reinterpret_cast<uint32_t*>(out + H.off_woff);
+  if (launch_hfill(*hdesc, out, s) != hipSuccess) return LBF_E_HIP;
+  if (hipMemcpyAsync(out + H.off_raw, blob + V.off_raw, V.n_tiles * LBF_TILE, hipMemcpyDeviceToDevice, s) !=
+          hipSuccess ||
+      hipMemcpyAsync(out + H.off_idx, blob + V.off_idx, 4 * (V.n_tiles + 1), hipMemcpyDeviceToDevice, s) !=
+          hipSuccess)
+    return LBF_E_HIP;
+  if (V.n_esc &&
+      hipMemcpyAsync(out + H.off_esc, blob + V.off_esc, V.n_esc, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return LBF_E_HIP;
+  if (launch_hwoff(*desc, blob, hdesc->len, words, out_woff, s) != hipSuccess) return LBF_E_HIP;
+  if (launch_hpack(*desc, blob, hcode_of(hdesc->len), out_woff, reinterpret_cast<uint32_t*>(out + H.off_bits),
+                   hdesc->stream_words, s) != hipSuccess)
+    return LBF_E_HIP;
+  return LBF_OK;
+}
+
+int lbf_hdecode(const lbf_hdesc* hdesc, const void* d_hblob, void* d_w_out, hipStream_t s) {
+  const int rc = hcheck(hdesc);
+  if (rc) return rc;
+  if (hdesc->rows * hdesc->cols == 0) return LBF_OK;
+  if (!d_hblob || !d_w_out) return LBF_E_INVAL;
+  if (!aligned(d_hblob, 256) || !aligned(d_w_out, 16)) return LBF_E_ALIGN;
+  if (launch_hdecode(*hdesc, hcode_of(hdesc->len), static_cast<const uint8_t*>(d_hblob),
+                     static_cast<uint16_t*>(d_w_out), s) != hipSuccess)
     return LBF_E_HIP;
   return LBF_OK;
 }

@@ -1,0 +1,512 @@
+// lbf_huff.hip — K15H, the entropy-coded variant: format v1's 4-bit codes
+// Huffman-coded tile by tile, and their GPU decoder.  The English page's
+// larger K15 reduction is for an entropy-coded form of the split ("Lossless
+// LLM Weight Compression vs 8-bit GGUF", opening section); DFloat11 codes the
+// exponent this way and keeps sign and mantissa raw ("你的 bf16 模型,有 5 個
+// bit 是廢的", section 二).  The format is declared in include/lbf.h.
+//
+// Re-coding a v1 blob (all reads of its codes are coalesced 8-byte loads):
+//   k_hcount        code counts over the real weights
+//   k_htile_words   32-bit words of every tile's stream
+//   k_hscan         one workgroup: woff[t] = words of tiles before t
+//   k_hpack         one wave per tile: each lane's codes are OR-ed into the
+//                   tile's words in LDS at the lane's prefix bit offset, then
+//                   the words are written out coalesced
+//
+// Decoding (k_hdecode, one wave per tile, persistent grid): the only side
+// information is each tile's first word, so lanes cannot know where their
+// codes start.  The tile's stream is staged in LDS and cut into 64 equal bit
+// windows; lane l decodes the codes that start inside window l, starting
+// first at the window's first bit (a guess for every lane but lane 0).  A
+// prefix code decoded from a wrong bit position typically falls back into
+// step with the true code boundaries within a few codes, so most guessed
+// lanes already end where the truth ends.  The wave then repeats: every lane
+// takes the end position of the lane before it as its start; lanes whose
+// start changed decode again; this stops when no start changes (lane l is
+// exact after at most l rounds, typically one or two).  A prefix sum of the
+// lanes' code counts places every code at its weight index in LDS, and the
+// rest is format v1's decode: the table exponents, the escapes of the tile
+// and the raw bytes assembled into BF16.  Codes of up to 12 bits are found
+// with one lookup in a 4096-entry LDS table indexed by the next 12 stream
+// bits; longer ones (rare: escapes and outlier exponents) by comparing the
+// next 15 bits against each symbol's code.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <vector>
+
+#include "lbf_device.h"
+#include "lbf_internal.h"
+
+namespace lbf {
+
+constexpr int kHWaves = 4;                               // encode kernels
+constexpr int kHDecWaves = 8;                            // decoder
+constexpr uint32_t kHTableBits = 12;                     // primary decode table
+constexpr uint32_t kHMaxWords = LBF_HMAX_TILE_WORDS;     // words of one tile's stream
+constexpr uint32_t kHWordsLds = kHMaxWords + 2;          // + zero guard words
+
+// Code of weight 16 lane + q from the lane's two split-half nibble words.
+__device__ __forceinline__ uint32_t code_at(u32x2 nib, int q) {
+  const uint32_t word = (q < 8) ? nib.x : nib.y;
+  return (word >> (8 * (q & 3) + 4 * ((q >> 2) & 1))) & 15u;
+}
+
+__global__ void k_hzero(uint32_t* p, uint32_t n) {
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+// Code counts: per-wave LDS bins, then one global add per bin and block.
+__global__ __launch_bounds__(kHWaves * kWave) void k_hcount(const uint8_t* __restrict__ nib, uint64_t n,
+                                                            uint64_t n_tiles, uint32_t* __restrict__ counts) {
+  __shared__ uint32_t h[kHWaves][16];
+  const uint32_t wave = threadIdx.x >> 6;
+  if (threadIdx.x < kHWaves * 16) (&h[0][0])[threadIdx.x] = 0u;
+  __syncthreads();
+  const uint64_t groups = n_tiles * kWave;  // 16 weights (8 nibble bytes) each
+  for (uint64_t g = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; g < groups;
+       g += (uint64_t)gridDim.x * blockDim.x) {
+    const u32x2 v = load_nt(reinterpret_cast<const u32x2*>(nib) + g);
+    const uint64_t w0 = g * 16;
+#pragma unroll
+    for (int q = 0; q < 16; q++)
+      if (w0 + q < n) atomicAdd(&h[wave][code_at(v, q)], 1u);
+  }
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    uint32_t s = 0;
+    for (int w = 0; w < kHWaves; w++) s += h[w][threadIdx.x];
+    if (s) atomicAdd(&counts[threadIdx.x], s);
+  }
+}
+
+// Length of code c from the 16 lengths packed 4 bits each into two words.
+__device__ __forceinline__ uint32_t packed_len(uint32_t c, uint32_t len_lo, uint32_t len_hi) {
+  return ((c < 8 ? len_lo : len_hi) >> (4 * (c & 7u))) & 15u;
+}
+
+__global__ __launch_bounds__(kHWaves * kWave) void k_htile_words(const uint8_t* __restrict__ nib, uint64_t n,
+                                                                 uint64_t n_tiles, uint32_t len_lo, uint32_t len_hi,
+                                                                 uint32_t* __restrict__ words) {
+  const int lane = lane_id();
+  const uint64_t t = (uint64_t)blockIdx.x * kHWaves + (threadIdx.x >> 6);
+  if (t >= n_tiles) return;
+  const u32x2 v = load_nt(reinterpret_cast<const u32x2*>(nib + t * (kTile / 2)) + lane);
+  const uint64_t w0 = t * kTile + (uint64_t)lane * 16;
+  uint32_t bits = 0;
+#pragma unroll
+  for (int q = 0; q < 16; q++)
+    if (w0 + q < n) bits += packed_len(code_at(v, q), len_lo, len_hi);
+  for (int o = 32; o >= 1; o >>= 1) bits += (uint32_t)__shfl_xor((int)bits, o, kWave);
+  if (lane == 0) words[t] = (bits + 31) / 32;
+}
+
+// woff[0] = 0, woff[t + 1] = woff[t] + words[t]; one workgroup of 1024.
+__global__ __launch_bounds__(1024) void k_hscan(const uint32_t* __restrict__ words, uint64_t n_tiles,
+                                                uint32_t* __restrict__ woff) {
+  __shared__ uint32_t part[1024];
+  __shared__ uint32_t carry;
+  const uint32_t tid = threadIdx.x;
+  if (tid == 0) {
+    carry = 0;
+    woff[0] = 0;
+  }
+  __syncthreads();
+  for (uint64_t base = 0; base < n_tiles; base += 1024) {
+    part[tid] = (base + tid < n_tiles) ? words[base + tid] : 0u;
+    __syncthreads();
+    for (uint32_t d = 1; d < 1024; d <<= 1) {  // inclusive scan
+      const uint32_t add = tid >= d ? part[tid - d] : 0u;
+      __syncthreads();
+      part[tid] += add;
+      __syncthreads();
+    }
+    if (base + tid < n_tiles) woff[base + tid + 1] = carry + part[tid];
+    __syncthreads();
+    if (tid == 0) carry += part[1023];
+    __syncthreads();
+  }
+}
+
+struct HPackArgs {
+  const uint8_t* nib;
+  const uint32_t* woff;
+  uint32_t* bits;
+  uint64_t n, n_tiles, stream_words;
+  uint32_t sym[16];  // reversed code << 4 | length
+};
+
+__global__ __launch_bounds__(kHWaves * kWave) void k_hpack(HPackArgs a) {
+  __shared__ uint32_t buf[kHWaves][kHWordsLds];
+  __shared__ uint32_t symtab[16];
+  const uint32_t wave = threadIdx.x >> 6;
+  const int lane = lane_id();
+  if (threadIdx.x < 16) symtab[threadIdx.x] = a.sym[threadIdx.x];
+  __syncthreads();
+  const uint64_t t = (uint64_t)blockIdx.x * kHWaves + wave;
+  if (t >= a.n_tiles) return;
+  uint32_t* tb = buf[wave];
+  for (uint32_t i = (uint32_t)lane; i < kHWordsLds; i += kWave) tb[i] = 0u;
+  const u32x2 v = load_nt(reinterpret_cast<const u32x2*>(a.nib + t * (kTile / 2)) + lane);
+  const uint64_t w0 = t * kTile + (uint64_t)lane * 16;
+  uint32_t nbits = 0;
+#pragma unroll
+  for (int q = 0; q < 16; q++)
+    if (w0 + q < a.n) nbits += symtab[code_at(v, q)] & 15u;
+  // exclusive prefix of the lanes' bit counts (each < 256), bit by bit
+  uint32_t pos = 0;
+#pragma unroll
+  for (int b = 0; b < 8; b++) pos += ballot_rank(__builtin_amdgcn_ballot_w64((nbits >> b) & 1u)) << b;
+  wave_lds_sync();
+  uint32_t wi = pos >> 5, nacc = pos & 31u;
+  uint64_t acc = 0;  // pending bits of word wi, from bit 0 (bits below pos belong to earlier lanes)
+#pragma unroll
+  for (int q = 0; q < 16; q++) {
+    if (w0 + q < a.n) {
+      const uint32_t e = symtab[code_at(v, q)];
+      acc |= (uint64_t)(e >> 4) << nacc;
+      nacc += e & 15u;
+      if (nacc >= 32) {
+        if (wi < kHMaxWords) atomicOr(&tb[wi], (uint32_t)acc);
+        acc >>= 32;
+        nacc -= 32;
+        wi++;
+      }
+    }
+  }
+  if (nacc && wi < kHMaxWords) atomicOr(&tb[wi], (uint32_t)acc);
+  wave_lds_sync();
+  const uint64_t base = a.woff[t];
+  uint64_t nw = a.woff[t + 1] - base;
+  if (a.woff[t + 1] < base) nw = 0;
+  if (nw > kHMaxWords) nw = kHMaxWords;
+  for (uint32_t i = (uint32_t)lane; i < nw; i += kWave)
+    if (base + i < a.stream_words) a.bits[base + i] = tb[i];
+}
+
+// ---- decoder ---------------------------------------------------------------------
+
+struct HDecArgs {
+  const uint8_t* raw;
+  const uint32_t* bits;
+  const uint32_t* woff;
+  const uint32_t* idx;
+  const uint8_t* esc;
+  uint16_t* out;
+  uint32_t n, n_tiles, n_esc, stream_words;
+  uint32_t waves;  // waves in the grid
+  Lut lut;
+  uint32_t base4;
+  uint32_t sym[16];  // reversed code << 4 | length
+};
+
+// Symbol << 4 | length of the code at stream bit pos (W: the tile's words).
+__device__ __forceinline__ uint32_t hdec(const uint32_t* W, const uint8_t* table, const uint32_t* symtab,
+                                         uint32_t pos) {
+  const uint32_t i = pos >> 5;
+  const uint32_t v = __builtin_amdgcn_alignbit(W[i + 1], W[i], pos & 31u);
+  uint32_t e = table[v & ((1u << kHTableBits) - 1)];
+  if ((e & 15u) == 0) {  // a code longer than the table: match the next 15 bits
+    e = 1u;              // no match (corrupt stream): symbol 0, one bit, so decoding moves on
+    for (int s = 0; s < 16; s++) {
+      const uint32_t d = symtab[s], L = d & 15u;
+      if (L > kHTableBits && (v & ((1u << L) - 1)) == (d >> 4)) e = ((uint32_t)s << 4) | L;
+    }
+  }
+  return e;
+}
+
+// Decode the codes that start in [pos, hi): their count and the end of the last.
+__device__ __forceinline__ void hrun(const uint32_t* W, const uint8_t* table, const uint32_t* symtab, uint32_t pos,
+                                     uint32_t hi, uint32_t& end, uint32_t& cnt) {
+  uint32_t c = 0;
+  while (pos < hi) {
+    pos += hdec(W, table, symtab, pos) & 15u;
+    c++;
+  }
+  end = pos;
+  cnt = c;
+}
+
+template <bool CONTIG>
+__global__ __launch_bounds__(kHDecWaves * kWave) void k_hdecode(HDecArgs a) {
+  __shared__ uint8_t table[1u << kHTableBits];
+  __shared__ uint32_t symtab[16];
+  __shared__ uint32_t words[kHDecWaves][kHWordsLds];
+  __shared__ __align__(16) uint8_t codes[kHDecWaves][kTile];
+  __shared__ uint8_t esc_lds[kHDecWaves][kTile];
+  const uint32_t wave = threadIdx.x >> 6;
+  const int lane = lane_id();
+  if (threadIdx.x < 16) symtab[threadIdx.x] = a.sym[threadIdx.x];
+  __syncthreads();
+  for (uint32_t i = threadIdx.x; i < (1u << kHTableBits); i += blockDim.x) {
+    uint32_t e = 0;
+    for (int s = 0; s < 16; s++) {
+      const uint32_t d = symtab[s], L = d & 15u;
+      if (L && L <= kHTableBits && (i & ((1u << L) - 1)) == (d >> 4)) e = ((uint32_t)s << 4) | L;
+    }
+    table[i] = (uint8_t)e;
+  }
+  __syncthreads();
+  uint32_t* W = words[wave];
+  uint8_t* C = codes[wave];
+
+  for (uint32_t t = blockIdx.x * kHDecWaves + wave; t < a.n_tiles; t += a.waves) {
+    // the tile's words, clamped to the stream so a corrupt woff stays in bounds
+    const uint32_t w0 = min(a.woff[t], a.stream_words);
+    const uint32_t w1 = min(max(a.woff[t + 1], w0), a.stream_words);
+    const uint32_t nw = min(w1 - w0, kHMaxWords);
+    const u32x4 rv = load_nt(reinterpret_cast<const u32x4*>(a.raw + (size_t)t * kTile) + lane);
+    for (uint32_t i = (uint32_t)lane; i < nw + 2; i += kWave) W[i] = i < nw ? a.bits[w0 + i] : 0u;
+    reinterpret_cast<u32x4*>(C)[lane] = u32x4{0, 0, 0, 0};
+    uint32_t first, n_esc_t;
+    tile_escape_range(a.idx, t, a.n_esc, first, n_esc_t);
+    wave_lds_sync();
+
+    // lane windows of `win` bits; speculative starts, then repair
+    const uint32_t nbits = 32 * nw, win = (nbits + 63) >> 6;
+    const uint32_t lo = min((uint32_t)lane * win, nbits), hi = min(lo + win, nbits);
+    uint32_t s = lo, e, cnt;
+    hrun(W, table, symtab, s, hi, e, cnt);
+    for (int round = 0; round < kWave; round++) {
+      uint32_t ns = (uint32_t)__shfl_up((int)e, 1, kWave);
+      if (lane == 0) ns = 0;
+      const bool moved = ns != s;
+      if (__builtin_amdgcn_ballot_w64(moved) == 0) break;
+      if (moved) {
+        s = ns;
+        hrun(W, table, symtab, s, hi, e, cnt);
+      }
+    }
+    // first weight index of the lane's codes: exclusive prefix of the counts (< 256)
+    uint32_t k = 0;
+#pragma unroll
+    for (int b = 0; b < 8; b++) k += ballot_rank(__builtin_amdgcn_ballot_w64((cnt >> b) & 1u)) << b;
+    const uint64_t tile0 = (uint64_t)t * kTile;
+    const uint32_t n_real = (uint32_t)min<uint64_t>(kTile, a.n - tile0);
+    for (uint32_t pos = s; pos < hi; k++) {
+      const uint32_t d = hdec(W, table, symtab, pos);
+      if (k < n_real) C[k] = (uint8_t)(d >> 4);
+      pos += d & 15u;
+    }
+    wave_lds_sync();
+
+    // format v1's decode from here: codes -> exponents, escapes, raw bytes
+    const u32x4 c4 = reinterpret_cast<const u32x4*>(C)[lane];
+    const u32x2 nib = u32x2{c4.x | (c4.y << 4), c4.z | (c4.w << 4)};
+    uint32_t E[4];
+    exponents16<CONTIG>(nib, a.lut, a.base4, E);
+    if (n_esc_t) place_escapes(nib, a.esc, first, n_esc_t, esc_lds[wave], E);
+    uint32_t w[8];
+    assemble16(rv, E, w);
+    const uint64_t e0 = tile0 + (uint64_t)lane * 16;
+    if (e0 + 16 <= a.n) {
+      u32x4* o = reinterpret_cast<u32x4*>(a.out + e0);
+      __builtin_nontemporal_store((u32x4){w[0], w[1], w[2], w[3]}, o);
+      __builtin_nontemporal_store((u32x4){w[4], w[5], w[6], w[7]}, o + 1);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; i++)
+        if (e0 + i < a.n) a.out[e0 + i] = (uint16_t)(w[i >> 1] >> (16 * (i & 1)));
+    }
+    wave_lds_sync();  // the words and codes are rewritten for the next tile
+  }
+}
+
+// ---- host side ---------------------------------------------------------------------
+
+// Huffman code lengths (see include/lbf.h for the procedure and its tie rule).
+// Leaves, then merged nodes, live in one array; each merge records its two
+// children, and lengths are the depths found walking down from the root.
+void huffman_lengths(const uint64_t count[16], uint8_t len[16]) {
+  std::fill(len, len + 16, (uint8_t)0);
+  std::vector<int> sym;
+  for (int s = 0; s < 16; s++)
+    if (count[s]) sym.push_back(s);
+  std::stable_sort(sym.begin(), sym.end(), [&](int a, int b) { return count[a] < count[b]; });
+  const int m = (int)sym.size();
+  if (m == 0) return;
+  if (m == 1) {
+    len[sym[0]] = 1;
+    return;
+  }
+  struct Node {
+    uint64_t weight;
+    int child[2];  // -1 for a leaf
+  };
+  std::vector<Node> node;
+  for (int s : sym) node.push_back(Node{count[s], {-1, -1}});
+  size_t leaf = 0, merged = (size_t)m;  // fronts of the two queues
+  while (node.size() < (size_t)(2 * m - 1)) {
+    int take[2];
+    for (int k = 0; k < 2; k++) {
+      const bool use_leaf = leaf < (size_t)m && (merged >= node.size() || node[leaf].weight <= node[merged].weight);
+      take[k] = (int)(use_leaf ? leaf++ : merged++);
+    }
+    node.push_back(Node{node[take[0]].weight + node[take[1]].weight, {take[0], take[1]}});
+  }
+  std::vector<std::pair<int, int>> stack{{(int)node.size() - 1, 0}};
+  while (!stack.empty()) {
+    const auto [id, depth] = stack.back();
+    stack.pop_back();
+    if (node[id].child[0] < 0) {
+      len[sym[id]] = (uint8_t)depth;
+    } else {
+      stack.push_back({node[id].child[0], depth + 1});
+      stack.push_back({node[id].child[1], depth + 1});
+    }
+  }
+}
+
+// Canonical codes, reversed for the least-significant-bit-first stream:
+// symbols in (length, symbol) order take consecutive values, the value
+// doubling (shifting left) whenever the length grows.
+HCode hcode_of(const uint8_t len[16]) {
+  HCode h{};
+  std::vector<int> order;
+  for (int s = 0; s < 16; s++)
+    if (len[s]) order.push_back(s);
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return len[a] < len[b]; });
+  uint32_t code = 0, prev = 0;
+  for (int s : order) {
+    code <<= (len[s] - prev);
+    prev = len[s];
+    uint32_t rev = 0;
+    for (uint32_t b = 0; b < len[s]; b++) rev |= ((code >> b) & 1u) << (len[s] - 1 - b);
+    h.sym[s] = rev << 4 | len[s];
+    code++;
+  }
+  return h;
+}
+
+HLayout hlayout_of(uint64_t rows, uint64_t cols, uint64_t n_esc, uint64_t stream_words) {
+  auto up = [](uint64_t v) { return (v + 255) & ~uint64_t(255); };
+  HLayout L;
+  L.n = rows * cols;
+  L.n_tiles = (L.n + LBF_TILE - 1) / LBF_TILE;
+  L.n_esc = n_esc;
+  L.stream_words = stream_words;
+  L.off_raw = LBF_HEADER_BYTES;
+  L.off_bits = up(L.off_raw + L.n_tiles * LBF_TILE);
+  L.off_woff = up(L.off_bits + 4 * stream_words);
+  L.off_idx = up(L.off_woff + 4 * (L.n_tiles + 1));
+  L.off_esc = up(L.off_idx + 4 * (L.n_tiles + 1));
+  L.blob_bytes = up(L.off_esc + n_esc);
+  return L;
+}
+
+static void pack_lengths(const uint8_t len[16], uint32_t& lo, uint32_t& hi) {
+  lo = hi = 0;
+  for (int c = 0; c < 8; c++) {
+    lo |= (uint32_t)len[c] << (4 * c);
+    hi |= (uint32_t)len[8 + c] << (4 * c);
+  }
+}
+
+hipError_t launch_hcount(const lbf_desc& d, const uint8_t* blob, uint32_t* counts, hipStream_t s) {
+  const Layout L = layout_of(d.rows, d.cols, d.n_esc);
+  hipLaunchKernelGGL(k_hzero, dim3(1), dim3(64), 0, s, counts, 16u);
+  if (L.n_tiles) {
+    const uint64_t groups = L.n_tiles * kWave;
+    const unsigned grid = (unsigned)std::min<uint64_t>(4096, (groups + kHWaves * kWave - 1) / (kHWaves * kWave));
+    hipLaunchKernelGGL(k_hcount, dim3(grid), dim3(kHWaves * kWave), 0, s, blob + L.off_nib, L.n, L.n_tiles, counts);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_hwoff(const lbf_desc& d, const uint8_t* blob, const uint8_t len[16], uint32_t* words,
+                        uint32_t* woff, hipStream_t s) {
+  const Layout L = layout_of(d.rows, d.cols, d.n_esc);
+  uint32_t lo, hi;
+  pack_lengths(len, lo, hi);
+  if (L.n_tiles) {
+    const unsigned grid = (unsigned)((L.n_tiles + kHWaves - 1) / kHWaves);
+    hipLaunchKernelGGL(k_htile_words, dim3(grid), dim3(kHWaves * kWave), 0, s, blob + L.off_nib, L.n, L.n_tiles, lo,
+                       hi, words);
+  }
+  hipLaunchKernelGGL(k_hscan, dim3(1), dim3(1024), 0, s, words, L.n_tiles, woff);
+  return hipGetLastError();
+}
+
+hipError_t launch_hpack(const lbf_desc& d, const uint8_t* blob, const HCode& code, const uint32_t* woff,
+                        uint32_t* bits, uint64_t stream_words, hipStream_t s) {
+  const Layout L = layout_of(d.rows, d.cols, d.n_esc);
+  if (!L.n_tiles) return hipSuccess;
+  HPackArgs a;
+  a.nib = blob + L.off_nib;
+  a.woff = woff;
+  a.bits = bits;
+  a.n = L.n;
+  a.n_tiles = L.n_tiles;
+  a.stream_words = stream_words;
+  for (int c = 0; c < 16; c++) a.sym[c] = code.sym[c];
+  const unsigned grid = (unsigned)((L.n_tiles + kHWaves - 1) / kHWaves);
+  hipLaunchKernelGGL(k_hpack, dim3(grid), dim3(kHWaves * kWave), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_hdecode(const lbf_hdesc& h, const HCode& code, const uint8_t* blob, uint16_t* out, hipStream_t s) {
+  const HLayout L = hlayout_of(h.rows, h.cols, h.n_esc, h.stream_words);
+  if (!L.n_tiles) return hipSuccess;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hipErrorUnknown;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return hipErrorUnknown;
+  const KLut k = klut_from(h.lut, h.n_codes);
+  HDecArgs a;
+  a.raw = blob + L.off_raw;
+  a.bits = reinterpret_cast<const uint32_t*>(blob + L.off_bits);
+  a.woff = reinterpret_cast<const uint32_t*>(blob + L.off_woff);
+  a.idx = reinterpret_cast<const uint32_t*>(blob + L.off_idx);
+  a.esc = blob + L.off_esc;
+  a.out = out;
+  a.n = (uint32_t)L.n;
+  a.n_tiles = (uint32_t)L.n_tiles;
+  a.n_esc = (uint32_t)L.n_esc;
+  a.stream_words = (uint32_t)L.stream_words;
+  a.lut = Lut{k.t[0], k.t[1], k.t[2], k.t[3]};
+  a.base4 = k.base4;
+  for (int c = 0; c < 16; c++) a.sym[c] = code.sym[c];
+  const uint64_t blocks = std::min<uint64_t>((L.n_tiles + kHDecWaves - 1) / kHDecWaves, (uint64_t)std::max(cus, 1) * 4);
+  a.waves = (uint32_t)(blocks * kHDecWaves);
+  if (k.contiguous)
+    hipLaunchKernelGGL(k_hdecode<true>, dim3((unsigned)blocks), dim3(kHDecWaves * kWave), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_hdecode<false>, dim3((unsigned)blocks), dim3(kHDecWaves * kWave), 0, s, a);
+  return hipGetLastError();
+}
+
+// The header (128 descriptor bytes, then zeros) and every gap the format pads.
+struct HFillArgs {
+  uint8_t* blob;
+  uint32_t head[32];
+  uint64_t gap_at[4], gap_len[4];
+};
+
+__global__ __launch_bounds__(256) void k_hfill(HFillArgs a) {
+  const uint64_t tid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  if (tid < LBF_HEADER_BYTES / 4)
+    reinterpret_cast<uint32_t*>(a.blob)[tid] = tid < 32 ? a.head[tid] : 0u;
+  for (int g = 0; g < 4; g++)
+    for (uint64_t i = tid; i < a.gap_len[g]; i += stride) a.blob[a.gap_at[g] + i] = 0;
+}
+
+hipError_t launch_hfill(const lbf_hdesc& h, uint8_t* blob, hipStream_t s) {
+  const HLayout L = hlayout_of(h.rows, h.cols, h.n_esc, h.stream_words);
+  HFillArgs a;
+  a.blob = blob;
+  std::memcpy(a.head, &h, sizeof a.head);
+  a.gap_at[0] = L.off_bits + 4 * L.stream_words;
+  a.gap_len[0] = L.off_woff - a.gap_at[0];
+  a.gap_at[1] = L.off_woff + 4 * (L.n_tiles + 1);
+  a.gap_len[1] = L.off_idx - a.gap_at[1];
+  a.gap_at[2] = L.off_idx + 4 * (L.n_tiles + 1);
+  a.gap_len[2] = L.off_esc - a.gap_at[2];
+  a.gap_at[3] = L.off_esc + L.n_esc;
+  a.gap_len[3] = L.blob_bytes - a.gap_at[3];
+  hipLaunchKernelGGL(k_hfill, dim3(1), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace lbf

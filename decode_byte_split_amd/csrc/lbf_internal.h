@@ -23,6 +23,7 @@ struct KLut {
   int contiguous;  // lut[c] == lut[0] + c for every c < n_codes
 };
 KLut klut_of(const lbf_desc& d);
+KLut klut_from(const uint8_t lut[16], int n_codes);
 
 // Launchers (defined next to their kernels).  All enqueue on `s` and return
 // the launch status.
@@ -48,6 +49,25 @@ struct GemvGroup {
 };
 hipError_t launch_gemv(const GemvGroup* groups, int n_groups, int batch, int y_dtype, hipStream_t s);
 hipError_t launch_gemm(const GemvGroup* groups, int n_groups, int batch, int y_dtype, hipStream_t s);
+
+// K15H (entropy-coded variant): layout, code, and launchers (lbf_huff.hip).
+struct HLayout {
+  uint64_t n, n_tiles, n_esc, stream_words;
+  uint64_t off_raw, off_bits, off_woff, off_idx, off_esc, blob_bytes;
+};
+HLayout hlayout_of(uint64_t rows, uint64_t cols, uint64_t n_esc, uint64_t stream_words);
+void huffman_lengths(const uint64_t count[16], uint8_t len[16]);
+struct HCode {
+  uint32_t sym[16];  // code c: its canonical value bit-reversed << 4 | its length (0: unused)
+};
+HCode hcode_of(const uint8_t len[16]);
+hipError_t launch_hcount(const lbf_desc& d, const uint8_t* blob, uint32_t* counts, hipStream_t s);
+hipError_t launch_hwoff(const lbf_desc& d, const uint8_t* blob, const uint8_t len[16], uint32_t* words,
+                        uint32_t* woff, hipStream_t s);
+hipError_t launch_hpack(const lbf_desc& d, const uint8_t* blob, const HCode& code, const uint32_t* woff,
+                        uint32_t* bits, uint64_t stream_words, hipStream_t s);
+hipError_t launch_hfill(const lbf_hdesc& h, uint8_t* blob, hipStream_t s);
+hipError_t launch_hdecode(const lbf_hdesc& h, const HCode& code, const uint8_t* blob, uint16_t* out, hipStream_t s);
 
 // lbf_gemm stages each wave's tile index words (16 rows x cols / 1024 tiles)
 // in LDS; rows longer than this many tiles are not supported.

@@ -65,6 +65,43 @@ class Desc(ctypes.Structure):
 assert ctypes.sizeof(Desc) == 96
 
 
+class HDesc(ctypes.Structure):
+    """Mirror of ``lbf_hdesc`` (128 bytes, the first bytes of every K15H blob)."""
+
+    _fields_ = [
+        ("magic", ctypes.c_uint32),
+        ("version", ctypes.c_uint16),
+        ("tile_log2", ctypes.c_uint16),
+        ("rows", ctypes.c_uint64),
+        ("cols", ctypes.c_uint64),
+        ("n_esc", ctypes.c_uint64),
+        ("off_raw", ctypes.c_uint64),
+        ("off_bits", ctypes.c_uint64),
+        ("off_woff", ctypes.c_uint64),
+        ("off_idx", ctypes.c_uint64),
+        ("off_esc", ctypes.c_uint64),
+        ("blob_bytes", ctypes.c_uint64),
+        ("stream_words", ctypes.c_uint64),
+        ("lut", ctypes.c_uint8 * 16),
+        ("n_codes", ctypes.c_uint8),
+        ("max_len", ctypes.c_uint8),
+        ("reserved", ctypes.c_uint8 * 2),
+        ("len", ctypes.c_uint8 * 16),
+        ("desc_crc", ctypes.c_uint32),
+    ]
+
+    def to_bytes(self) -> bytes:
+        return ctypes.string_at(ctypes.addressof(self), ctypes.sizeof(self))
+
+    @classmethod
+    def from_bytes(cls, b) -> "HDesc":
+        b = bytes(b)[:ctypes.sizeof(cls)]
+        return cls.from_buffer_copy(b)
+
+
+assert ctypes.sizeof(HDesc) == 128
+
+
 class LbfError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -98,6 +135,15 @@ def lib():
         L.lbf_verify.argtypes = [dp, vp, vp, vp]
         L.lbf_crc32.restype = i32
         L.lbf_crc32.argtypes = [vp, u64, vp, vp]
+        hp = ctypes.POINTER(HDesc)
+        L.lbf_hdesc_check.restype = i32
+        L.lbf_hdesc_check.argtypes = [hp]
+        L.lbf_hencode_work_bytes.restype = u64
+        L.lbf_hencode_work_bytes.argtypes = [dp]
+        L.lbf_hencode.restype = i32
+        L.lbf_hencode.argtypes = [dp, vp, vp, u64, vp, u64, hp, vp]
+        L.lbf_hdecode.restype = i32
+        L.lbf_hdecode.argtypes = [hp, vp, vp, vp]
         for name in ("lbf_gemv", "lbf_gemm"):
             f = getattr(L, name)
             f.restype = i32
@@ -107,7 +153,8 @@ def lib():
 
 
 EXPORTS = ("lbf_strerror", "lbf_encode_work_bytes", "lbf_desc_check", "lbf_encode", "lbf_decode", "lbf_verify",
-           "lbf_crc32", "lbf_gemv", "lbf_gemm")
+           "lbf_crc32", "lbf_gemv", "lbf_gemm", "lbf_hdesc_check", "lbf_hencode_work_bytes", "lbf_hencode",
+           "lbf_hdecode")
 
 
 def strerror(status: int) -> str:
@@ -201,6 +248,73 @@ def decode(blob: Blob, out=None, stream=None):
     if out is None:
         out = torch.empty((blob.rows, blob.cols), dtype=torch.bfloat16, device=blob.data.device)
     _check(lib().lbf_decode(ctypes.byref(blob.desc), _ptr(blob.data), _ptr(out), _stream(stream)), "lbf_decode")
+    return out
+
+
+@dataclass
+class HBlob:
+    """An entropy-coded (K15H) weight tensor: host descriptor + device blob."""
+
+    desc: HDesc
+    data: "object"  # torch.Tensor, uint8, on the GPU
+
+    @property
+    def rows(self) -> int:
+        return int(self.desc.rows)
+
+    @property
+    def cols(self) -> int:
+        return int(self.desc.cols)
+
+    @property
+    def n_esc(self) -> int:
+        return int(self.desc.n_esc)
+
+    @property
+    def nbytes(self) -> int:
+        return int(self.desc.blob_bytes)
+
+
+def hdesc_check(d: HDesc) -> int:
+    return int(lib().lbf_hdesc_check(ctypes.byref(d)))
+
+
+def hencode(blob: Blob, stream=None) -> HBlob:
+    """Re-code a format-v1 blob as an entropy-coded K15H blob on the GPU."""
+    torch = _torch()
+    L = lib()
+    s = _stream(stream)
+    wb = int(L.lbf_hencode_work_bytes(ctypes.byref(blob.desc)))
+    if wb == 0:
+        raise LbfError(LBF_E_DESC, "lbf_hencode_work_bytes")
+    work = torch.empty(wb, dtype=torch.uint8, device=blob.data.device)
+    h = HDesc()
+    _check(L.lbf_hencode(ctypes.byref(blob.desc), _ptr(blob.data), _ptr(work), wb, None, 0, ctypes.byref(h), s),
+           "lbf_hencode phase 1")
+    out = torch.empty(int(h.blob_bytes), dtype=torch.uint8, device=blob.data.device)
+    _check(L.lbf_hencode(ctypes.byref(blob.desc), _ptr(blob.data), _ptr(work), wb, _ptr(out), out.numel(),
+                         ctypes.byref(h), s), "lbf_hencode phase 2")
+    if stream is not None:
+        work.record_stream(stream)
+        out.record_stream(stream)
+    return HBlob(h, out)
+
+
+def from_host_hblob(blob_bytes: np.ndarray, device="cuda") -> HBlob:
+    """Wrap a K15H blob produced elsewhere as a device HBlob."""
+    torch = _torch()
+    b = np.ascontiguousarray(blob_bytes, dtype=np.uint8)
+    d = HDesc.from_bytes(b[:128].tobytes())
+    _check(hdesc_check(d), "K15H blob header")
+    return HBlob(d, torch.from_numpy(b.copy()).to(device))
+
+
+def hdecode(blob: HBlob, out=None, stream=None):
+    """Rebuild the exact BF16 tensor from a K15H blob."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty((blob.rows, blob.cols), dtype=torch.bfloat16, device=blob.data.device)
+    _check(lib().lbf_hdecode(ctypes.byref(blob.desc), _ptr(blob.data), _ptr(out), _stream(stream)), "lbf_hdecode")
     return out
 
 

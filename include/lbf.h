@@ -198,6 +198,89 @@ int lbf_verify(const lbf_desc* desc, const void* d_blob, uint32_t* d_flags, hipS
  */
 int lbf_crc32(const void* d_data, uint64_t n, uint32_t* d_crc, hipStream_t s);
 
+/*
+ * ---- K15H: the entropy-coded variant ----------------------------------------
+ * The English page's larger K15 reduction belongs to an entropy-coded form of
+ * the byte split ("Lossless LLM Weight Compression vs 8-bit GGUF", opening
+ * section), and DFloat11 entropy-codes the exponent while sign and mantissa
+ * stay raw ("你的 bf16 模型,有 5 個 bit 是廢的", section 二).  K15H keeps format
+ * v1's symbols (the 4-bit code of every weight: 0..14 for the table's
+ * exponents, 15 for an escape) and codes them with a Huffman code:
+ *  - code lengths from Huffman's procedure over the codes' counts among the
+ *    n real weights, run with two queues (used symbols sorted by count, then
+ *    symbol; merged nodes in creation order; a leaf wins a tie); a lone used
+ *    symbol gets length 1; no length exceeds 15;
+ *  - canonical code values (RFC 1951, section 3.2.2), written most
+ *    significant bit first into a bit stream whose bit k is bit k % 32 of
+ *    32-bit word k / 32;
+ *  - each 1024-weight tile is a stream of whole words (its codes in element
+ *    order, unused bits zero); woff[t] is tile t's first word.
+ * Blob layout (every plane at a multiple of 256; blob_bytes too):
+ *   [0, 256)   header: the 128-byte lbf_hdesc, then zeros
+ *   off_raw    raw plane, exactly format v1's (n_tiles * 1024 bytes)
+ *   off_bits   code stream, stream_words 32-bit words
+ *   off_woff   uint32 woff[n_tiles + 1] (woff[n_tiles] = stream_words)
+ *   off_idx    uint32 idx[n_tiles + 1], format v1's escape index
+ *   off_esc    escape stream, format v1's
+ */
+#define LBF_HMAGIC 0x4846424Cu /* "LBFH" little-endian */
+#define LBF_HVERSION 1
+#define LBF_HMAX_TILE_WORDS 480 /* 1024 codes of at most 15 bits */
+
+/* Host copy of a K15H blob's header; byte-for-byte its first 128 bytes. */
+typedef struct lbf_hdesc {
+  uint32_t magic;      /* LBF_HMAGIC */
+  uint16_t version;    /* LBF_HVERSION */
+  uint16_t tile_log2;  /* LBF_TILE_LOG2 */
+  uint64_t rows, cols, n_esc;
+  uint64_t off_raw, off_bits, off_woff, off_idx, off_esc, blob_bytes;
+  uint64_t stream_words;
+  uint8_t lut[16];     /* as lbf_desc */
+  uint8_t n_codes;     /* as lbf_desc */
+  uint8_t max_len;     /* largest len[] */
+  uint8_t reserved[2]; /* zero */
+  uint8_t len[16];     /* Huffman code length of code c (0: c never occurs) */
+  uint32_t desc_crc;   /* CRC-32 (IEEE) of the 124 bytes before this field */
+} lbf_hdesc;
+
+/* Host-only check of a K15H descriptor: magic, version, CRC, layout, table,
+ * and code lengths (a complete prefix code when two or more codes are used).
+ * Returns LBF_OK or LBF_E_DESC (LBF_E_INVAL for NULL). */
+int lbf_hdesc_check(const lbf_hdesc* hdesc);
+
+/* Bytes of device workspace lbf_hencode needs for the tensor of `desc`
+ * (0 if desc fails lbf_desc_check). */
+uint64_t lbf_hencode_work_bytes(const lbf_desc* desc);
+
+/*
+ * lbf_hencode — re-code a format-v1 blob as a K15H blob (two phases, as
+ * lbf_encode).  The source must be a valid v1 blob (lbf_verify passes): its
+ * codes are read, not checked.
+ *   desc, d_blob  the v1 blob (256-byte aligned) and its descriptor
+ *   d_work        device workspace, 256-byte aligned, at least
+ *                 lbf_hencode_work_bytes(desc) bytes; contents on entry
+ *                 do not matter
+ *   hdesc         host; phase 1 writes it, phase 2 reads it
+ * Phase 1 (d_hblob == NULL): counts the codes and sizes every tile's stream
+ *   on the GPU, builds the code on the host, fills *hdesc.  Waits for the
+ *   stream.
+ * Phase 2 (d_hblob != NULL): writes the whole K15H blob on `s`; hdesc must be
+ *   the unchanged phase-1 result for the same v1 blob; d_hblob 256-byte
+ *   aligned, hblob_cap >= hdesc->blob_bytes (else LBF_E_CAPACITY).
+ */
+int lbf_hencode(const lbf_desc* desc, const void* d_blob, void* d_work, uint64_t work_bytes, void* d_hblob,
+                uint64_t hblob_cap, lbf_hdesc* hdesc, hipStream_t s);
+
+/*
+ * lbf_hdecode — rebuild the exact BF16 tensor from a K15H blob.
+ *   hdesc      host copy of the blob's header (checked with lbf_hdesc_check)
+ *   d_hblob    device, 256-byte aligned, hdesc->blob_bytes long
+ *   d_w_out    device, bf16 [rows, cols], 16-byte aligned; fully overwritten
+ * Bit-exact as lbf_decode.  A corrupt stream or index decodes to wrong
+ * values but never reads or writes outside the blob and the output.
+ */
+int lbf_hdecode(const lbf_hdesc* hdesc, const void* d_hblob, void* d_w_out, hipStream_t s);
+
 #ifdef __cplusplus
 }
 #endif

@@ -132,3 +132,88 @@ def test_calls_validate_before_touching_the_gpu():
     assert L.lbf_crc32(256 + 4, 100, 256, None) == lbf.LBF_E_ALIGN
     assert L.lbf_crc32(None, 100, 256, None) == lbf.LBF_E_INVAL
     assert L.lbf_crc32(256, 100, None, None) == lbf.LBF_E_INVAL
+
+
+# ---- K15H descriptors -----------------------------------------------------------
+
+def _oracle_hdesc(W):
+    lbf = _lbf()
+    blob = O.hencode(W)
+    return lbf.HDesc.from_bytes(blob[:128].tobytes()), blob
+
+
+@pytest.mark.parametrize("case", ["gauss", "ragged", "empty", "patterns", "one_symbol", "outliers"])
+def test_oracle_hheaders_pass_library_check(case):
+    lbf = _lbf()
+    rng = np.random.default_rng(2)
+    W = {"gauss": lambda: synth.gaussian(rng, 64, 1024, 0.02, 0.001, 100.0),
+         "ragged": lambda: synth.gaussian(rng, 3, 5, 0.02, 0.0, 1.0),
+         "empty": lambda: np.zeros((0, 8), dtype=np.uint16),
+         "patterns": lambda: synth.all_patterns(64, 1024),
+         "one_symbol": lambda: np.full((2, 1500), 0x3F80, dtype=np.uint16),
+         "outliers": lambda: synth.gaussian(rng, 16, 1024, 0.02, 0.2, 100.0)}[case]()
+    h, blob = _oracle_hdesc(W)
+    assert lbf.hdesc_check(h) == 0
+    assert h.blob_bytes == blob.size
+    # the library's own code lengths for the oracle's counts are the oracle's
+    d, _ = _oracle_desc(W)
+    assert lbf.lib().lbf_hencode_work_bytes(ctypes.byref(d)) >= 256 + 4 * (2 * ((W.size + 1023) // 1024) + 1)
+
+
+def test_corrupt_hdescriptors_rejected():
+    lbf = _lbf()
+    h, _ = _oracle_hdesc(synth.gaussian(np.random.default_rng(3), 8, 1024, 0.02, 0.001, 100.0))
+    raw = bytearray(h.to_bytes())
+    for off in range(0, 128):
+        bad = bytearray(raw)
+        bad[off] ^= 0x10
+        assert lbf.hdesc_check(lbf.HDesc.from_bytes(bytes(bad))) == lbf.LBF_E_DESC, off
+
+
+def test_self_consistent_but_invalid_hdescriptors_rejected():
+    lbf = _lbf()
+    h, _ = _oracle_hdesc(synth.gaussian(np.random.default_rng(4), 8, 1024, 0.02, 0.001, 100.0))
+
+    def resign(x):
+        x.desc_crc = O.crc32(np.frombuffer(x.to_bytes()[:124], dtype=np.uint8))
+        return x
+
+    def variant(edit):
+        x = lbf.HDesc.from_bytes(h.to_bytes())
+        edit(x)
+        return lbf.hdesc_check(resign(x))
+
+    assert variant(lambda x: None) == 0
+    used = [c for c in range(16) if h.len[c]]
+    assert variant(lambda x: x.len.__setitem__(used[0], x.len[used[0]] + 1)) == lbf.LBF_E_DESC  # Kraft sum < 1
+    assert variant(lambda x: x.len.__setitem__(used[-1], 16)) == lbf.LBF_E_DESC  # longer than 15
+    assert variant(lambda x: setattr(x, "max_len", x.max_len + 1)) == lbf.LBF_E_DESC
+    assert variant(lambda x: x.len.__setitem__(14, 0) if h.n_codes == 15 else x.len.__setitem__(13, 3)) == lbf.LBF_E_DESC
+    assert variant(lambda x: setattr(x, "stream_words", x.stream_words + 64)) == lbf.LBF_E_DESC  # layout moves
+    assert variant(lambda x: setattr(x, "off_bits", x.off_bits + 256)) == lbf.LBF_E_DESC
+    assert variant(lambda x: setattr(x, "stream_words", 480 * 8 + 1)) == lbf.LBF_E_DESC  # more than 480 words/tile
+
+
+def test_hcalls_validate_before_touching_the_gpu():
+    lbf = _lbf()
+    L = lbf.lib()
+    W = synth.gaussian(np.random.default_rng(5), 4, 1024, 0.02, 0.001, 100.0)
+    h, _ = _oracle_hdesc(W)
+    d, _ = _oracle_desc(W)
+    bad = lbf.HDesc.from_bytes(h.to_bytes())
+    bad.rows += 1
+    assert L.lbf_hdecode(ctypes.byref(bad), 256, 256, None) == lbf.LBF_E_DESC
+    assert L.lbf_hdecode(ctypes.byref(h), 256 + 16, 256, None) == lbf.LBF_E_ALIGN
+    assert L.lbf_hdecode(ctypes.byref(h), None, 256, None) == lbf.LBF_E_INVAL
+    wb = L.lbf_hencode_work_bytes(ctypes.byref(d))
+    assert L.lbf_hencode(ctypes.byref(d), 256, 256, wb - 1, None, 0, ctypes.byref(lbf.HDesc()), None) == lbf.LBF_E_CAPACITY
+    assert L.lbf_hencode(ctypes.byref(d), 256 + 8, 256, wb, None, 0, ctypes.byref(lbf.HDesc()), None) == lbf.LBF_E_ALIGN
+    assert L.lbf_hencode(ctypes.byref(d), None, 256, wb, None, 0, ctypes.byref(lbf.HDesc()), None) == lbf.LBF_E_INVAL
+    vbad = lbf.Desc.from_bytes(d.to_bytes())
+    vbad.cols += 1
+    assert L.lbf_hencode(ctypes.byref(vbad), 256, 256, wb, None, 0, ctypes.byref(lbf.HDesc()), None) == lbf.LBF_E_DESC
+    # phase 2 with a K15H descriptor of another tensor
+    other, _ = _oracle_hdesc(synth.gaussian(np.random.default_rng(6), 4, 1024, 0.02, 0.001, 100.0))
+    if bytes(other.len) != bytes(h.len) or bytes(other.lut) != bytes(h.lut):
+        assert L.lbf_hencode(ctypes.byref(d), 256, 256, wb, 256, 1 << 30, ctypes.byref(bad), None) == lbf.LBF_E_DESC
+    assert L.lbf_hencode(ctypes.byref(d), 256, 256, wb, 256, h.blob_bytes - 1, ctypes.byref(h), None) == lbf.LBF_E_CAPACITY
