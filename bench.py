@@ -159,6 +159,9 @@ def main():
                          "above) and print its own line; for profiling")
     ap.add_argument("--model-sweep", action="store_true",
                     help="also code the full 32-layer weight set and time GEMV and decode sweeps over it (minutes)")
+    ap.add_argument("--k15h", action="store_true",
+                    help="time only the entropy-coded (K15H) variant on the layer: sizes against the order-0 bound, "
+                         "re-coding and decode; prints its own line")
     ap.add_argument("--rotate-gb", type=float, default=4.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB elementwise copy first (scale for FETCH_SIZE / WRITE_SIZE counter runs)")
@@ -177,6 +180,8 @@ def main():
 
     if args.gate_batch:
         return gate_batch(args)
+    if args.k15h:
+        return k15h_only(args)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the fused decode-GEMV has no cross-GPU step in this build "
@@ -247,6 +252,7 @@ def main():
 
     if args.extras:
         out["extra"] = extras(torch, lbf, synth, Ws, blobs, rot, copies, args)
+        out["extra"]["k15h_layer"] = k15h(torch, lbf, Ws, blobs)
     if args.model_sweep:
         del rot, calls
         torch.cuda.empty_cache()
@@ -351,6 +357,62 @@ def extras(torch, lbf, synth, Ws, blobs, rot, copies, args):
     del src, dst
     torch.cuda.empty_cache()
     return res
+
+
+def order0_bits(Ws) -> float:
+    """Order-0 entropy of the 16-bit values, bits per weight, pooled per tensor
+    (the lower bound for any code that stores each weight on its own)."""
+    total, n = 0.0, 0
+    for W in Ws:
+        c = np.bincount(W.reshape(-1), minlength=65536).astype(np.float64)
+        p = c[c > 0] / W.size
+        total += -float((p * np.log2(p)).sum()) * W.size
+        n += W.size
+    return total / n
+
+
+def k15h(torch, lbf, Ws, blobs, reps: int = 20):
+    """The entropy-coded variant on the layer: re-code every v1 blob on the
+    GPU, then time the standalone decode of all seven tensors (outputs in HBM)."""
+    t0 = time.time()
+    hb = [lbf.hencode(b) for b in blobs]
+    torch.cuda.synchronize()
+    t_code = time.time() - t0
+    n = sum(W.size for W in Ws)
+    hbytes = sum(h.nbytes for h in hb)
+    vbytes = sum(b.nbytes for b in blobs)
+    hrot = [hb] + [[lbf.HBlob(h.desc, h.data.clone()) for h in hb] for _ in range(3)]
+    outs = [torch.empty((h.rows, h.cols), dtype=torch.bfloat16, device="cuda") for h in hb]
+
+    def dec(i):
+        for h, o in zip(hrot[i % 4], outs):
+            lbf.hdecode(h, out=o)
+
+    ms = time_region(torch, dec, reps, 3)
+    del hrot, outs
+    torch.cuda.empty_cache()
+    h0 = order0_bits(Ws)
+    bits = 8.0 * hbytes / n
+    return {"bytes": hbytes, "bits_per_weight": round(bits, 4), "reduction_vs_bf16": round(1 - bits / 16, 5),
+            "order0_bound_bits": round(h0, 4), "above_bound_bits": round(bits - h0, 4),
+            "v1_bits_per_weight": round(8.0 * vbytes / n, 4),
+            "max_code_len": max(int(h.desc.max_len) for h in hb),
+            "recode_s": round(t_code, 3), "decode_us": round(ms * 1e3, 2),
+            "decode_bf16_equiv_GBs": round(2 * n / (ms * 1e-3) / 1e9, 1),
+            "decode_read_plus_write_GBs": round((hbytes + 2 * n) / (ms * 1e-3) / 1e9, 1)}
+
+
+def k15h_only(args):
+    import torch
+
+    from decode_byte_split_amd import lbf, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    Ws = [synth.layer_tensor(m) for m in range(len(synth.LAYER))]
+    blobs = [lbf.encode(dev(torch, W)) for W in Ws]
+    torch.cuda.synchronize()
+    r = k15h(torch, lbf, Ws, blobs, reps=args.steps)
+    print(json.dumps({"workload": "llama8b_layer_k15h", "tensors": [m[0] for m in synth.LAYER], **r}))
 
 
 def gate_batch(args):

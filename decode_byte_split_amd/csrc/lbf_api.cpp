@@ -117,7 +117,9 @@ static int hcheck(const lbf_hdesc* h) {
   if (crc32(h, offsetof(lbf_hdesc, desc_crc)) != h->desc_crc) return LBF_E_DESC;
   if (!shape_ok(h->rows, h->cols)) return LBF_E_DESC;
   const HLayout L = hlayout_of(h->rows, h->cols, h->n_esc, h->stream_words);
-  if (h->n_esc > L.n || h->stream_words > L.n_tiles * LBF_HMAX_TILE_WORDS) return LBF_E_DESC;
+  // every tile holds at least one code bit, so at least one word
+  if (h->n_esc > L.n || h->stream_words > L.n_tiles * LBF_HMAX_TILE_WORDS || h->stream_words < L.n_tiles)
+    return LBF_E_DESC;
   if (h->off_raw != L.off_raw || h->off_bits != L.off_bits || h->off_woff != L.off_woff ||
       h->off_idx != L.off_idx || h->off_esc != L.off_esc || h->blob_bytes != L.blob_bytes)
     return LBF_E_DESC;

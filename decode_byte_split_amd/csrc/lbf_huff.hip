@@ -45,7 +45,7 @@ constexpr int kHWaves = 4;                               // encode kernels
 constexpr int kHDecWaves = 8;                            // decoder
 constexpr uint32_t kHTableBits = 12;                     // primary decode table
 constexpr uint32_t kHMaxWords = LBF_HMAX_TILE_WORDS;     // words of one tile's stream
-constexpr uint32_t kHWordsLds = kHMaxWords + 2;          // + zero guard words
+constexpr uint32_t kHWordsLds = kHMaxWords + 4;          // + zero guard words
 
 // Code of weight 16 lane + q from the lane's two split-half nibble words.
 __device__ __forceinline__ uint32_t code_at(u32x2 nib, int q) {
@@ -195,43 +195,139 @@ struct HDecArgs {
   const uint8_t* esc;
   uint16_t* out;
   uint32_t n, n_tiles, n_esc, stream_words;
-  uint32_t waves;  // waves in the grid
+  uint32_t esc_last;  // last readable byte of `esc` (clamp for unconditional loads)
+  uint32_t waves;     // waves in the grid
   Lut lut;
   uint32_t base4;
   uint32_t sym[16];  // reversed code << 4 | length
 };
 
-// Symbol << 4 | length of the code at stream bit pos (W: the tile's words).
-__device__ __forceinline__ uint32_t hdec(const uint32_t* W, const uint8_t* table, const uint32_t* symtab,
-                                         uint32_t pos) {
-  const uint32_t i = pos >> 5;
-  const uint32_t v = __builtin_amdgcn_alignbit(W[i + 1], W[i], pos & 31u);
-  uint32_t e = table[v & ((1u << kHTableBits) - 1)];
-  if ((e & 15u) == 0) {  // a code longer than the table: match the next 15 bits
-    e = 1u;              // no match (corrupt stream): symbol 0, one bit, so decoding moves on
-    for (int s = 0; s < 16; s++) {
-      const uint32_t d = symtab[s], L = d & 15u;
-      if (L > kHTableBits && (v & ((1u << L) - 1)) == (d >> 4)) e = ((uint32_t)s << 4) | L;
-    }
+// Decode table entry for the next 12 stream bits: up to four whole codes.
+//   bits 0..3    total length of those codes (0: the first code is longer
+//                than 12 bits and is found by hdec_long instead)
+//   bits 4..14   bit j - 1 set if a code starts at offset j (1 <= j <= 11);
+//                a code always starts at offset 0
+//   bits 16..31  the symbols, 4 bits each, first code lowest
+__device__ __forceinline__ uint32_t entry_len(uint32_t e) { return e & 15u; }
+__device__ __forceinline__ uint32_t entry_starts(uint32_t e) { return 1u | ((e >> 3) & 0xFFEu); }
+
+// The single code longer than the table at the low bits of v (at least 15
+// valid): symbol << 4 | length; no match (a corrupt stream) gives symbol 0
+// and length 1, so decoding always moves on.
+__device__ __forceinline__ uint32_t hdec_long(const uint32_t* symtab, uint32_t v) {
+  uint32_t e = 1u;
+#pragma nounroll
+  for (int s = 0; s < 16; s++) {
+    const uint32_t d = symtab[s], L = d & 15u;
+    if (L > kHTableBits && (v & ((1u << L) - 1)) == (d >> 4)) e = ((uint32_t)s << 4) | L;
   }
   return e;
 }
 
-// Decode the codes that start in [pos, hi): their count and the end of the last.
-__device__ __forceinline__ void hrun(const uint32_t* W, const uint8_t* table, const uint32_t* symtab, uint32_t pos,
-                                     uint32_t hi, uint32_t& end, uint32_t& cnt) {
-  uint32_t c = 0;
-  while (pos < hi) {
-    pos += hdec(W, table, symtab, pos) & 15u;
-    c++;
+// One decode step at the low bits of v: the codes it covers (`starts`, bit j
+// = a code starting j bits on), its length `len`, and its symbols.  Codes
+// starting at or after `room` bits belong to the next lane: they are cut off,
+// and `len` then ends at the first of them.
+struct Step {
+  uint32_t starts, len, syms;
+};
+
+__device__ __forceinline__ Step hstep(const uint32_t* table, const uint32_t* symtab, uint32_t v, uint32_t room) {
+  Step st;
+  const uint32_t e = table[v & ((1u << kHTableBits) - 1)];
+  if (entry_len(e)) {
+    st.len = entry_len(e);
+    st.starts = entry_starts(e);
+    st.syms = e >> 16;
+  } else {
+    const uint32_t d = hdec_long(symtab, v);
+    st.len = d & 15u;
+    st.starts = 1u;
+    st.syms = d >> 4;
   }
-  end = pos;
-  cnt = c;
+  if (st.len > room) {  // room >= 1: the first code is always the lane's
+    const uint32_t rest = (st.starts | (1u << st.len)) >> room;
+    st.starts &= (1u << room) - 1;
+    st.len = room + (uint32_t)__builtin_ctz(rest);
+  }
+  return st;
+}
+
+// The tile's stream bits from a position on, least significant first, in a
+// 64-bit register with at least 32 valid bits; the next word is read from
+// LDS one refill ahead, so a decode step waits only for its table lookup.
+struct BitReader {
+  uint64_t buf;
+  uint32_t have, next, ahead;
+};
+
+__device__ __forceinline__ void br_init(BitReader& r, const uint32_t* W, uint32_t pos) {
+  const uint32_t i = pos >> 5;
+  r.buf = (((uint64_t)W[i + 1] << 32) | W[i]) >> (pos & 31u);
+  r.have = 64 - (pos & 31u);
+  r.next = i + 2;
+  r.ahead = W[min(r.next, kHWordsLds - 1)];
+}
+
+__device__ __forceinline__ void br_skip(BitReader& r, const uint32_t* W, uint32_t L) {
+  r.buf >>= L;
+  r.have -= L;
+  if (r.have < 32) {
+    r.buf |= (uint64_t)r.ahead << r.have;
+    r.have += 32;
+    r.next++;
+    r.ahead = W[min(r.next, kHWordsLds - 1)];
+  }
+}
+
+// What a tile needs from memory, loaded one tile ahead of its decode: the
+// words of its stream (word lane + 64 j in bits[j]), its raw bytes, and the
+// first 64 bytes of its escape slice.  Every load is issued unconditionally
+// from a clamped, in-bounds address (unused results are replaced), so the
+// compiler's in-order load counting stays exact across loop iterations.
+constexpr int kHBitRegs = (kHMaxWords + kWave - 1) / kWave;
+
+struct HTile {
+  uint32_t w0, nw, first, n_esc;  // wave-uniform
+  u32x4 raw;
+  uint32_t bits[kHBitRegs];
+  uint32_t escv;
+};
+
+// Index words of tile t (woff and idx pairs) into lanes 0 and 1.
+__device__ __forceinline__ void htile_index(const HDecArgs& a, uint32_t t, int lane, uint32_t& wv, uint32_t& iv) {
+  const uint32_t j = min(t + (uint32_t)(lane & 1), a.n_tiles);
+  wv = a.woff[j];
+  iv = a.idx[j];
+}
+
+__device__ __forceinline__ void htile_load(const HDecArgs& a, uint32_t t, int lane, uint32_t wv, uint32_t iv,
+                                           HTile& T) {
+  const uint32_t wa = (uint32_t)__builtin_amdgcn_readlane((int)wv, 0);
+  const uint32_t wb = (uint32_t)__builtin_amdgcn_readlane((int)wv, 1);
+  T.w0 = min(wa, a.stream_words);
+  T.nw = min(min(max(wb, T.w0), a.stream_words) - T.w0, kHMaxWords);
+  uint32_t ia = (uint32_t)__builtin_amdgcn_readlane((int)iv, 0);
+  uint32_t ib = (uint32_t)__builtin_amdgcn_readlane((int)iv, 1);
+  ib = min(ib, a.n_esc);  // as tile_escape_range
+  ia = min(ia, ib);
+  T.first = ia;
+  T.n_esc = min(ib - ia, (uint32_t)kTile);
+  const uint32_t tc = min(t, a.n_tiles - 1);
+  T.raw = load_nt(reinterpret_cast<const u32x4*>(a.raw + (size_t)tc * kTile) + lane);
+#pragma unroll
+  for (int j = 0; j < kHBitRegs; j++) {
+    const uint32_t i = (uint32_t)lane + kWave * j;
+    const uint32_t v = a.bits[min(T.w0 + i, a.stream_words - 1)];
+    T.bits[j] = i < T.nw ? v : 0u;
+  }
+  const uint32_t ev = a.esc[min(T.first + (uint32_t)lane, a.esc_last)];
+  T.escv = (uint32_t)lane < T.n_esc ? ev : 0u;
 }
 
 template <bool CONTIG>
 __global__ __launch_bounds__(kHDecWaves * kWave) void k_hdecode(HDecArgs a) {
-  __shared__ uint8_t table[1u << kHTableBits];
+  __shared__ uint32_t table[1u << kHTableBits];
   __shared__ uint32_t symtab[16];
   __shared__ uint32_t words[kHDecWaves][kHWordsLds];
   __shared__ __align__(16) uint8_t codes[kHDecWaves][kTile];
@@ -240,35 +336,83 @@ __global__ __launch_bounds__(kHDecWaves * kWave) void k_hdecode(HDecArgs a) {
   const int lane = lane_id();
   if (threadIdx.x < 16) symtab[threadIdx.x] = a.sym[threadIdx.x];
   __syncthreads();
+  // single-code table first (symbol << 4 | length, 0 for codes over 12 bits),
+  // in the codes buffer, then the multi-code entries by chaining it
+  uint8_t* single = &codes[0][0];
   for (uint32_t i = threadIdx.x; i < (1u << kHTableBits); i += blockDim.x) {
     uint32_t e = 0;
     for (int s = 0; s < 16; s++) {
       const uint32_t d = symtab[s], L = d & 15u;
       if (L && L <= kHTableBits && (i & ((1u << L) - 1)) == (d >> 4)) e = ((uint32_t)s << 4) | L;
     }
-    table[i] = (uint8_t)e;
+    single[i] = (uint8_t)e;
+  }
+  __syncthreads();
+  for (uint32_t i = threadIdx.x; i < (1u << kHTableBits); i += blockDim.x) {
+    uint32_t pos = 0, starts = 0, syms = 0, n = 0;
+    while (n < 4 && pos < kHTableBits) {
+      const uint32_t d = single[i >> pos], L = d & 15u;
+      if (!L || L > kHTableBits - pos) break;  // no whole code left in the 12 bits
+      starts |= 1u << pos;
+      syms |= (d >> 4) << (4 * n);
+      n++;
+      pos += L;
+    }
+    table[i] = n ? (pos | ((starts >> 1) << 4) | (syms << 16)) : 0u;
   }
   __syncthreads();
   uint32_t* W = words[wave];
   uint8_t* C = codes[wave];
+  uint8_t* X = esc_lds[wave];
 
-  for (uint32_t t = blockIdx.x * kHDecWaves + wave; t < a.n_tiles; t += a.waves) {
-    // the tile's words, clamped to the stream so a corrupt woff stays in bounds
-    const uint32_t w0 = min(a.woff[t], a.stream_words);
-    const uint32_t w1 = min(max(a.woff[t + 1], w0), a.stream_words);
-    const uint32_t nw = min(w1 - w0, kHMaxWords);
-    const u32x4 rv = load_nt(reinterpret_cast<const u32x4*>(a.raw + (size_t)t * kTile) + lane);
-    for (uint32_t i = (uint32_t)lane; i < nw + 2; i += kWave) W[i] = i < nw ? a.bits[w0 + i] : 0u;
+  uint32_t t = blockIdx.x * kHDecWaves + wave;
+  if (t >= a.n_tiles) return;
+  // two-deep pipeline: index words two tiles ahead, tile data one tile ahead
+  uint32_t wv, iv, wv_next, iv_next;
+  htile_index(a, t, lane, wv, iv);
+  htile_index(a, t + a.waves, lane, wv_next, iv_next);
+  HTile cur;
+  htile_load(a, t, lane, wv, iv, cur);
+
+  for (; t < a.n_tiles; t += a.waves) {
+    HTile nxt;
+    htile_load(a, t + a.waves, lane, wv_next, iv_next, nxt);
+    uint32_t wv_nn, iv_nn;
+    htile_index(a, t + 2 * a.waves, lane, wv_nn, iv_nn);
+
+#pragma unroll
+    for (int j = 0; j < kHBitRegs; j++) {
+      const uint32_t i = (uint32_t)lane + kWave * j;
+      if (i < kHWordsLds) W[i] = cur.bits[j];  // zeros from nw on: the guard words
+    }
     reinterpret_cast<u32x4*>(C)[lane] = u32x4{0, 0, 0, 0};
-    uint32_t first, n_esc_t;
-    tile_escape_range(a.idx, t, a.n_esc, first, n_esc_t);
+    if ((uint32_t)lane < cur.n_esc) X[lane] = (uint8_t)cur.escv;
+    for (uint32_t p = kWave + (uint32_t)lane; p < cur.n_esc; p += kWave) X[p] = a.esc[cur.first + p];  // rare
     wave_lds_sync();
 
-    // lane windows of `win` bits; speculative starts, then repair
-    const uint32_t nbits = 32 * nw, win = (nbits + 63) >> 6;
+    // lane windows of `win` bits; a first pass from every window's first bit
+    // records the code starts it meets (bit p - lo of `seen`, windows of at
+    // most 64 bits), so a later pass from the true start can stop at the
+    // first recorded start it lands on: from there both passes agree.
+    const uint32_t nbits = 32 * cur.nw, win = (nbits + 63) >> 6;
     const uint32_t lo = min((uint32_t)lane * win, nbits), hi = min(lo + win, nbits);
-    uint32_t s = lo, e, cnt;
-    hrun(W, table, symtab, s, hi, e, cnt);
+    const bool track = win <= 64;
+    uint64_t seen = 0;
+    uint32_t s = lo, e, cnt = 0;
+    {
+      BitReader r;
+      br_init(r, W, lo);
+      uint32_t pos = lo;
+      while (pos < hi) {
+        const Step st = hstep(table, symtab, (uint32_t)r.buf, hi - pos);
+        if (track) seen |= (uint64_t)st.starts << (pos - lo);
+        cnt += (uint32_t)__builtin_popcount(st.starts);
+        br_skip(r, W, st.len);
+        pos += st.len;
+      }
+      e = pos;
+    }
+    const uint32_t first_end = e;
     for (int round = 0; round < kWave; round++) {
       uint32_t ns = (uint32_t)__shfl_up((int)e, 1, kWave);
       if (lane == 0) ns = 0;
@@ -276,7 +420,25 @@ __global__ __launch_bounds__(kHDecWaves * kWave) void k_hdecode(HDecArgs a) {
       if (__builtin_amdgcn_ballot_w64(moved) == 0) break;
       if (moved) {
         s = ns;
-        hrun(W, table, symtab, s, hi, e, cnt);
+        BitReader r;
+        br_init(r, W, s);
+        uint32_t pos = s, c = 0;
+        while (pos < hi) {
+          const Step st = hstep(table, symtab, (uint32_t)r.buf, hi - pos);
+          const uint32_t hit = track ? (uint32_t)(seen >> (pos - lo)) & st.starts : 0u;
+          if (hit) {  // a code start the first pass also met: from there both agree
+            const uint32_t j = (uint32_t)__builtin_ctz(hit);
+            c += (uint32_t)__builtin_popcount(st.starts & ((1u << j) - 1));
+            c += (uint32_t)__builtin_popcountll(seen >> (pos + j - lo));
+            pos = first_end;
+            break;
+          }
+          c += (uint32_t)__builtin_popcount(st.starts);
+          br_skip(r, W, st.len);
+          pos += st.len;
+        }
+        e = pos;
+        cnt = c;
       }
     }
     // first weight index of the lane's codes: exclusive prefix of the counts (< 256)
@@ -285,10 +447,19 @@ __global__ __launch_bounds__(kHDecWaves * kWave) void k_hdecode(HDecArgs a) {
     for (int b = 0; b < 8; b++) k += ballot_rank(__builtin_amdgcn_ballot_w64((cnt >> b) & 1u)) << b;
     const uint64_t tile0 = (uint64_t)t * kTile;
     const uint32_t n_real = (uint32_t)min<uint64_t>(kTile, a.n - tile0);
-    for (uint32_t pos = s; pos < hi; k++) {
-      const uint32_t d = hdec(W, table, symtab, pos);
-      if (k < n_real) C[k] = (uint8_t)(d >> 4);
-      pos += d & 15u;
+    {
+      BitReader r;
+      br_init(r, W, s);
+      for (uint32_t pos = s; pos < hi;) {
+        const Step st = hstep(table, symtab, (uint32_t)r.buf, hi - pos);
+        const uint32_t n = (uint32_t)__builtin_popcount(st.starts);
+#pragma unroll
+        for (uint32_t m = 0; m < 4; m++)
+          if (m < n && k + m < n_real) C[k + m] = (uint8_t)((st.syms >> (4 * m)) & 15u);
+        k += n;
+        br_skip(r, W, st.len);
+        pos += st.len;
+      }
     }
     wave_lds_sync();
 
@@ -297,9 +468,13 @@ __global__ __launch_bounds__(kHDecWaves * kWave) void k_hdecode(HDecArgs a) {
     const u32x2 nib = u32x2{c4.x | (c4.y << 4), c4.z | (c4.w << 4)};
     uint32_t E[4];
     exponents16<CONTIG>(nib, a.lut, a.base4, E);
-    if (n_esc_t) place_escapes(nib, a.esc, first, n_esc_t, esc_lds[wave], E);
+    if (cur.n_esc) {
+      uint64_t m0, m1;
+      const uint32_t j = escape_rank(nib, m0, m1);
+      patch_escapes(X, j, cur.n_esc, m0, m1, E);
+    }
     uint32_t w[8];
-    assemble16(rv, E, w);
+    assemble16(cur.raw, E, w);
     const uint64_t e0 = tile0 + (uint64_t)lane * 16;
     if (e0 + 16 <= a.n) {
       u32x4* o = reinterpret_cast<u32x4*>(a.out + e0);
@@ -310,7 +485,10 @@ __global__ __launch_bounds__(kHDecWaves * kWave) void k_hdecode(HDecArgs a) {
       for (int i = 0; i < 16; i++)
         if (e0 + i < a.n) a.out[e0 + i] = (uint16_t)(w[i >> 1] >> (16 * (i & 1)));
     }
-    wave_lds_sync();  // the words and codes are rewritten for the next tile
+    wave_lds_sync();  // the words, codes and escapes are rewritten for the next tile
+    cur = nxt;
+    wv_next = wv_nn;
+    iv_next = iv_nn;
   }
 }
 
@@ -458,7 +636,9 @@ hipError_t launch_hdecode(const lbf_hdesc& h, const HCode& code, const uint8_t* 
   a.bits = reinterpret_cast<const uint32_t*>(blob + L.off_bits);
   a.woff = reinterpret_cast<const uint32_t*>(blob + L.off_woff);
   a.idx = reinterpret_cast<const uint32_t*>(blob + L.off_idx);
-  a.esc = blob + L.off_esc;
+  // with no escapes the escape plane is empty: point its (unused) loads at the index
+  a.esc = L.n_esc ? blob + L.off_esc : blob + L.off_idx;
+  a.esc_last = L.n_esc ? (uint32_t)(L.n_esc - 1) : 0u;
   a.out = out;
   a.n = (uint32_t)L.n;
   a.n_tiles = (uint32_t)L.n_tiles;
@@ -467,7 +647,14 @@ hipError_t launch_hdecode(const lbf_hdesc& h, const HCode& code, const uint8_t* 
   a.lut = Lut{k.t[0], k.t[1], k.t[2], k.t[3]};
   a.base4 = k.base4;
   for (int c = 0; c < 16; c++) a.sym[c] = code.sym[c];
-  const uint64_t blocks = std::min<uint64_t>((L.n_tiles + kHDecWaves - 1) / kHDecWaves, (uint64_t)std::max(cus, 1) * 4);
+  // a persistent grid: exactly the workgroups that can be resident at once
+  int per_cu = 0;
+  const hipError_t occ =
+      k.contiguous ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_hdecode<true>, kHDecWaves * kWave, 0)
+                   : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_hdecode<false>, kHDecWaves * kWave, 0);
+  if (occ != hipSuccess) return occ;
+  const uint64_t blocks = std::min<uint64_t>((L.n_tiles + kHDecWaves - 1) / kHDecWaves,
+                                             (uint64_t)std::max(cus, 1) * (uint64_t)std::max(per_cu, 1));
   a.waves = (uint32_t)(blocks * kHDecWaves);
   if (k.contiguous)
     hipLaunchKernelGGL(k_hdecode<true>, dim3((unsigned)blocks), dim3(kHDecWaves * kWave), 0, s, a);
