@@ -758,3 +758,20 @@ int lbfo_hdecode(const uint8_t* blob, uint64_t blob_len, uint16_t* out, uint64_t
   }
   return 0;
 }
+
+/* ---- the gated MLP product of the layer ---------------------------------
+ * h[b*rows + r] = silu(g) * u with g = sum_k G[r,k] x[b,k], u = sum_k U[r,k]
+ * x[b,k] (both as lbfo_matvec, float64) and silu(z) = z / (1 + e^-z): the
+ * gate_proj / up_proj pair of the 8B-shaped layer's MLP, whose product feeds
+ * down_proj.  Also returns ag, au (sum |G||x|, sum |U||x|) and g, u for the
+ * error bound.  Reading: the MLP of the 8B-shaped decoder layer is SwiGLU
+ * (the pages name the layer's tensors, not its activation).
+ */
+double lbfo_silu(double z) { return z / (1.0 + exp(-z)); }
+
+void lbfo_swiglu(const uint16_t* G, const uint16_t* U, uint64_t rows, uint64_t cols, const uint16_t* x,
+                 uint64_t batch, double* h, double* g, double* u, double* ag, double* au) {
+  lbfo_matvec(G, rows, cols, x, batch, g, ag);
+  lbfo_matvec(U, rows, cols, x, batch, u, au);
+  for (uint64_t i = 0; i < batch * rows; i++) h[i] = lbfo_silu(g[i]) * u[i];
+}

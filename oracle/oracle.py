@@ -66,6 +66,10 @@ def lib():
         L.lbfo_entropy_exponent.argtypes = [_u16p, _u64]
         L.lbfo_verify.restype = ctypes.c_uint
         L.lbfo_verify.argtypes = [_u8p, _u64, _u8p]
+        L.lbfo_silu.restype = ctypes.c_double
+        L.lbfo_silu.argtypes = [ctypes.c_double]
+        L.lbfo_swiglu.restype = None
+        L.lbfo_swiglu.argtypes = [_u16p, _u16p, _u64, _u64, _u16p, _u64, _f64p, _f64p, _f64p, _f64p, _f64p]
         L.lbfo_huffman_lengths.restype = None
         L.lbfo_huffman_lengths.argtypes = [_u64p, _u8p]
         L.lbfo_canonical_codes.restype = None
@@ -318,3 +322,25 @@ def hdecode(blob: np.ndarray) -> np.ndarray:
     if rc != 0:
         raise ValueError("oracle hdecode failed (%d)" % rc)
     return out
+
+
+# ---- the gated MLP product ---------------------------------------------------
+
+
+def silu(z: float) -> float:
+    return float(lib().lbfo_silu(float(z)))
+
+
+def swiglu(G: np.ndarray, U: np.ndarray, x: np.ndarray):
+    """h[b, r] = silu(G x)[b, r] * (U x)[b, r] in float64; also g, u, and the
+    magnitude sums ag = sum |G||x|, au = sum |U||x| (all [batch, rows])."""
+    G, U, x = _bf16(G), _bf16(U), _bf16(x)
+    if x.ndim == 1:
+        x = x[None, :]
+    R, K = G.shape
+    if U.shape != G.shape or x.shape[1] != K:
+        raise ValueError("gate and up must have one shape, x one column per input")
+    B = x.shape[0]
+    out = [np.zeros((B, R), dtype=np.float64) for _ in range(5)]
+    lib().lbfo_swiglu(_p(G, _u16p), _p(U, _u16p), R, K, _p(x, _u16p), B, *[_p(o, _f64p) for o in out])
+    return tuple(out)  # h, g, u, ag, au

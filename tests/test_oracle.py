@@ -390,3 +390,37 @@ def test_matvec_nonfinite_propagates():
     # include NaNs; every other row is finite
     assert np.isnan(y[0, 7]) and np.isnan(y[0, 15])
     assert np.isfinite(np.delete(y[0], [7, 15])).all()
+
+
+# ---- the gated MLP product (SwiGLU) ------------------------------------------
+
+def test_silu_against_scipy_and_identities():
+    from scipy.special import expit
+
+    z = np.concatenate([np.linspace(-30, 30, 121), [0.0, 1e-8, -1e-8, 700.0, -700.0]])
+    got = np.array([O.silu(v) for v in z])
+    assert np.allclose(got, z * expit(z), rtol=1e-14, atol=1e-300)
+    assert O.silu(0.0) == 0.0
+    # sigma(z) + sigma(-z) = 1, so silu(z) - silu(-z) = z
+    assert np.allclose([O.silu(v) - O.silu(-v) for v in z[:121]], z[:121], rtol=1e-13, atol=1e-13)
+
+
+def test_swiglu_one_hot_and_components():
+    rng = np.random.default_rng(91)
+    G = synth.gaussian(rng, 9, 1024, 0.05, 0.0, 1.0)
+    U = synth.gaussian(rng, 9, 1024, 0.05, 0.0, 1.0)
+    k = 77
+    x = np.zeros((1, 1024), dtype=np.uint16)
+    x[0, k] = 0x3F80  # one-hot 1.0: g and u are column k exactly
+    h, g, u, ag, au = O.swiglu(G, U, x)
+    gk = synth.bf16_to_f32(G[:, k]).astype(np.float64)
+    uk = synth.bf16_to_f32(U[:, k]).astype(np.float64)
+    from scipy.special import expit
+
+    assert np.array_equal(g[0], gk) and np.array_equal(u[0], uk)
+    assert np.allclose(h[0], gk * expit(gk) * uk, rtol=1e-14, atol=0)
+    assert np.array_equal(ag[0], np.abs(gk)) and np.array_equal(au[0], np.abs(uk))
+    # the components agree with the plain product
+    xr = synth.activations(rng, 2, 1024)
+    h2, g2, u2, _, _ = O.swiglu(G, U, xr)
+    assert np.array_equal(g2, O.matvec(G, xr)[0]) and np.array_equal(u2, O.matvec(U, xr)[0])
