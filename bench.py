@@ -159,6 +159,9 @@ def main():
                          "above) and print its own line; for profiling")
     ap.add_argument("--model-sweep", action="store_true",
                     help="also code the full 32-layer weight set and time GEMV and decode sweeps over it (minutes)")
+    ap.add_argument("--layer-step", action="store_true",
+                    help="time only one decode step of the whole layer at batch 1 (QKV grouped, o_proj, gate/up "
+                         "with the SiLU-mul epilogue fused, down_proj on its output) against raw BF16; own line")
     ap.add_argument("--k15h", action="store_true",
                     help="time only the entropy-coded (K15H) variant on the layer: sizes against the order-0 bound, "
                          "re-coding and decode; prints its own line")
@@ -182,6 +185,8 @@ def main():
         return gate_batch(args)
     if args.k15h:
         return k15h_only(args)
+    if args.layer_step:
+        return layer_step_only(args)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the fused decode-GEMV has no cross-GPU step in this build "
@@ -253,6 +258,7 @@ def main():
     if args.extras:
         out["extra"] = extras(torch, lbf, synth, Ws, blobs, rot, copies, args)
         out["extra"]["k15h_layer"] = k15h(torch, lbf, Ws, blobs)
+        out["extra"]["layer_step_b1"] = layer_step(torch, lbf, synth, Ws, blobs)
     if args.model_sweep:
         del rot, calls
         torch.cuda.empty_cache()
@@ -400,6 +406,95 @@ def k15h(torch, lbf, Ws, blobs, reps: int = 20):
             "recode_s": round(t_code, 3), "decode_us": round(ms * 1e3, 2),
             "decode_bf16_equiv_GBs": round(2 * n / (ms * 1e-3) / 1e9, 1),
             "decode_read_plus_write_GBs": round((hbytes + 2 * n) / (ms * 1e-3) / 1e9, 1)}
+
+
+def layer_step(torch, lbf, synth, Ws, blobs, reps: int = 50):
+    """One batch-1 decode step of the 8B-shaped layer, weights only (attention
+    itself is not part of the coded path): q/k/v in one grouped launch on one
+    x, o_proj on its own x, gate/up in one launch with the SiLU-mul epilogue,
+    down_proj on that output (bf16).  Compared with the same step unfused
+    (gate/up as a grouped GEMV, then silu * up in torch) and with raw BF16
+    torch (concatenated QKV and gate/up weights, F.linear)."""
+    F = torch.nn.functional
+    Q, K, V, O_, G, U, D = range(7)
+    copies = 4
+    brot = [blobs] + [[lbf.Blob(b.desc, b.data.clone()) for b in blobs] for _ in range(copies - 1)]
+    x_attn = dev(torch, synth.layer_x(Q))
+    x_o = dev(torch, synth.layer_x(O_))
+    x_mlp = dev(torch, synth.layer_x(G))
+    f32, bf = lbf.LBF_F32, lbf.LBF_BF16
+    qkv_out = [torch.empty((1, blobs[m].rows), dtype=torch.float32, device="cuda") for m in (Q, K, V)]
+    o_out = torch.empty((1, blobs[O_].rows), dtype=torch.float32, device="cuda")
+    h = torch.empty((1, blobs[G].rows), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((1, blobs[D].rows), dtype=torch.float32, device="cuda")
+    gu = [torch.empty((1, blobs[m].rows), dtype=torch.float32, device="cuda") for m in (G, U)]
+    qkv_calls = [lbf.prepare([r[Q], r[K], r[V]], [x_attn] * 3, f32, outs=qkv_out) for r in brot]
+    o_calls = [lbf.prepare([r[O_]], [x_o], f32, outs=[o_out]) for r in brot]
+    d_calls = [lbf.prepare([r[D]], [h], f32, outs=[y]) for r in brot]
+    gu_calls = [lbf.prepare([r[G], r[U]], [x_mlp] * 2, f32, outs=gu) for r in brot]
+
+    def fused(i):
+        r = brot[i % copies]
+        qkv_calls[i % copies]()
+        o_calls[i % copies]()
+        lbf.swiglu(r[G], r[U], x_mlp, bf, out=h)
+        d_calls[i % copies]()
+
+    def unfused(i):
+        qkv_calls[i % copies]()
+        o_calls[i % copies]()
+        gu_calls[i % copies]()
+        torch.mul(F.silu(gu[0]), gu[1], out=gu[0])
+        h.copy_(gu[0])
+        d_calls[i % copies]()
+
+    ms_fused = time_region(torch, fused, reps, 5)
+    ms_unfused = time_region(torch, unfused, reps, 5)
+    ms_swiglu = time_region(torch, lambda i: lbf.swiglu(brot[i % copies][G], brot[i % copies][U], x_mlp, bf, out=h),
+                            reps, 5)
+    del brot, qkv_calls, o_calls, d_calls, gu_calls
+    torch.cuda.empty_cache()
+    # raw BF16: best case for torch, concatenated weights
+    raw = []
+    for _ in range(copies):
+        w = [dev(torch, W) for W in Ws]
+        raw.append((torch.cat([w[Q], w[K], w[V]]), w[O_], torch.cat([w[G], w[U]]), w[D]))
+        del w
+    rows_g = Ws[G].shape[0]
+
+    def torch_step(i):
+        wqkv, wo, wgu, wd = raw[i % copies]
+        F.linear(x_attn, wqkv)
+        F.linear(x_o, wo)
+        t = F.linear(x_mlp, wgu)
+        hh = F.silu(t[:, :rows_g]) * t[:, rows_g:]
+        F.linear(hh, wd)
+
+    ms_torch = time_region(torch, torch_step, reps, 5)
+    del raw
+    torch.cuda.empty_cache()
+    n = sum(W.size for W in Ws)
+    coded = sum(b.nbytes for b in blobs)
+    return {"weights": n, "coded_bytes": coded, "bf16_bytes": 2 * n, "launches_fused": 4,
+            "fused_step_us": round(ms_fused * 1e3, 2), "unfused_step_us": round(ms_unfused * 1e3, 2),
+            "torch_bf16_step_us": round(ms_torch * 1e3, 2),
+            "speedup_vs_bf16": round(ms_torch / ms_fused, 3),
+            "gate_up_swiglu_us": round(ms_swiglu * 1e3, 2),
+            "fused_step_hbm_frac": round(coded / (ms_fused * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "torch_step_hbm_frac": round(2 * n / (ms_torch * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def layer_step_only(args):
+    import torch
+
+    from decode_byte_split_amd import lbf, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    Ws = [synth.layer_tensor(m) for m in range(len(synth.LAYER))]
+    blobs = [lbf.encode(dev(torch, W)) for W in Ws]
+    torch.cuda.synchronize()
+    r = layer_step(torch, lbf, synth, Ws, blobs, reps=args.steps)
+    print(json.dumps({"workload": "llama8b_layer_decode_step_b1", **r}))
 
 
 def k15h_only(args):

@@ -422,6 +422,23 @@ static int product(bool mfma, const lbf_desc* descs, const void* const* d_blobs,
   return LBF_OK;
 }
 
+int lbf_gemv_swiglu(const lbf_desc* gate_desc, const void* d_gate_blob, const lbf_desc* up_desc,
+                    const void* d_up_blob, const void* d_x, int batch, void* d_h, int h_dtype, hipStream_t s) {
+  if (h_dtype != LBF_F32 && h_dtype != LBF_BF16) return LBF_E_INVAL;
+  if (batch < 1 || batch > 8 || !gate_desc || !up_desc) return LBF_E_INVAL;
+  const lbf_desc descs[2] = {*gate_desc, *up_desc};
+  const void* blobs[2] = {d_gate_blob, d_up_blob};
+  const void* xs[2] = {d_x, d_x};
+  void* hs[2] = {d_h, d_h};
+  std::vector<GemvGroup> groups;
+  const int rc = build_groups(descs, blobs, 2, xs, hs, groups);
+  if (rc) return rc;
+  if (gate_desc->rows != up_desc->rows || gate_desc->cols != up_desc->cols) return LBF_E_SHAPE;
+  if ((uint64_t)batch * gate_desc->cols * 2 > kGatedMaxXBytes) return LBF_E_UNSUPPORTED;
+  if (launch_gemv_gated(groups[0], groups[1], batch, d_h, h_dtype, s) != hipSuccess) return LBF_E_HIP;
+  return LBF_OK;
+}
+
 int lbf_gemv(const lbf_desc* descs, const void* const* d_blobs, int n_groups, const void* const* d_x, int batch,
              void* const* d_y, int y_dtype, hipStream_t s) {
   return product(false, descs, d_blobs, n_groups, d_x, batch, d_y, y_dtype, s);

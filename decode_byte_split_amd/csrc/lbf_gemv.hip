@@ -384,6 +384,7 @@ struct RingLaunch {
   uint32_t xsrc_group[LBF_MAX_GROUPS];  // groups whose x arrays are staged (distinct pointers)
   uint32_t n_rows, n_xsrc;
   int n_groups, y_bf16;
+  void* h;  // gated product (g[0] = gate, g[1] = up): h[b, r] = silu(gate) * up
 };
 
 struct Slot {
@@ -403,12 +404,15 @@ __device__ __forceinline__ Planes ptrs_of(const GemvGroup& G) {
   return planes_of(G.blob, (uint64_t)G.rows * (G.cols >> 10));
 }
 
+// Unit q of the launch: a row of one group, or (GATED) row q of the gate
+// tensor followed by row q of the up tensor.
+template <bool GATED>
 __device__ __forceinline__ Pos row_pos(const RingLaunch& L, uint32_t q) {
   Pos p;
   p.valid = q < L.n_rows;
   const uint32_t qq = p.valid ? q : L.n_rows - 1;
   uint32_t g = 0;
-  while (g + 1 < (uint32_t)L.n_groups && L.g[g + 1].cost_begin <= qq) g++;
+  while (!GATED && g + 1 < (uint32_t)L.n_groups && L.g[g + 1].cost_begin <= qq) g++;
   p.g = g;
   p.r = qq - (uint32_t)L.g[g].cost_begin;
   p.T = L.g[g].cols >> 10;
@@ -487,7 +491,9 @@ __device__ __forceinline__ void ring_exponents(u32x2 nib, const GemvGroup& G, ui
   }
 }
 
-template <int B, int W>
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+template <int B, int W, bool GATED>
 __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const uint32_t wave = uniform(threadIdx.x >> 6);
@@ -512,7 +518,7 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
     const uint32_t b = blockIdx.x, per = gridDim.x >> 3;
     const uint32_t cu = (gridDim.x & 7u) ? b : (b & 7u) * per + (b >> 3);
     const uint64_t q = cu + (uint64_t)k * gridDim.x;
-    return row_pos(L, q < L.n_rows ? (uint32_t)q : L.n_rows);
+    return row_pos<GATED>(L, q < L.n_rows ? (uint32_t)q : L.n_rows);
   };
   auto advance = [&](const Pos& p) -> Pos {
     if (p.valid && p.c + kRingChunk < p.T) {
@@ -522,6 +528,13 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
       return n;
     }
     if (!p.valid) return p;
+    if (GATED && p.g == 0) {  // the gate row is done: the same row of the up tensor
+      Pos n = p;
+      n.g = 1;
+      n.c = 0;
+      n.S = min((uint32_t)kRingChunk, p.T);
+      return n;
+    }
     return next_row();
   };
 
@@ -549,8 +562,9 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
   __syncthreads();
 
   float acc[B][2];
+  float gsum[B];  // GATED: the finished gate sums of the current row
 #pragma unroll
-  for (int bb = 0; bb < B; bb++) acc[bb][0] = acc[bb][1] = 0.f;
+  for (int bb = 0; bb < B; bb++) acc[bb][0] = acc[bb][1] = gsum[bb] = 0.f;
 
   // one step: chunk p0 in `cur` is decoded; the next chunk p1 (index in
   // `nx1` already) gets its escapes and planes; the one after, p2, its index
@@ -596,13 +610,27 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
         acc[bb][0] = acc[bb][1] = 0.f;
       }
     }
+    // GATED: the gate row's sums wait in gsum; the up row's end stores
+    // silu(gate) * up into h
+    bool store = row_end;
+    void* out = G.y;
+    if (GATED) {
+      if (row_end && p0.g == 0) {
+#pragma unroll
+        for (int bb = 0; bb < B; bb++) gsum[bb] = v[bb];
+      }
+      store = row_end && p0.g == 1;
+      out = L.h;
+#pragma unroll
+      for (int bb = 0; bb < B; bb++) v[bb] = store ? silu(gsum[bb]) * v[bb] : 0.f;
+    }
 #pragma unroll
     for (int bb = 0; bb < B; bb++) {
       if (L.y_bf16) {
-        const __amdgpu_buffer_rsrc_t yr = make_rsrc(static_cast<uint16_t*>(G.y) + (size_t)bb * G.rows + p0.r, row_end ? 2u : 0u);
+        const __amdgpu_buffer_rsrc_t yr = make_rsrc(static_cast<uint16_t*>(out) + (size_t)bb * G.rows + p0.r, store ? 2u : 0u);
         __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(v[bb]), yr, (uint32_t)lane * 2, 0, 0);
       } else {
-        const __amdgpu_buffer_rsrc_t yr = make_rsrc(static_cast<float*>(G.y) + (size_t)bb * G.rows + p0.r, row_end ? 4u : 0u);
+        const __amdgpu_buffer_rsrc_t yr = make_rsrc(static_cast<float*>(out) + (size_t)bb * G.rows + p0.r, store ? 4u : 0u);
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v[bb]), yr, (uint32_t)lane * 4, 0, 0);
       }
     }
@@ -620,7 +648,7 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
 
 // Batch 1..4: 16 waves a workgroup (4 per SIMD, <= 128 VGPRs each); batch
 // 5..8 needs more registers for x and the sums: 8 waves (2 per SIMD).
-template <int B>
+template <int B, bool GATED = false>
 static hipError_t run_ring_kernel(RingLaunch& L, hipStream_t s) {
   constexpr int W = B <= 4 ? kRingWaves : kRingWaves / 2;
   static std::atomic<int> ready{0};  // attribute set for this instance (per process)
@@ -629,14 +657,41 @@ static hipError_t run_ring_kernel(RingLaunch& L, hipStream_t s) {
   if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return hipErrorUnknown;
   if (!ready.load(std::memory_order_acquire)) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_ring<B, W>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_ring<B, W, GATED>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     ready.store(1, std::memory_order_release);
   }
   const uint32_t grid = (uint32_t)std::min<uint64_t>((uint64_t)cus, L.n_rows);
-  hipLaunchKernelGGL((k_gemv_ring<B, W>), dim3(grid), dim3(W * kWave), lds, s, L);
+  hipLaunchKernelGGL((k_gemv_ring<B, W, GATED>), dim3(grid), dim3(W * kWave), lds, s, L);
   return hipGetLastError();
+}
+
+hipError_t launch_gemv_gated(const GemvGroup& gate, const GemvGroup& up, int batch, void* h, int h_dtype,
+                             hipStream_t s) {
+  static_assert(kGatedMaxXBytes == kRingXMax, "the gated launch stages x in the ring kernel's LDS area");
+  if ((uint64_t)batch * gate.cols * 2 > kRingXMax) return hipErrorInvalidValue;  // x must fit in LDS
+  RingLaunch L;
+  L.g[0] = gate;
+  L.g[1] = up;
+  L.g[0].cost_begin = L.g[1].cost_begin = 0;
+  L.x_off[0] = L.x_off[1] = 0;
+  L.xsrc_group[0] = 0;  // one x for both
+  L.n_xsrc = 1;
+  L.n_rows = gate.rows;
+  L.n_groups = 2;
+  L.y_bf16 = h_dtype == LBF_BF16;
+  L.h = h;
+  switch (batch) {
+    case 1: return run_ring_kernel<1, true>(L, s);
+    case 2: return run_ring_kernel<2, true>(L, s);
+    case 3: return run_ring_kernel<3, true>(L, s);
+    case 4: return run_ring_kernel<4, true>(L, s);
+    case 5: return run_ring_kernel<5, true>(L, s);
+    case 6: return run_ring_kernel<6, true>(L, s);
+    case 7: return run_ring_kernel<7, true>(L, s);
+    default: return run_ring_kernel<8, true>(L, s);
+  }
 }
 
 // Ring path if x of all groups (distinct arrays) fits in LDS.
@@ -675,6 +730,7 @@ static hipError_t launch_ring(const GemvGroup* groups, int n_groups, int batch, 
   L.n_rows = (uint32_t)rows;
   L.n_groups = n_groups;
   L.y_bf16 = y_dtype == LBF_BF16;
+  L.h = nullptr;
   used = true;
   switch (batch) {
     case 1: return run_ring_kernel<1>(L, s);

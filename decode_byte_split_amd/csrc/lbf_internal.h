@@ -49,6 +49,11 @@ struct GemvGroup {
 };
 hipError_t launch_gemv(const GemvGroup* groups, int n_groups, int batch, int y_dtype, hipStream_t s);
 hipError_t launch_gemm(const GemvGroup* groups, int n_groups, int batch, int y_dtype, hipStream_t s);
+// h = silu(gate x) * (up x), one launch; x (batch * cols bf16) must fit the
+// ring kernel's LDS x area.
+constexpr uint64_t kGatedMaxXBytes = 98304;
+hipError_t launch_gemv_gated(const GemvGroup& gate, const GemvGroup& up, int batch, void* h, int h_dtype,
+                             hipStream_t s);
 
 // K15H (entropy-coded variant): layout, code, and launchers (lbf_huff.hip).
 struct HLayout {

@@ -135,6 +135,8 @@ def lib():
         L.lbf_verify.argtypes = [dp, vp, vp, vp]
         L.lbf_crc32.restype = i32
         L.lbf_crc32.argtypes = [vp, u64, vp, vp]
+        L.lbf_gemv_swiglu.restype = i32
+        L.lbf_gemv_swiglu.argtypes = [dp, vp, dp, vp, vp, i32, vp, i32, vp]
         hp = ctypes.POINTER(HDesc)
         L.lbf_hdesc_check.restype = i32
         L.lbf_hdesc_check.argtypes = [hp]
@@ -153,7 +155,7 @@ def lib():
 
 
 EXPORTS = ("lbf_strerror", "lbf_encode_work_bytes", "lbf_desc_check", "lbf_encode", "lbf_decode", "lbf_verify",
-           "lbf_crc32", "lbf_gemv", "lbf_gemm", "lbf_hdesc_check", "lbf_hencode_work_bytes", "lbf_hencode",
+           "lbf_crc32", "lbf_gemv", "lbf_gemm", "lbf_gemv_swiglu", "lbf_hdesc_check", "lbf_hencode_work_bytes", "lbf_hencode",
            "lbf_hdecode")
 
 
@@ -248,6 +250,21 @@ def decode(blob: Blob, out=None, stream=None):
     if out is None:
         out = torch.empty((blob.rows, blob.cols), dtype=torch.bfloat16, device=blob.data.device)
     _check(lib().lbf_decode(ctypes.byref(blob.desc), _ptr(blob.data), _ptr(out), _stream(stream)), "lbf_decode")
+    return out
+
+
+def swiglu(gate: Blob, up: Blob, x, h_dtype: int = LBF_F32, out=None, stream=None):
+    """h = silu(gate x) * (up x) in one launch (x: bf16 [batch, cols], batch 1..8)."""
+    torch = _torch()
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise ValueError("x must be bfloat16 [batch, cols]")
+    x = x.contiguous()
+    batch = int(x.shape[0])
+    if out is None:
+        out = torch.empty((batch, gate.rows), dtype=torch.float32 if h_dtype == LBF_F32 else torch.bfloat16,
+                          device=x.device)
+    _check(lib().lbf_gemv_swiglu(ctypes.byref(gate.desc), _ptr(gate.data), ctypes.byref(up.desc), _ptr(up.data),
+                                 _ptr(x), batch, _ptr(out), h_dtype, _stream(stream)), "lbf_gemv_swiglu")
     return out
 
 

@@ -151,6 +151,28 @@ int lbf_gemv(const lbf_desc* descs, const void* const* d_blobs, int n_groups, co
              int batch, void* const* d_y, int y_dtype, hipStream_t s);
 
 /*
+ * lbf_gemv_swiglu — the gated MLP product of a decoder layer in one launch:
+ *   h[b, r] = silu(g[b, r]) * u[b, r],  g = W_gate x,  u = W_up x,
+ * sums in fp32 as lbf_gemv, silu(z) = z / (1 + e^-z) in fp32.  One wave
+ * decodes gate row r and then up row r, so g and u never leave registers and
+ * the two products and the activation cost one launch and one write of h.
+ * Decoding pays only where it hides under weight traffic and serving is bound
+ * by weight bandwidth ("Verlustfreie LLM-Gewichtskompression vs. 8-bit GGUF",
+ * opening section: a Split12 serving test ran slower than BF16; "Lossless
+ * LLM Weight Compression vs 8-bit GGUF", section "Lossless compression or Q8
+ * GGUF: which should you deploy?"), so the layer's small epilogues are fused.
+ *   gate_desc, d_gate_blob, up_desc, d_up_blob   the two tensors: same
+ *              [rows, cols] (LBF_E_SHAPE otherwise), blobs 256-byte aligned
+ *   d_x        device bf16 [batch, cols], 16-byte aligned; batch 1..8
+ *   d_h        device [batch, rows], 4-byte aligned, element type h_dtype
+ *              (LBF_F32, or LBF_BF16 rounded to nearest even); overwritten
+ * Requires cols % 1024 == 0 (LBF_E_SHAPE) and batch * cols * 2 <= 98304 (x is
+ * staged once in LDS; LBF_E_UNSUPPORTED otherwise).
+ */
+int lbf_gemv_swiglu(const lbf_desc* gate_desc, const void* d_gate_blob, const lbf_desc* up_desc,
+                    const void* d_up_blob, const void* d_x, int batch, void* d_h, int h_dtype, hipStream_t s);
+
+/*
  * lbf_gemm — the same product for batch >= 9, on bf16 MFMA (matrix cores)
  * with fp32 accumulation; the decoded weights go straight into the MFMA
  * operand registers and are never written to memory.  (Same page, section

@@ -217,3 +217,25 @@ def test_hcalls_validate_before_touching_the_gpu():
     if bytes(other.len) != bytes(h.len) or bytes(other.lut) != bytes(h.lut):
         assert L.lbf_hencode(ctypes.byref(d), 256, 256, wb, 256, 1 << 30, ctypes.byref(bad), None) == lbf.LBF_E_DESC
     assert L.lbf_hencode(ctypes.byref(d), 256, 256, wb, 256, h.blob_bytes - 1, ctypes.byref(h), None) == lbf.LBF_E_CAPACITY
+
+
+def test_swiglu_validates_before_touching_the_gpu():
+    lbf = _lbf()
+    L = lbf.lib()
+    d, _ = _oracle_desc(np.zeros((8, 2048), dtype=np.uint16))
+    other, _ = _oracle_desc(np.zeros((8, 3072), dtype=np.uint16))
+    wide, _ = _oracle_desc(np.zeros((1, 65536), dtype=np.uint16))
+    bad = lbf.Desc.from_bytes(d.to_bytes())
+    bad.cols += 1
+    r = ctypes.byref
+    assert L.lbf_gemv_swiglu(r(bad), 256, r(d), 256, 256, 1, 256, 0, None) == lbf.LBF_E_DESC
+    assert L.lbf_gemv_swiglu(r(d), 256, r(other), 256, 256, 1, 256, 0, None) == lbf.LBF_E_SHAPE
+    assert L.lbf_gemv_swiglu(r(d), 256, r(d), 256, 256, 9, 256, 0, None) == lbf.LBF_E_INVAL
+    assert L.lbf_gemv_swiglu(r(d), 256, r(d), 256, 256, 0, 256, 0, None) == lbf.LBF_E_INVAL
+    assert L.lbf_gemv_swiglu(r(d), 256, r(d), 256, 256, 1, 256, 5, None) == lbf.LBF_E_INVAL
+    assert L.lbf_gemv_swiglu(None, 256, r(d), 256, 256, 1, 256, 0, None) == lbf.LBF_E_INVAL
+    assert L.lbf_gemv_swiglu(r(d), 256 + 64, r(d), 256, 256, 1, 256, 0, None) == lbf.LBF_E_ALIGN
+    assert L.lbf_gemv_swiglu(r(d), 256, r(d), 256, 256 + 8, 1, 256, 0, None) == lbf.LBF_E_ALIGN
+    assert L.lbf_gemv_swiglu(r(wide), 256, r(wide), 256, 256, 2, 256, 0, None) == lbf.LBF_E_UNSUPPORTED
+    small, _ = _oracle_desc(np.zeros((3, 5), dtype=np.uint16))
+    assert L.lbf_gemv_swiglu(r(small), 256, r(small), 256, 256, 1, 256, 0, None) == lbf.LBF_E_SHAPE
