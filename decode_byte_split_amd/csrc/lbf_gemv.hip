@@ -10,8 +10,7 @@
 // bottleneck is weight bandwidth), so both kernels here are HBM streams:
 //
 //  * k_gemv_ring (x of every tensor of the call fits in 96 KiB of LDS): one
-//    workgroup per CU (16 waves for batch 1..4, 8 for 5..8), rows dealt to
-//    CUs, waves take
+//    workgroup per CU (16 waves), rows dealt to CUs, waves take
 //    rows from an LDS counter and stream them through a three-slot register
 //    ring (details at the kernel);
 //  * k_gemv (everything else): persistent workgroups, each taking one
@@ -374,7 +373,7 @@ static hipError_t run(GemvLaunch& L, hipStream_t s) {
 // index needs nothing).  Every memory operation is issued unconditionally
 // (a disabled one gets a zero-length buffer range) and the ring is unrolled
 // by three, so the compiler counts outstanding loads exactly.
-constexpr int kRingWaves = 16;  // waves per workgroup for batch 1..4 (4 per SIMD); 8 for batch 5..8
+constexpr int kRingWaves = 16;  // waves per workgroup (4 per SIMD), every batch
 constexpr int kRingChunk = 4;  // tiles per chunk (at most; the last of a row may be shorter)
 constexpr uint32_t kRingXMax = 98304;
 
@@ -580,22 +579,39 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
 #pragma unroll
     for (int j = 0; j < kRingChunk; j++) {
       if ((uint32_t)j < p0.S) {
-        uint32_t xr[B][8];
-#pragma unroll
-        for (int bb = 0; bb < B; bb++) {
+        // batch rows 0..kEarly-1: x read before the decode (hides the LDS
+        // latency); the rest one row at a time after it (fewer live registers)
+        constexpr int kEarly = B <= 4 ? B : 2;
+        auto xload = [&](int bb, uint32_t* xv) {
           const uint8_t* xs = x_g + (size_t)((bb * p0.T + p0.c + j) * 2) * kTile + lane * 16;
           const u32x4 a0 = *reinterpret_cast<const u32x4*>(xs);
           const u32x4 a1 = *reinterpret_cast<const u32x4*>(xs + kTile);
-          xr[bb][0] = a0.x; xr[bb][1] = a0.y; xr[bb][2] = a0.z; xr[bb][3] = a0.w;
-          xr[bb][4] = a1.x; xr[bb][5] = a1.y; xr[bb][6] = a1.z; xr[bb][7] = a1.w;
-        }
+          xv[0] = a0.x; xv[1] = a0.y; xv[2] = a0.z; xv[3] = a0.w;
+          xv[4] = a1.x; xv[5] = a1.y; xv[6] = a1.z; xv[7] = a1.w;
+        };
+        uint32_t xr[kEarly][8];
+#pragma unroll
+        for (int bb = 0; bb < kEarly; bb++) xload(bb, xr[bb]);
         const uint32_t ia = (uint32_t)__builtin_amdgcn_readlane((int)cur.idxv, j);
         const uint32_t ib = (uint32_t)__builtin_amdgcn_readlane((int)cur.idxv, j + 1);
         uint32_t E[4];
         ring_exponents(cur.nib[j], G, ia, ib, cur.escv, f0, n0, P.esc, slot_lds, E);
         uint32_t w[8];
         assemble16(cur.raw[j], E, w);
-        dot16<B>(w, xr, acc);
+#pragma unroll
+        for (int bb = 0; bb < B; bb++) {
+          uint32_t xl[8];
+          if (bb < kEarly) {
+#pragma unroll
+            for (int q = 0; q < 8; q++) xl[q] = xr[bb < kEarly ? bb : 0][q];
+          } else {
+            xload(bb, xl);
+          }
+#pragma unroll
+          for (int q = 0; q < 8; q++)
+            acc[bb][q & 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[q]),
+                                                             __builtin_bit_cast(bf16x2, xl[q]), acc[bb][q & 1], false);
+        }
       }
     }
     // row end: the sums of row p0.r are stored by lane 0 (range 0 otherwise)
@@ -646,11 +662,12 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
     }
 }
 
-// Batch 1..4: 16 waves a workgroup (4 per SIMD, <= 128 VGPRs each); batch
-// 5..8 needs more registers for x and the sums: 8 waves (2 per SIMD).
+// 16 waves a workgroup (4 per SIMD, <= 128 VGPRs each) for every batch:
+// above batch 4 only two batch rows of x are read before a tile's decode and
+// the others one at a time after it, which keeps batch 8 within 128 VGPRs.
 template <int B, bool GATED = false>
 static hipError_t run_ring_kernel(RingLaunch& L, hipStream_t s) {
-  constexpr int W = B <= 4 ? kRingWaves : kRingWaves / 2;
+  constexpr int W = kRingWaves;
   static std::atomic<int> ready{0};  // attribute set for this instance (per process)
   const uint32_t lds = kRingXMax + W * kTile + 16;
   int dev = 0, cus = 0;
