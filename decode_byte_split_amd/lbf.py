@@ -212,6 +212,27 @@ def _check(rc: int, what: str):
         raise LbfError(rc, what)
 
 
+def _check_blob(blob, desc=None):
+    """The device buffer must hold at least the descriptor's blob_bytes (the
+    kernels read that far) and sit on the GPU."""
+    d = blob.desc if desc is None else desc
+    t = blob.data
+    if not t.is_cuda or not t.is_contiguous() or t.numel() * t.element_size() < int(d.blob_bytes):
+        raise ValueError("blob data must be a contiguous GPU buffer of at least %d bytes" % int(d.blob_bytes))
+
+
+def _check_word(t, what: str):
+    if not t.is_cuda or not t.is_contiguous() or t.numel() * t.element_size() < 4:
+        raise ValueError("%s must be a contiguous GPU tensor of at least 4 bytes" % what)
+
+
+def _check_tensor(t, numel: int, dtype, what: str):
+    """The library writes or reads exactly `numel` elements of `dtype` at
+    t.data_ptr(): refuse anything that would let it run past the tensor."""
+    if not t.is_cuda or t.dtype != dtype or not t.is_contiguous() or t.numel() != numel:
+        raise ValueError("%s must be a contiguous %s tensor of %d elements on the GPU" % (what, dtype, numel))
+
+
 def encode(w, stream=None) -> Blob:
     """Code a 2-D BF16 tensor (torch.bfloat16 or int16/uint16 bit patterns on the GPU)."""
     torch = _torch()
@@ -249,6 +270,8 @@ def decode(blob: Blob, out=None, stream=None):
     torch = _torch()
     if out is None:
         out = torch.empty((blob.rows, blob.cols), dtype=torch.bfloat16, device=blob.data.device)
+    _check_blob(blob)
+    _check_tensor(out, blob.rows * blob.cols, torch.bfloat16, "out")
     _check(lib().lbf_decode(ctypes.byref(blob.desc), _ptr(blob.data), _ptr(out), _stream(stream)), "lbf_decode")
     return out
 
@@ -256,13 +279,16 @@ def decode(blob: Blob, out=None, stream=None):
 def swiglu(gate: Blob, up: Blob, x, h_dtype: int = LBF_F32, out=None, stream=None):
     """h = silu(gate x) * (up x) in one launch (x: bf16 [batch, cols], batch 1..8)."""
     torch = _torch()
-    if x.dtype != torch.bfloat16 or x.dim() != 2:
-        raise ValueError("x must be bfloat16 [batch, cols]")
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != gate.cols or not x.is_cuda:
+        raise ValueError("x must be bfloat16 [batch, cols of the weights] on the GPU")
     x = x.contiguous()
     batch = int(x.shape[0])
+    hdt = torch.float32 if h_dtype == LBF_F32 else torch.bfloat16
     if out is None:
-        out = torch.empty((batch, gate.rows), dtype=torch.float32 if h_dtype == LBF_F32 else torch.bfloat16,
-                          device=x.device)
+        out = torch.empty((batch, gate.rows), dtype=hdt, device=x.device)
+    _check_blob(gate)
+    _check_blob(up)
+    _check_tensor(out, batch * gate.rows, hdt, "out")
     _check(lib().lbf_gemv_swiglu(ctypes.byref(gate.desc), _ptr(gate.data), ctypes.byref(up.desc), _ptr(up.data),
                                  _ptr(x), batch, _ptr(out), h_dtype, _stream(stream)), "lbf_gemv_swiglu")
     return out
@@ -301,6 +327,7 @@ def hencode(blob: Blob, stream=None) -> HBlob:
     torch = _torch()
     L = lib()
     s = _stream(stream)
+    _check_blob(blob)
     wb = int(L.lbf_hencode_work_bytes(ctypes.byref(blob.desc)))
     if wb == 0:
         raise LbfError(LBF_E_DESC, "lbf_hencode_work_bytes")
@@ -331,6 +358,8 @@ def hdecode(blob: HBlob, out=None, stream=None):
     torch = _torch()
     if out is None:
         out = torch.empty((blob.rows, blob.cols), dtype=torch.bfloat16, device=blob.data.device)
+    _check_blob(blob)
+    _check_tensor(out, blob.rows * blob.cols, torch.bfloat16, "out")
     _check(lib().lbf_hdecode(ctypes.byref(blob.desc), _ptr(blob.data), _ptr(out), _stream(stream)), "lbf_hdecode")
     return out
 
@@ -343,6 +372,8 @@ def verify_into(blob: Blob, flags, desc: Desc | None = None, stream=None) -> Non
     its own descriptor); the failed-check mask lands in ``flags`` (a one-element
     int32 or uint32 device tensor) when the stream reaches it.  Does not wait."""
     d = blob.desc if desc is None else desc
+    _check_blob(blob, d)
+    _check_word(flags, "flags")
     _check(lib().lbf_verify(ctypes.byref(d), _ptr(blob.data), _ptr(flags), _stream(stream)), "lbf_verify")
 
 
@@ -361,6 +392,7 @@ def crc32_into(t, out, stream=None) -> None:
     (a one-element int32 or uint32 device tensor).  Does not wait."""
     if not t.is_cuda or not t.is_contiguous():
         raise ValueError("crc32 takes a contiguous tensor on the GPU")
+    _check_word(out, "out")
     _check(lib().lbf_crc32(_ptr(t), t.numel() * t.element_size(), _ptr(out), _stream(stream)), "lbf_crc32")
 
 
@@ -385,17 +417,21 @@ class Prepared:
         n = len(blobs)
         if len(xs) != n:
             raise ValueError("one x per blob")
+        for b in blobs:
+            _check_blob(b)
         batch = int(xs[0].shape[0])
         xs = [x.contiguous() for x in xs]
         for x, b in zip(xs, blobs):
-            if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[0] != batch or x.shape[1] != b.cols:
-                raise ValueError("x must be bfloat16 [batch, cols] with the same batch for every group")
+            if (x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[0] != batch or x.shape[1] != b.cols
+                    or not x.is_cuda):
+                raise ValueError("x must be bfloat16 [batch, cols] on the GPU with the same batch for every group")
         tdt = torch.float32 if y_dtype == LBF_F32 else torch.bfloat16
         if outs is None:
             outs = [torch.empty((batch, b.rows), dtype=tdt, device=b.data.device) for b in blobs]
+        if len(outs) != n:
+            raise ValueError("one output per blob")
         for y, b in zip(outs, blobs):
-            if y.dtype != tdt or not y.is_contiguous() or y.numel() != batch * b.rows:
-                raise ValueError("each output must be a contiguous %s tensor of batch * rows elements" % tdt)
+            _check_tensor(y, batch * b.rows, tdt, "each output")
         self._keep = (list(blobs), xs, outs)
         self.outs = outs
         self._fn, self._what = fn, what
