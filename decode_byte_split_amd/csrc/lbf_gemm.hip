@@ -31,9 +31,10 @@
 //  - x is staged per step (256 columns of every batch row) into LDS, padded
 //    so the 16-byte operand reads are conflict-free, double-buffered with one
 //    barrier per step, and loaded two steps ahead through two register sets;
-//    the coded chunks run through a ring of four register slots (three steps
-//    in flight); every load is issued unconditionally (invalid ones go out of
-//    the buffer range and return 0).
+//    the coded chunks run through a ring of four register slots (two steps
+//    in flight, which keeps up to 32 columns at two waves per SIMD); every
+//    load is issued unconditionally (invalid ones go out of the buffer range
+//    and return 0).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -151,14 +152,13 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
     }
   };
 
-  // issue order (loads retire in order): x 2 steps ahead, coded data 3
+  // issue order (loads retire in order): x and coded data 2 steps ahead
   GSlot s0, s1, s2, s3;
   XRegs xa, xb;
   load_x(xa, 0);
   load_step(s0, 0);
   load_x(xb, 1);
   load_step(s1, 1);
-  load_step(s2, 2);
 
   // the row block's index words idx[t_first .. t_first + tiles_here] and
   // escape bytes (staged by its first wave), clamped to the stream so a
@@ -207,13 +207,13 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
         return (uint32_t)esc_l[pos - a0];
     };
 
-    // step k: x of step k + 2 and coded data of step k + 3 are issued, step k
+    // step k: x of step k + 2 and coded data of step k + 2 are issued, step k
     // is computed from slot `cur` and x buffer k % 2, and x of step k + 1
     // (issued a step earlier) goes to x buffer (k + 1) % 2.  A tile starts
     // every 4 steps (TILE_START).
-    auto step = [&](GSlot& cur, GSlot& nx3, XRegs& x_in, const XRegs& x_out, uint32_t k, auto tile_start) {
+    auto step = [&](GSlot& cur, GSlot& nx2, XRegs& x_in, const XRegs& x_out, uint32_t k, auto tile_start) {
       load_x(x_in, k + 2);
-      load_step(nx3, k + 3);
+      load_step(nx2, k + 2);
       if constexpr (decltype(tile_start)::value) {
         const uint32_t c = (k >> 2) * S + kh;
         uint32_t ia = e_lo, ib = e_lo;
@@ -283,10 +283,10 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
 
     // n_steps is a multiple of 4: one iteration is one tile
     for (uint32_t k = 0; k < n_steps; k += 4) {
-      step(s0, s3, xa, xb, k, std::true_type{});
-      step(s1, s0, xb, xa, k + 1, std::false_type{});
-      step(s2, s1, xa, xb, k + 2, std::false_type{});
-      step(s3, s2, xb, xa, k + 3, std::false_type{});
+      step(s0, s2, xa, xb, k, std::true_type{});
+      step(s1, s3, xb, xa, k + 1, std::false_type{});
+      step(s2, s0, xa, xb, k + 2, std::false_type{});
+      step(s3, s1, xb, xa, k + 3, std::false_type{});
     }
   };
   if (dense)
@@ -383,13 +383,15 @@ hipError_t launch_gemm(const GemvGroup* groups, int n_groups, int batch, int y_d
     }
     L.wg_begin[n_groups] = wg;
     L.idx_bytes = (4 * (16 * t_max + 1) + 15) & ~15u;
-    // up to 16 columns, rows of two or more tiles split K over two waves per
-    // row block (8 waves a workgroup, two per SIMD, no register spills)
+    // up to 32 columns, rows of two or more tiles split K over two waves per
+    // row block (8 waves a workgroup, two per SIMD): a gate-sized tensor has
+    // too few 16-row blocks to fill the chip otherwise; with 48 or 64
+    // columns the split would spill registers
     const bool split = t_min >= 2;
     hipError_t e;
     switch ((nb + 15) / 16) {
       case 1: e = split ? run_gemm<1, 2>(L, wg, s) : run_gemm<1, 1>(L, wg, s); break;
-      case 2: e = run_gemm<2, 1>(L, wg, s); break;
+      case 2: e = split ? run_gemm<2, 2>(L, wg, s) : run_gemm<2, 1>(L, wg, s); break;
       case 3: e = run_gemm<3, 1>(L, wg, s); break;
       default: e = run_gemm<4, 1>(L, wg, s); break;
     }
