@@ -79,6 +79,60 @@ def time_region(torch, fn, steps: int, warmup: int) -> float:
     return t0.elapsed_time(t1) / steps
 
 
+def time_each(torch, fn, steps: int, warmup: int):
+    """Per-launch durations (ms): each call between its own pair of HIP
+    events on the launch stream; returns (median, min)."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        fn(warmup + i)
+        b.record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    return t[len(t) // 2], t[0]
+
+
+READ_BYTES = 1 << 30  # the read-stream ceiling runs over 1 GiB
+
+
+def read_ceiling(torch, reps: int = 10) -> float:
+    """GB/s of a plain read stream (liblbf_measure.so: 128-bit non-temporal
+    loads, XOR-reduced) over 1 GiB, the practical ceiling for a kernel that
+    only reads HBM."""
+    import ctypes
+
+    L = ctypes.CDLL(os.path.join(ROOT, "decode_byte_split_amd", "liblbf_measure.so"))
+    L.lbfm_read_stream.restype = ctypes.c_int
+    L.lbfm_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    buf = torch.ones(READ_BYTES // 4, dtype=torch.float32, device="cuda")
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    blocks = torch.cuda.get_device_properties(0).multi_processor_count  # one workgroup per CU
+    s = torch.cuda.current_stream().cuda_stream
+
+    def run(i):
+        rc = L.lbfm_read_stream(buf.data_ptr(), READ_BYTES, out.data_ptr(), blocks, s)
+        assert rc == 0, "read-stream kernel failed (%d)" % rc
+
+    ms = time_region(torch, run, reps, 3)
+    del buf, out
+    torch.cuda.empty_cache()
+    return READ_BYTES / (ms * 1e-3) / 1e9
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 COPY_ELEMS = 1 << 28  # float32 elements of the calibration copy: 1 GiB read, 1 GiB written
 
 
@@ -142,7 +196,8 @@ def cpu_baseline(Ws, xs, min_seconds: float):
     gbs = 2.0 * n * passes / t / 1e9
     return {"value": gbs, "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": "full 8B-shaped layer (7 tensors, %d weights) x %d pass(es): oracle decode of each "
-                      "oracle-coded blob + float64 matvec at batch 1, %.1f s" % (n, passes, t)}
+                      "oracle-coded blob + float64 matvec at batch 1, %.1f s" % (n, passes, t),
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
 
 
 def main():
@@ -220,11 +275,22 @@ def main():
     calls = [lbf.prepare(r, xd, lbf.LBF_F32, outs=ys) for r in rot]
     step = lambda i: calls[i % copies]()
     ms_step = time_region(torch, step, args.steps, args.warmup)
+    ms_median, ms_min = time_each(torch, step, max(args.steps // 2, 10), 3)
     alg = sum(algorithmic_bytes(b, 1, 4) for b in blobs)
     achieved = alg / (ms_step * 1e-3) / 1e9
     value = 2.0 * n_weights / (ms_step * 1e-3) / 1e9
     log("launch mean %.2f us: %.1f GB/s BF16-equiv, %.1f GB/s algorithmic (%.1f %% of 8 TB/s)"
         % (ms_step * 1e3, value, achieved, 100 * achieved / HBM_PEAK_GBS))
+
+    # side lanes, same run: the read-stream ceiling, and the uncompressed
+    # layer through torch's F.linear (four rotating BF16 copies)
+    ceiling = read_ceiling(torch)
+    wrot = [[dev(torch, W) for W in Ws] for _ in range(4)]
+    raw_ms = time_region(torch, lambda i: [torch.nn.functional.linear(x, w) for x, w in zip(xd, wrot[i % 4])],
+                         20, 3)
+    del wrot
+    torch.cuda.empty_cache()
+    log("read-stream ceiling %.1f GB/s; raw BF16 F.linear layer %.2f us" % (ceiling, raw_ms * 1e3))
 
     traffic = None
     if os.path.exists(COUNTERS):
@@ -252,7 +318,12 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": KERNEL, "algorithmic_bytes_per_launch": alg,
-                     "launch_ms_mean": round(ms_step, 5)},
+                     "launch_ms_mean": round(ms_step, 5), "launch_ms_median": round(ms_median, 5),
+                     "launch_ms_min": round(ms_min, 5), "read_stream_ceiling": round(ceiling, 1),
+                     "frac_of_read_stream_ceiling": round(achieved / ceiling, 4)},
+        "side_lanes": {"raw_bf16_linear_layer_us": round(raw_ms * 1e3, 2),
+                       "speedup_vs_raw_bf16": round(raw_ms / ms_step, 3),
+                       "read_stream_ceiling_GBs": round(ceiling, 1)},
     }
 
     if args.extras:
