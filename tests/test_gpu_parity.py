@@ -271,3 +271,25 @@ def test_gemv_many_groups_mixed_shapes(env):
     for W, x, y in zip(Ws, xs, ys):
         y_ref, a_ref = O.matvec(W, x)
         check_product(y, y_ref, a_ref, False)
+
+
+@pytest.mark.parametrize("batch", [1, 2])
+def test_gemv_tiny_groups_share_x(env, batch):
+    """31 one-row tensors sharing one x tensor, then a 300 x 30720 tensor, in
+    one grouped call: outputs of tensors that share an x and of a tensor with
+    a 60 KB (batch 1) or 120 KB (batch 2) x all match the oracle."""
+    torch, lbf = env
+    rng = np.random.default_rng([9, batch])
+    Ws = [synth.gaussian(rng, 1, 1024, 0.02, 0.01, 100.0) for _ in range(31)]
+    Ws.append(synth.gaussian(rng, 300, 30720, 0.02, 0.002, 100.0))
+    xs_small = dev(torch, synth.activations(rng, batch, 1024))
+    x_big = synth.activations(rng, batch, 30720)
+    blobs = [lbf.from_host_blob(O.encode(W)) for W in Ws]
+    ys = lbf.gemv(blobs, [xs_small] * 31 + [dev(torch, x_big)], lbf.LBF_F32)
+    torch.cuda.synchronize()
+    x_small = host(xs_small)
+    for W, y in zip(Ws[:31], ys[:31]):
+        y_ref, a_ref = O.matvec(W, x_small)
+        check_product(y, y_ref, a_ref, False)
+    y_ref, a_ref = O.matvec(Ws[31], x_big)
+    check_product(ys[31], y_ref, a_ref, False)
