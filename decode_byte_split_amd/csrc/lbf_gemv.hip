@@ -374,7 +374,12 @@ static hipError_t run(GemvLaunch& L, hipStream_t s) {
 // (a disabled one gets a zero-length buffer range) and the ring is unrolled
 // by three, so the compiler counts outstanding loads exactly.
 constexpr int kRingWaves = 16;  // waves per workgroup (4 per SIMD), every batch
-constexpr int kRingChunk = 4;  // tiles per chunk (at most; the last of a row may be shorter)
+// Ring geometry: tiles a chunk (the last of a row may be shorter) and chunks
+// in the ring (N - 2 have their planes in flight while one is decoded).  Two
+// tiles with four or five slots, or one tile with eight, measured slower:
+// the per-chunk scalar work grows faster than the extra loads in flight help.
+constexpr int kRingTiles = 4;
+constexpr int kRingSlots = 3;
 constexpr uint32_t kRingXMax = 98304;
 
 struct RingLaunch {
@@ -386,9 +391,10 @@ struct RingLaunch {
   void* h;  // gated product (g[0] = gate, g[1] = up): h[b, r] = silu(gate) * up
 };
 
+template <int C>
 struct Slot {
-  u32x4 raw[kRingChunk];
-  u32x2 nib[kRingChunk];
+  u32x4 raw[C];
+  u32x2 nib[C];
   uint32_t idxv;  // lane j: idx[t0 + j], j <= S
   uint32_t escv;  // lane p: escape p of the chunk's slice, p < 64
 };
@@ -403,33 +409,50 @@ __device__ __forceinline__ Planes ptrs_of(const GemvGroup& G) {
   return planes_of(G.blob, (uint64_t)G.rows * (G.cols >> 10));
 }
 
+// Group table in two VGPRs, lane g for group g (loaded once per kernel):
+// first global row (all ones past the last group) and tiles per row.
+struct GroupRegs {
+  uint32_t first_row, tiles;
+};
+
+__device__ __forceinline__ GroupRegs group_regs(const RingLaunch& L, int lane) {
+  GroupRegs v;
+  const bool in = lane < L.n_groups;
+  const GemvGroup& G = L.g[in ? lane : 0];
+  v.first_row = in ? (uint32_t)G.cost_begin : ~0u;
+  v.tiles = G.cols >> 10;
+  return v;
+}
+
 // Unit q of the launch: a row of one group, or (GATED) row q of the gate
-// tensor followed by row q of the up tensor.
-template <bool GATED>
-__device__ __forceinline__ Pos row_pos(const RingLaunch& L, uint32_t q) {
+// tensor followed by row q of the up tensor.  The group is the last one whose
+// first row is at or before q (a ballot over the group table, no memory).
+template <bool GATED, int C>
+__device__ __forceinline__ Pos row_pos(const RingLaunch& L, const GroupRegs& GR, uint32_t q) {
   Pos p;
   p.valid = q < L.n_rows;
   const uint32_t qq = p.valid ? q : L.n_rows - 1;
-  uint32_t g = 0;
-  while (!GATED && g + 1 < (uint32_t)L.n_groups && L.g[g + 1].cost_begin <= qq) g++;
+  const uint32_t g = GATED ? 0u : (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(GR.first_row <= qq)) - 1u;
   p.g = g;
-  p.r = qq - (uint32_t)L.g[g].cost_begin;
-  p.T = L.g[g].cols >> 10;
+  p.r = GATED ? qq : qq - (uint32_t)__builtin_amdgcn_readlane((int)GR.first_row, (int)g);
+  p.T = GATED ? L.g[0].cols >> 10 : (uint32_t)__builtin_amdgcn_readlane((int)GR.tiles, (int)g);
   p.c = 0;
-  p.S = p.valid ? min((uint32_t)kRingChunk, p.T) : 0u;
+  p.S = p.valid ? min((uint32_t)C, p.T) : 0u;
   return p;
 }
 
 __device__ __forceinline__ uint64_t tile_of(const Pos& p) { return (uint64_t)p.r * p.T + p.c; }
 
-__device__ __forceinline__ void load_idx(Slot& s, const RingLaunch& L, const Pos& p, int lane) {
+template <int C>
+__device__ __forceinline__ void load_idx(Slot<C>& s, const RingLaunch& L, const Pos& p, int lane) {
   const Planes P = ptrs_of(L.g[p.g]);
   const __amdgpu_buffer_rsrc_t r = make_rsrc(P.idx + tile_of(p), p.valid ? (p.S + 1) * 4 : 0u);
   s.idxv = __builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)lane * 4, 0, 0);
 }
 
 // Escape slice of the chunk (from its index, already loaded) and its planes.
-__device__ __forceinline__ void load_data(Slot& s, const RingLaunch& L, const Pos& p, uint32_t& e_first,
+template <int C>
+__device__ __forceinline__ void load_data(Slot<C>& s, const RingLaunch& L, const Pos& p, uint32_t& e_first,
                                           uint32_t& e_cnt, int lane) {
   const GemvGroup& G = L.g[p.g];
   const Planes P = ptrs_of(G);
@@ -442,7 +465,7 @@ __device__ __forceinline__ void load_data(Slot& s, const RingLaunch& L, const Po
   const __amdgpu_buffer_rsrc_t rr = make_rsrc(P.raw + t0 * kTile, p.S * kTile);
   const __amdgpu_buffer_rsrc_t rn = make_rsrc(P.nib + t0 * (kTile / 2), p.S * (kTile / 2));
 #pragma unroll
-  for (int j = 0; j < kRingChunk; j++) {
+  for (int j = 0; j < C; j++) {
     s.raw[j] = __builtin_amdgcn_raw_buffer_load_b128(rr, (uint32_t)lane * 16 + j * kTile, 0, kNonTemporal);
     s.nib[j] = __builtin_amdgcn_raw_buffer_load_b64(rn, (uint32_t)lane * 8 + j * (kTile / 2), 0, kNonTemporal);
   }
@@ -492,11 +515,24 @@ __device__ __forceinline__ void ring_exponents(u32x2 nib, const GemvGroup& G, ui
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
-template <int B, int W, bool GATED>
+// One round of a ring of N slots: step(integral_constant<K>) for K = 0..N-1,
+// stopping at the first that reports no further chunk.
+template <int K, int N, class F>
+__device__ __forceinline__ bool ring_round(F& f) {
+  if constexpr (K == N) {
+    return true;
+  } else {
+    if (!f(std::integral_constant<int, K>{})) return false;
+    return ring_round<K + 1, N>(f);
+  }
+}
+
+template <int B, int W, bool GATED, int C, int N>
 __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const uint32_t wave = uniform(threadIdx.x >> 6);
   const int lane = lane_id();
+  const GroupRegs GR = GATED ? GroupRegs{0u, 0u} : group_regs(L, lane);  // the gated launch has one row space
   uint8_t* slot_lds = smem + kRingXMax + wave * kTile;
   uint32_t* lctr = reinterpret_cast<uint32_t*>(smem + kRingXMax + W * kTile);
 
@@ -517,13 +553,13 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
     const uint32_t b = blockIdx.x, per = gridDim.x >> 3;
     const uint32_t cu = (gridDim.x & 7u) ? b : (b & 7u) * per + (b >> 3);
     const uint64_t q = cu + (uint64_t)k * gridDim.x;
-    return row_pos<GATED>(L, q < L.n_rows ? (uint32_t)q : L.n_rows);
+    return row_pos<GATED, C>(L, GR, q < L.n_rows ? (uint32_t)q : L.n_rows);
   };
   auto advance = [&](const Pos& p) -> Pos {
-    if (p.valid && p.c + kRingChunk < p.T) {
+    if (p.valid && p.c + C < p.T) {
       Pos n = p;
-      n.c = p.c + kRingChunk;
-      n.S = min((uint32_t)kRingChunk, p.T - n.c);
+      n.c = p.c + C;
+      n.S = min((uint32_t)C, p.T - n.c);
       return n;
     }
     if (!p.valid) return p;
@@ -531,19 +567,25 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
       Pos n = p;
       n.g = 1;
       n.c = 0;
-      n.S = min((uint32_t)kRingChunk, p.T);
+      n.S = min((uint32_t)C, p.T);
       return n;
     }
     return next_row();
   };
 
-  Slot s0, s1, s2;
-  Pos p0 = next_row();
-  Pos p1 = advance(p0);
-  uint32_t f0, n0, f1, n1;
-  load_idx(s0, L, p0, lane);
-  load_idx(s1, L, p1, lane);
-  load_data(s0, L, p0, f0, n0, lane);
+  // ring of N slots: the chunk decoded at rotation K is in slot K; then the
+  // planes and escapes of the next N - 2 chunks are in flight and the index
+  // of the one after them
+  Slot<C> sl[N];
+  Pos pp[N];
+  uint32_t ef[N], en[N];  // escape slice (first, count) of each slot's chunk
+  pp[0] = next_row();
+#pragma unroll
+  for (int i = 1; i < N - 1; i++) pp[i] = advance(pp[i - 1]);
+#pragma unroll
+  for (int i = 0; i < N - 1; i++) load_idx(sl[i], L, pp[i], lane);
+#pragma unroll
+  for (int i = 0; i < N - 2; i++) load_data(sl[i], L, pp[i], ef[i], en[i], lane);
   // stage every distinct x array while the first loads are in flight:
   // element (b, t, lane, half) at x_off + ((b*T + t)*2 + half)*1024 + lane*16
   for (uint32_t k = 0; k < L.n_xsrc; k++) {
@@ -567,17 +609,27 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
 
   // one step: chunk p0 in `cur` is decoded; the next chunk p1 (index in
   // `nx1` already) gets its escapes and planes; the one after, p2, its index
-  auto step = [&](Slot& cur, Slot& nx1, Slot& nx2) -> bool {
-    const Pos p2 = advance(p1);
-    load_idx(nx2, L, p2, lane);
-    load_data(nx1, L, p1, f1, n1, lane);
+  auto step = [&](auto rot) -> bool {
+    constexpr int K = decltype(rot)::value, I1 = (K + N - 1) % N, I2 = (K + N - 2) % N;
+    pp[I1] = advance(pp[I2]);
+    load_idx(sl[I1], L, pp[I1], lane);
+    load_data(sl[I2], L, pp[I2], ef[I2], en[I2], lane);
+    Slot<C>& cur = sl[K];
+    const Pos& p0 = pp[K];
+    const uint32_t f0 = ef[K], n0 = en[K];
     const GemvGroup& G = L.g[p0.g];
     const Planes P = ptrs_of(G);
     const uint8_t* x_g = smem + L.x_off[p0.g];
     slot_lds[lane] = (uint8_t)cur.escv;  // the chunk's escapes, for the patch path
     wave_lds_sync();
+    // bit j: the index gives tile j escapes (lane j compares idx[t0 + j] with
+    // idx[t0 + j + 1], fetched from lane j + 1 by a row shift); tiles without
+    // escapes decode with no per-tile scalar work
+    const uint32_t idx_up = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)cur.idxv, 0x101, 0xF, 0xF, false);
+    const uint64_t esc_tiles = __builtin_amdgcn_ballot_w64((uint32_t)lane < p0.S && idx_up != cur.idxv);
+    const bool contig = G.flags & 1u;
 #pragma unroll
-    for (int j = 0; j < kRingChunk; j++) {
+    for (int j = 0; j < C; j++) {
       if ((uint32_t)j < p0.S) {
         // batch rows 0..kEarly-1: x read before the decode (hides the LDS
         // latency); the rest one row at a time after it (fewer live registers)
@@ -592,10 +644,16 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
         uint32_t xr[kEarly][8];
 #pragma unroll
         for (int bb = 0; bb < kEarly; bb++) xload(bb, xr[bb]);
-        const uint32_t ia = (uint32_t)__builtin_amdgcn_readlane((int)cur.idxv, j);
-        const uint32_t ib = (uint32_t)__builtin_amdgcn_readlane((int)cur.idxv, j + 1);
         uint32_t E[4];
-        ring_exponents(cur.nib[j], G, ia, ib, cur.escv, f0, n0, P.esc, slot_lds, E);
+        if ((esc_tiles >> j) & 1u) {
+          const uint32_t ia = (uint32_t)__builtin_amdgcn_readlane((int)cur.idxv, j);
+          const uint32_t ib = (uint32_t)__builtin_amdgcn_readlane((int)cur.idxv, j + 1);
+          ring_exponents(cur.nib[j], G, ia, ib, cur.escv, f0, n0, P.esc, slot_lds, E);
+        } else if (contig) {
+          exponents16<true>(cur.nib[j], Lut{G.lut[0], G.lut[1], G.lut[2], G.lut[3]}, G.base4, E);
+        } else {
+          exponents16<false>(cur.nib[j], Lut{G.lut[0], G.lut[1], G.lut[2], G.lut[3]}, G.base4, E);
+        }
         uint32_t w[8];
         assemble16(cur.raw[j], E, w);
 #pragma unroll
@@ -615,7 +673,7 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
       }
     }
     // row end: the sums of row p0.r are stored by lane 0 (range 0 otherwise)
-    const bool row_end = p0.valid && p0.c + kRingChunk >= p0.T;
+    const bool row_end = p0.valid && p0.c + C >= p0.T;
     float v[B];
 #pragma unroll
     for (int bb = 0; bb < B; bb++) v[bb] = 0.f;
@@ -651,14 +709,10 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
       }
     }
     wave_lds_sync();  // the slot is rewritten by the next chunk
-    p0 = p1;
-    p1 = p2;
-    f0 = f1;
-    n0 = n1;
-    return p0.valid;
+    return pp[(K + 1) % N].valid;
   };
-  if (p0.valid)
-    while (step(s0, s1, s2) && step(s1, s2, s0) && step(s2, s0, s1)) {
+  if (pp[0].valid)
+    while (ring_round<0, N>(step)) {
     }
 }
 
@@ -667,20 +721,20 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
 // the others one at a time after it, which keeps batch 8 within 128 VGPRs.
 template <int B, bool GATED = false>
 static hipError_t run_ring_kernel(RingLaunch& L, hipStream_t s) {
-  constexpr int W = kRingWaves;
+  constexpr int W = kRingWaves, C = kRingTiles, N = kRingSlots;
   static std::atomic<int> ready{0};  // attribute set for this instance (per process)
   const uint32_t lds = kRingXMax + W * kTile + 16;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return hipErrorUnknown;
   if (!ready.load(std::memory_order_acquire)) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_ring<B, W, GATED>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_ring<B, W, GATED, C, N>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     ready.store(1, std::memory_order_release);
   }
   const uint32_t grid = (uint32_t)std::min<uint64_t>((uint64_t)cus, L.n_rows);
-  hipLaunchKernelGGL((k_gemv_ring<B, W, GATED>), dim3(grid), dim3(W * kWave), lds, s, L);
+  hipLaunchKernelGGL((k_gemv_ring<B, W, GATED, C, N>), dim3(grid), dim3(W * kWave), lds, s, L);
   return hipGetLastError();
 }
 
