@@ -28,13 +28,15 @@
 //    of them for trained weights) puts that exponent into the lane's own LUT
 //    slot 15 and needs no ranking; otherwise the lane ranks its escapes
 //    across the 4 lanes of its row with ds_bpermute and patches them from LDS;
-//  - x is staged per step (256 columns of every batch row) into LDS, padded
-//    so the 16-byte operand reads are conflict-free, double-buffered with one
-//    barrier per step, and loaded two steps ahead through two register sets;
-//    the coded chunks run through a ring of four register slots (two steps
-//    in flight, which keeps up to 32 columns at two waves per SIMD); every
-//    load is issued unconditionally (invalid ones go out of the buffer range
-//    and return 0).
+//  - x is staged per step (256 columns of every batch row) in LDS, loaded
+//    straight into it (buffer_load_dwordx4 ... lds: no registers) one step
+//    ahead into the other of two buffers, with one barrier per step; each
+//    row's 16-byte column chunks sit in slots XOR-swizzled by the row so the
+//    operand reads are at most two-way bank conflicted; the coded chunks run
+//    through a ring of four register slots (two steps in flight), which
+//    keeps every column count at two waves per SIMD; every coded load is
+//    issued unconditionally (invalid ones go out of the buffer range and
+//    return 0).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -53,7 +55,7 @@ constexpr int kGemmWaves = 4;
 constexpr int kGemmRows = 16 * kGemmWaves;     // rows per workgroup
 constexpr int kGemmBatch = 64;                 // batch columns per launch
 constexpr int kStepK = 256;                    // columns per pipeline step
-constexpr int kXStride = kStepK * 2 + 16;      // LDS bytes per staged x row
+constexpr int kXStride = kStepK * 2;           // LDS bytes per staged x row (16-byte chunks swizzled)
 constexpr uint32_t kEscCap = 2048;             // escape bytes per wave held in LDS
 constexpr uint32_t kOOB = 0x80000000u;         // a buffer offset past every range used here (all < 2^31)
 
@@ -124,40 +126,33 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
       Sl.nib[j] = __builtin_amdgcn_raw_buffer_load_b64(rn, vn + 32u * j, sn, 0);
     }
   };
-  // x of step k for every K part: piece p = 256 S m + threadIdx.x is part
-  // h = p / (512 NB) (the same for a whole wave), batch row (p / 32) % (16 NB),
-  // bytes 16 (p % 32) of the part's 256 columns; rows past the batch are past
-  // the range
-  struct XRegs {
-    u32x4 v[NB * 2];
-  };
-  auto load_x = [&](XRegs& xr, uint32_t k) {
+  // x of step k for every K part, loaded straight into LDS (no registers):
+  // chunk P = 256 S m + threadIdx.x (16 bytes) is part h = P / (512 NB),
+  // batch row (P / 32) % (16 NB) and slot s = P % 32 of that row, which holds
+  // column chunk s ^ (row & 7) of the step's 256 columns; one instruction
+  // fills 64 consecutive slots.  A part past the row's tiles gets zeros.
+  auto dma_x = [&](uint32_t k, uint32_t buf) {
 #pragma unroll
     for (int m = 0; m < NB * 2; m++) {
-      const uint32_t p = 256u * S * m + threadIdx.x;
-      const uint32_t h = uniform(p / (512u * NB)), row = (p >> 5) % (16u * NB);
+      const uint32_t p0 = 256u * S * m + uniform(threadIdx.x & ~63u);  // the wave's first chunk
+      const uint32_t p = p0 + (uint32_t)lane;
+      const uint32_t h = p0 / (512u * NB), pp = p % (512u * NB), row = pp >> 5, slot = pp & 31u;
       const uint32_t c = (k >> 2) * S + h;
-      const bool ok = k < n_steps && c < T;
-      const uint32_t vo = ok ? row * G.cols * 2 + (p & 31u) * 16u : kOOB;
-      const uint32_t so = ok ? (c * kTile + (k & 3u) * kStepK) * 2 : 0u;
-      xr.v[m] = __builtin_amdgcn_raw_buffer_load_b128(rx, vo, so, kNonTemporal);
-    }
-  };
-  auto store_x = [&](const XRegs& xr, uint32_t buf) {
-#pragma unroll
-    for (int m = 0; m < NB * 2; m++) {
-      const uint32_t p = 256u * S * m + threadIdx.x;
-      const uint32_t h = p / (512u * NB), row = (p >> 5) % (16u * NB);
-      *reinterpret_cast<u32x4*>(xs + (buf * S + h) * kXBuf + row * kXStride + (p & 31u) * 16u) = xr.v[m];
+      uint8_t* dst = xs + (buf * S + h) * kXBuf + (p0 % (512u * NB)) * 16u;
+      if (c < T) {
+        const uint32_t vo = row * G.cols * 2 + (slot ^ (row & 7u)) * 16u;
+        const uint32_t so = (c * kTile + (k & 3u) * kStepK) * 2;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)dst, 16, vo, so, 0, 0);
+      } else {
+        *reinterpret_cast<u32x4*>(dst + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+      }
     }
   };
 
-  // issue order (loads retire in order): x and coded data 2 steps ahead
+  // issue order (loads retire in order): x of step 0, coded data 2 steps ahead
   GSlot s0, s1, s2, s3;
-  XRegs xa, xb;
-  load_x(xa, 0);
+  dma_x(0, 0);
   load_step(s0, 0);
-  load_x(xb, 1);
   load_step(s1, 1);
 
   // the row block's index words idx[t_first .. t_first + tiles_here] and
@@ -177,7 +172,7 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
       for (uint32_t w = (uint32_t)lane; w < nw; w += kWave) reinterpret_cast<uint32_t*>(esc_l)[w] = src[w];
     }
   }
-  store_x(xa, 0);
+  __builtin_amdgcn_s_waitcnt(0);  // x of step 0 is in LDS (every load of this wave done)
   __syncthreads();
   if (rows_here) {
     e_lo = idx_l[0];
@@ -186,6 +181,7 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
     dense = e_hi - a0 > kEscCap;
   }
 
+  const uint32_t xsw[2] = {((2u * lq) ^ (li & 7u)) * 16u, ((2u * lq + 1u) ^ (li & 7u)) * 16u};
   f32x4 acc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; nb++) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -211,9 +207,14 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
     // is computed from slot `cur` and x buffer k % 2, and x of step k + 1
     // (issued a step earlier) goes to x buffer (k + 1) % 2.  A tile starts
     // every 4 steps (TILE_START).
-    auto step = [&](GSlot& cur, GSlot& nx2, XRegs& x_in, const XRegs& x_out, uint32_t k, auto tile_start) {
-      load_x(x_in, k + 2);
+    auto step = [&](GSlot& cur, GSlot& nx2, uint32_t k, auto tile_start) {
+      // x of step k + 1 into the other buffer (read last in step k - 1,
+      // before the barrier that ended it), then coded data of step k + 2
+      const bool more = k + 1 < n_steps;
+      if (more) dma_x(k + 1, (k + 1) & 1u);
+      __builtin_amdgcn_sched_barrier(0);
       load_step(nx2, k + 2);
+      __builtin_amdgcn_sched_barrier(0);
       if constexpr (decltype(tile_start)::value) {
         const uint32_t c = (k >> 2) * S + kh;
         uint32_t ia = e_lo, ib = e_lo;
@@ -231,7 +232,7 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
         run = 0;
       }
       const Lut lut{G.lut[0], G.lut[1], G.lut[2], t3};
-      const uint8_t* xb = xs + ((k & 1u) * S + kh) * kXBuf + li * kXStride + lq * 32u;
+      const uint8_t* xb = xs + ((k & 1u) * S + kh) * kXBuf + li * kXStride;
 #pragma unroll
       for (int j = 0; j < 4; j++) {
         uint32_t E[4];
@@ -272,21 +273,23 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
           const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{w[4 * h], w[4 * h + 1], w[4 * h + 2], w[4 * h + 3]});
 #pragma unroll
           for (int nb = 0; nb < NB; nb++) {
-            const u32x4 xv = *reinterpret_cast<const u32x4*>(xb + nb * 16 * kXStride + j * 128 + h * 16);
+            const u32x4 xv = *reinterpret_cast<const u32x4*>(xb + nb * 16 * kXStride + j * 128 + xsw[h]);
             acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, xv), acc[nb], 0, 0, 0);
           }
         }
       }
-      store_x(x_out, (k + 1) & 1u);
+      // this wave's x of step k + 1 has landed (only the 8 coded loads of
+      // step k + 2 are younger); the barrier makes every wave's visible
+      if (more) __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8), expcnt/lgkmcnt not waited
       __syncthreads();
     };
 
     // n_steps is a multiple of 4: one iteration is one tile
     for (uint32_t k = 0; k < n_steps; k += 4) {
-      step(s0, s2, xa, xb, k, std::true_type{});
-      step(s1, s3, xb, xa, k + 1, std::false_type{});
-      step(s2, s0, xa, xb, k + 2, std::false_type{});
-      step(s3, s1, xb, xa, k + 3, std::false_type{});
+      step(s0, s2, k, std::true_type{});
+      step(s1, s3, k + 1, std::false_type{});
+      step(s2, s0, k + 2, std::false_type{});
+      step(s3, s1, k + 3, std::false_type{});
     }
   };
   if (dense)
