@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
       const uint32_t c = (k >> 2) * S + h;
       uint8_t* dst = xs + (buf * S + h) * kXBuf + (p0 % (512u * NB)) * 16u;
       if (c < T) {
-        const uint32_t vo = row * G.cols * 2 + (slot ^ (row & 7u)) * 16u;
+        const uint32_t vo = row * G.cols * 2 + (slot ^ (row & 15u)) * 16u;
         const uint32_t so = (c * kTile + (k & 3u) * kStepK) * 2;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)dst, 16, vo, so, 0, 0);
       } else {
@@ -181,7 +181,11 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
     dense = e_hi - a0 > kEscCap;
   }
 
-  const uint32_t xsw[2] = {((2u * lq) ^ (li & 7u)) * 16u, ((2u * lq + 1u) ^ (li & 7u)) * 16u};
+  // slot of column chunk 8 j + 2 lq + h in row nb 16 + li: (8 j + 2 lq + h) ^ li
+  // = 8 (j ^ (li >> 3)) + ((2 lq + h) ^ (li & 7)); byte offset 128 j + xsw[j & 1][h]
+  const uint32_t sw_lo0 = ((2u * lq) ^ (li & 7u)) * 16u, sw_lo1 = ((2u * lq + 1u) ^ (li & 7u)) * 16u;
+  const uint32_t flip = (li >> 3) * 128u;  // rows 8..15 of a block swap 128-byte groups 2i and 2i + 1
+  const uint32_t xsw[2][2] = {{sw_lo0 + flip, sw_lo1 + flip}, {sw_lo0 - flip, sw_lo1 - flip}};
   f32x4 acc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; nb++) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -273,7 +277,7 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
           const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{w[4 * h], w[4 * h + 1], w[4 * h + 2], w[4 * h + 3]});
 #pragma unroll
           for (int nb = 0; nb < NB; nb++) {
-            const u32x4 xv = *reinterpret_cast<const u32x4*>(xb + nb * 16 * kXStride + j * 128 + xsw[h]);
+            const u32x4 xv = *reinterpret_cast<const u32x4*>(xb + nb * 16 * kXStride + j * 128 + xsw[j & 1][h]);
             acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, xv), acc[nb], 0, 0, 0);
           }
         }
@@ -386,17 +390,17 @@ hipError_t launch_gemm(const GemvGroup* groups, int n_groups, int batch, int y_d
     }
     L.wg_begin[n_groups] = wg;
     L.idx_bytes = (4 * (16 * t_max + 1) + 15) & ~15u;
-    // up to 32 columns, rows of two or more tiles split K over two waves per
-    // row block (8 waves a workgroup, two per SIMD): a gate-sized tensor has
-    // too few 16-row blocks to fill the chip otherwise; with 48 or 64
-    // columns the split would spill registers
+    // rows of two or more tiles split K over two waves per row block (8
+    // waves a workgroup, two per SIMD): a gate-sized tensor has too few
+    // 16-row blocks to fill the chip otherwise (at 64 columns the split
+    // takes gate_proj from 46 to 37 us)
     const bool split = t_min >= 2;
     hipError_t e;
     switch ((nb + 15) / 16) {
       case 1: e = split ? run_gemm<1, 2>(L, wg, s) : run_gemm<1, 1>(L, wg, s); break;
       case 2: e = split ? run_gemm<2, 2>(L, wg, s) : run_gemm<2, 1>(L, wg, s); break;
-      case 3: e = run_gemm<3, 1>(L, wg, s); break;
-      default: e = run_gemm<4, 1>(L, wg, s); break;
+      case 3: e = split ? run_gemm<3, 2>(L, wg, s) : run_gemm<3, 1>(L, wg, s); break;
+      default: e = split ? run_gemm<4, 2>(L, wg, s) : run_gemm<4, 1>(L, wg, s); break;
     }
     if (e != hipSuccess) return e;
   }
