@@ -29,8 +29,10 @@
 //    slot 15 and needs no ranking; otherwise the lane ranks its escapes
 //    across the 4 lanes of its row with ds_bpermute and patches them from LDS;
 //  - x is staged per step (256 columns of every batch row) in LDS, loaded
-//    straight into it (buffer_load_dwordx4 ... lds: no registers) one step
-//    ahead into the other of two buffers, with one barrier per step; each
+//    straight into it (buffer_load_dwordx4 ... lds: no registers): with up
+//    to 32 columns two steps at a time into four buffers, a barrier every
+//    second step; above, one step ahead into two buffers, a barrier every
+//    step (LDS holds no more at the occupancy the kernel runs at); each
 //    row's 16-byte column chunks sit in slots XOR-swizzled by the row so the
 //    operand reads are at most two-way bank conflicted; the coded chunks run
 //    through a ring of four register slots (two steps in flight), which
@@ -71,7 +73,7 @@ struct GSlot {
   u32x2 nib[4];
 };
 
-template <int NB, int S>
+template <int NB, int S, int XB>
 __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const uint32_t wave = uniform(threadIdx.x >> 6);
@@ -92,8 +94,8 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
   const uint64_t t_first = (uint64_t)r0 * T;
 
   constexpr uint32_t kXBuf = NB * 16 * kXStride;  // one K part's x of one step
-  uint8_t* xs = smem;                             // [2 buffers][S parts][NB * 16 rows][kXStride]
-  uint8_t* wl = smem + 2 * S * kXBuf + rb * (L.idx_bytes + kEscCap);  // shared by the row block's waves
+  uint8_t* xs = smem;                             // [XB buffers][S parts][NB * 16 rows][kXStride]
+  uint8_t* wl = smem + XB * S * kXBuf + rb * (L.idx_bytes + kEscCap);  // shared by the row block's waves
   uint32_t* idx_l = reinterpret_cast<uint32_t*>(wl);
   uint8_t* esc_l = wl + L.idx_bytes;
 
@@ -152,6 +154,7 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
   // issue order (loads retire in order): x of step 0, coded data 2 steps ahead
   GSlot s0, s1, s2, s3;
   dma_x(0, 0);
+  if (XB == 4 && 1 < n_steps) dma_x(1, 1);
   load_step(s0, 0);
   load_step(s1, 1);
 
@@ -212,10 +215,19 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
     // (issued a step earlier) goes to x buffer (k + 1) % 2.  A tile starts
     // every 4 steps (TILE_START).
     auto step = [&](GSlot& cur, GSlot& nx2, uint32_t k, auto tile_start) {
-      // x of step k + 1 into the other buffer (read last in step k - 1,
-      // before the barrier that ended it), then coded data of step k + 2
+      // XB == 2: x of step k + 1 into the other buffer (read last in step
+      // k - 1, before the barrier that ended it).  XB == 4: at even steps, x
+      // of steps k + 2 and k + 3 into the buffers read in steps k - 2 and
+      // k - 1; barriers only after odd steps.  Then coded data of step k + 2.
       const bool more = k + 1 < n_steps;
-      if (more) dma_x(k + 1, (k + 1) & 1u);
+      if constexpr (XB == 2) {
+        if (more) dma_x(k + 1, (k + 1) & 1u);
+      } else {
+        if ((k & 1u) == 0) {
+          if (k + 2 < n_steps) dma_x(k + 2, (k + 2) & 3u);
+          if (k + 3 < n_steps) dma_x(k + 3, (k + 3) & 3u);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
       load_step(nx2, k + 2);
       __builtin_amdgcn_sched_barrier(0);
@@ -236,7 +248,7 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
         run = 0;
       }
       const Lut lut{G.lut[0], G.lut[1], G.lut[2], t3};
-      const uint8_t* xb = xs + ((k & 1u) * S + kh) * kXBuf + li * kXStride;
+      const uint8_t* xb = xs + ((k % XB) * S + kh) * kXBuf + li * kXStride;
 #pragma unroll
       for (int j = 0; j < 4; j++) {
         uint32_t E[4];
@@ -284,8 +296,15 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
       }
       // this wave's x of step k + 1 has landed (only the 8 coded loads of
       // step k + 2 are younger); the barrier makes every wave's visible
-      if (more) __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8), expcnt/lgkmcnt not waited
-      __syncthreads();
+      if constexpr (XB == 2) {
+        if (more) __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8), expcnt/lgkmcnt not waited
+        __syncthreads();
+      } else if (k & 1u) {
+        // x of steps k + 1, k + 2 issued at step k - 1, before the coded
+        // loads of steps k + 1 and k + 2 (16 younger loads)
+        if (more) __builtin_amdgcn_s_waitcnt(0x0F70 | 16);  // vmcnt(16)
+        __syncthreads();
+      }
     };
 
     // n_steps is a multiple of 4: one iteration is one tile
@@ -349,20 +368,22 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
   }
 }
 
-// Largest dynamic LDS size each kernel instance was opened up to.
+// Largest dynamic LDS size each kernel instance was opened up to (x buffers:
+// four up to 32 columns, two above).
 static std::atomic<int> g_lds_set[4][2];
 
 template <int NB, int S>
 static hipError_t run_gemm(const GemmLaunch& L, uint32_t grid, hipStream_t s) {
-  const int lds = 2 * S * NB * 16 * kXStride + kGemmWaves * (int)(L.idx_bytes + kEscCap);
+  constexpr int XB = NB <= 2 ? 4 : 2;
+  const int lds = XB * S * NB * 16 * kXStride + kGemmWaves * (int)(L.idx_bytes + kEscCap);
   std::atomic<int>& set = g_lds_set[NB - 1][S - 1];
   if (set.load(std::memory_order_relaxed) < lds) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<NB, S>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<NB, S, XB>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     set.store(lds, std::memory_order_relaxed);
   }
-  hipLaunchKernelGGL((k_gemm<NB, S>), dim3(grid), dim3(kGemmWaves * S * kWave), lds, s, L);
+  hipLaunchKernelGGL((k_gemm<NB, S, XB>), dim3(grid), dim3(kGemmWaves * S * kWave), lds, s, L);
   return hipGetLastError();
 }
 
