@@ -177,9 +177,11 @@ def summarize_counters(fetch_csv: str, write_csv: str, kernel_key: str, alg_byte
     return out
 
 
-def cpu_baseline(Ws, xs, min_seconds: float):
+def cpu_baseline(Ws, xs, min_seconds: float, workers: int = 0):
     """The oracle (plain scalar C, one thread) on this host: decode the
-    layer's blobs and run the float64 matvec, repeated until min_seconds."""
+    layer's blobs and run the float64 matvec, repeated until min_seconds.
+    With workers > 1, also the same oracle calls in that many processes at
+    once (one tensor pass per job), the host's all-cores figure."""
     from oracle import oracle as O
 
     blobs = [O.encode(W) for W in Ws]  # untimed: the baseline is decode + product
@@ -194,10 +196,70 @@ def cpu_baseline(Ws, xs, min_seconds: float):
         t += time.perf_counter() - t0
         passes += 1
     gbs = 2.0 * n * passes / t / 1e9
-    return {"value": gbs, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "full 8B-shaped layer (7 tensors, %d weights) x %d pass(es): oracle decode of each "
-                      "oracle-coded blob + float64 matvec at batch 1, %.1f s" % (n, passes, t),
-            "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
+    out = {"value": gbs, "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": "full 8B-shaped layer (7 tensors, %d weights) x %d pass(es): oracle decode of each "
+                     "oracle-coded blob + float64 matvec at batch 1, %.1f s" % (n, passes, t),
+           "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
+    if workers > 1:
+        out["all_cores"] = oracle_all_cores(blobs, xs, min_seconds, workers)
+    return out
+
+
+def _oracle_worker_init():
+    from oracle import oracle as O
+
+    O.lib()  # load the oracle library before any job is timed
+
+
+def _oracle_job(item):
+    """One oracle pass over one tensor (a worker process): decode + matvec."""
+    from oracle import oracle as O
+
+    blob_path, x_path = item
+    W = O.decode(np.load(blob_path, mmap_mode="r"))
+    O.matvec(W, np.load(x_path))
+    return W.size
+
+
+def oracle_all_cores(blobs, xs, min_seconds: float, workers: int):
+    """The same oracle calls as cpu_baseline in `workers` processes at once:
+    jobs are (tensor, pass) pairs, the blobs are shared through memory-mapped
+    files, and the figure is weights processed over wall time.  A worker that
+    dies or a job slower than a minute ends this leg with an error entry,
+    never the benchmark."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    import shutil
+    import tempfile
+
+    d = tempfile.mkdtemp(prefix="lbf_oracle_")
+    try:
+        items = []
+        for m, (b, x) in enumerate(zip(blobs, xs)):
+            bp, xp = os.path.join(d, "blob%d.npy" % m), os.path.join(d, "x%d.npy" % m)
+            np.save(bp, b)
+            np.save(xp, x)
+            items.append((bp, xp))
+        # fresh interpreters (spawn): nothing of this process's GPU state
+        with cf.ProcessPoolExecutor(workers, mp_context=mp.get_context("spawn"),
+                                    initializer=_oracle_worker_init) as pool:
+            def run(jobs):
+                return sum(f.result(timeout=60.0) for f in [pool.submit(_oracle_job, j) for j in jobs])
+
+            run([items[1]] * workers)  # every worker up and warm
+            per_round = max(1, 4 * workers // len(items))
+            weights, t, rounds = 0, 0.0, 0
+            while rounds == 0 or t < min_seconds:
+                t0 = time.perf_counter()
+                weights += run(items * per_round)
+                t += time.perf_counter() - t0
+                rounds += 1
+    except Exception as e:  # noqa: BLE001 - reported in the JSON line instead
+        return {"error": "%s: %s" % (type(e).__name__, e), "cores": workers}
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
+    return {"value": 2.0 * weights / t / 1e9, "unit": "GB/s", "cores": workers, "kind": "oracle",
+            "sample": "the same layer passes in %d processes at once: %d weights in %.1f s" % (workers, weights, t)}
 
 
 def main():
@@ -337,7 +399,7 @@ def main():
 
     if not args.no_cpu:
         log("timing the CPU oracle (~%.0f s)" % args.cpu_seconds)
-        out["cpu_baseline"] = cpu_baseline(Ws, xs, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(Ws, xs, args.cpu_seconds, min(16, os.cpu_count() or 1))
     print(json.dumps(out))
 
 

@@ -1,0 +1,17 @@
+"""Host-side pieces of bench.py that run without a GPU: the CPU oracle
+baseline on one core and in several processes at once."""
+import numpy as np
+
+import bench
+from decode_byte_split_amd import synth
+
+
+def test_cpu_baseline_one_core_and_all_cores():
+    rng = np.random.default_rng(3)
+    Ws = [synth.gaussian(rng, 64, 1024, 0.02, 0.001, 50.0) for _ in range(2)]
+    xs = [synth.activations(rng, 1, 1024) for _ in range(2)]
+    r = bench.cpu_baseline(Ws, xs, 0.2, 2)
+    assert r["kind"] == "oracle" and r["cores"] == 1 and r["value"] > 0
+    a = r["all_cores"]
+    assert "error" not in a, a
+    assert a["cores"] == 2 and a["kind"] == "oracle" and a["value"] > 0
