@@ -98,28 +98,31 @@ def time_each(torch, fn, steps: int, warmup: int):
 READ_BYTES = 1 << 30  # the read-stream ceiling runs over 1 GiB
 
 
-def read_ceiling(torch, reps: int = 10) -> float:
+def read_ceiling(torch, reps: int = 10, nbytes: int = READ_BYTES) -> float:
     """GB/s of a plain read stream (liblbf_measure.so: 128-bit non-temporal
-    loads, XOR-reduced) over 1 GiB, the practical ceiling for a kernel that
-    only reads HBM."""
+    loads, XOR-reduced) over nbytes (default 1 GiB: the practical ceiling for
+    a kernel that only reads HBM).  Smaller reads rotate over enough buffers
+    to keep the working set at 1 GiB or more, past the 256 MB cache."""
     import ctypes
 
     L = ctypes.CDLL(os.path.join(ROOT, "decode_byte_split_amd", "liblbf_measure.so"))
     L.lbfm_read_stream.restype = ctypes.c_int
     L.lbfm_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
-    buf = torch.ones(READ_BYTES // 4, dtype=torch.float32, device="cuda")
+    nbytes = max(16, nbytes // 16 * 16)
+    nbuf = -(-READ_BYTES // nbytes)
+    bufs = [torch.ones(nbytes // 4, dtype=torch.float32, device="cuda") for _ in range(nbuf)]
     out = torch.zeros(1, dtype=torch.int32, device="cuda")
     blocks = torch.cuda.get_device_properties(0).multi_processor_count  # one workgroup per CU
     s = torch.cuda.current_stream().cuda_stream
 
     def run(i):
-        rc = L.lbfm_read_stream(buf.data_ptr(), READ_BYTES, out.data_ptr(), blocks, s)
+        rc = L.lbfm_read_stream(bufs[i % nbuf].data_ptr(), nbytes, out.data_ptr(), blocks, s)
         assert rc == 0, "read-stream kernel failed (%d)" % rc
 
-    ms = time_region(torch, run, reps, 3)
-    del buf, out
+    ms = time_region(torch, run, max(reps, 3 * nbuf), 3)
+    del bufs, out
     torch.cuda.empty_cache()
-    return READ_BYTES / (ms * 1e-3) / 1e9
+    return nbytes / (ms * 1e-3) / 1e9
 
 
 def cpu_model() -> str:
@@ -347,12 +350,16 @@ def main():
     # side lanes, same run: the read-stream ceiling, and the uncompressed
     # layer through torch's F.linear (four rotating BF16 copies)
     ceiling = read_ceiling(torch)
+    # the same read over exactly the launch's algorithmic bytes: a kernel that
+    # only streams them, with its own launch, ramp-up and tail
+    same_us = alg / (read_ceiling(torch, 40, alg) * 1e9) * 1e6
     wrot = [[dev(torch, W) for W in Ws] for _ in range(4)]
     raw_ms = time_region(torch, lambda i: [torch.nn.functional.linear(x, w) for x, w in zip(xd, wrot[i % 4])],
                          20, 3)
     del wrot
     torch.cuda.empty_cache()
-    log("read-stream ceiling %.1f GB/s; raw BF16 F.linear layer %.2f us" % (ceiling, raw_ms * 1e3))
+    log("read-stream ceiling %.1f GB/s; the same read over the launch's %d bytes %.2f us; raw BF16 F.linear layer "
+        "%.2f us" % (ceiling, alg, same_us, raw_ms * 1e3))
 
     traffic = None
     if os.path.exists(COUNTERS):
@@ -382,7 +389,9 @@ def main():
                      "kernel": KERNEL, "algorithmic_bytes_per_launch": alg,
                      "launch_ms_mean": round(ms_step, 5), "launch_ms_median": round(ms_median, 5),
                      "launch_ms_min": round(ms_min, 5), "read_stream_ceiling": round(ceiling, 1),
-                     "frac_of_read_stream_ceiling": round(achieved / ceiling, 4)},
+                     "frac_of_read_stream_ceiling": round(achieved / ceiling, 4),
+                     "read_stream_same_bytes_us": round(same_us, 2),
+                     "speed_vs_same_bytes_read": round(same_us / (ms_step * 1e3), 4)},
         "side_lanes": {"raw_bf16_linear_layer_us": round(raw_ms * 1e3, 2),
                        "speedup_vs_raw_bf16": round(raw_ms / ms_step, 3),
                        "read_stream_ceiling_GBs": round(ceiling, 1)},
