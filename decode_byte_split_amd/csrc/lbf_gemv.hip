@@ -60,6 +60,63 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (r0 + r1) + (r2 + r3);
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// v from lane i ^ 32 (H = 32) or i ^ 16 (H = 16), by the gfx950 lane swaps:
+// swapping a register with itself leaves each lane's partner value in one
+// of the two results.
+template <int H>
+__device__ __forceinline__ float lane_xor(float v, bool upper) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto r = H == 32 ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
+                         : __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __builtin_bit_cast(float, upper ? r[0] : r[1]);
+}
+
+// out[b] = sum over the wave of in[b], b < B, uniform (B <= 8), in a fixed
+// order.  Instead of B separate reductions, B values are folded together:
+// at each of up to three lane bits (3, then 5, then 4) the lanes on one side
+// keep the lower half of their values and the others the upper half, each
+// adding its partner's copy of what it kept; one value a lane remains, which
+// is summed over the remaining lane bits and read from one lane per b.
+template <int B>
+__device__ __forceinline__ void wave_sums(const float (&in)[B], float (&out)[B], int lane) {
+  if constexpr (B == 1) {
+    out[0] = wave_sum(in[0]);
+  } else {
+    constexpr int P = B <= 2 ? 2 : (B <= 4 ? 4 : 8);
+    float v[P];
+#pragma unroll
+    for (int i = 0; i < P; i++) v[i] = i < B ? in[i] : 0.f;
+    auto fold = [&](int n, bool upper, auto partner) {
+#pragma unroll
+      for (int i = 0; i < n / 2; i++) {
+        const float keep = upper ? v[n / 2 + i] : v[i], give = upper ? v[i] : v[n / 2 + i];
+        v[i] = keep + partner(give);
+      }
+    };
+    fold(P, (lane & 8) != 0, [](float g) { return dpp_f<0x128>(g); });  // row_ror:8 = lane ^ 8 in a row
+    if constexpr (P >= 4) fold(P / 2, (lane & 32) != 0, [&](float g) { return lane_xor<32>(g, (lane & 32) != 0); });
+    if constexpr (P >= 8) fold(P / 4, (lane & 16) != 0, [&](float g) { return lane_xor<16>(g, (lane & 16) != 0); });
+    float t = v[0];
+    t += dpp_f<0xB1>(t);   // lane ^ 1
+    t += dpp_f<0x4E>(t);   // lane ^ 2
+    t += dpp_f<0x141>(t);  // 7 - lane within 8: the other quad
+    if constexpr (P <= 4) t += lane_xor<16>(t, (lane & 16) != 0);
+    if constexpr (P <= 2) t += lane_xor<32>(t, (lane & 32) != 0);
+    // value index = bit 3 (P / 2) + bit 5 (P / 4) + bit 4 (P / 8) of the lane
+#pragma unroll
+    for (int b = 0; b < B; b++) {
+      const int l = P == 8 ? ((b >> 2) << 3) | (((b >> 1) & 1) << 5) | ((b & 1) << 4)
+                           : (P == 4 ? ((b >> 1) << 3) | ((b & 1) << 5) : b << 3);
+      out[b] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, t), l));
+    }
+  }
+}
+
 template <int B>
 __device__ __forceinline__ void dot16(const uint32_t w[8], const uint32_t (*xr)[8], float acc[B][2]) {
 #pragma unroll
@@ -190,11 +247,13 @@ __device__ __forceinline__ void run_rows(RowBuf<SMAX>& A, const uint8_t* raw_p, 
                                          float (*part)[kGemvWaves][B], uint32_t wave, bool accumulate, int lane) {
   RowBuf<SMAX> Bf;
   auto finish = [&](uint32_t ul, float acc[B][2]) {
+    float in[B], sum[B];
 #pragma unroll
-    for (int b = 0; b < B; b++) {
-      const float s = wave_sum(acc[b][0] + acc[b][1]);
-      if (lane == 0) part[ul][wave][b] = (accumulate ? part[ul][wave][b] : 0.f) + s;
-    }
+    for (int b = 0; b < B; b++) in[b] = acc[b][0] + acc[b][1];
+    wave_sums<B>(in, sum, lane);
+#pragma unroll
+    for (int b = 0; b < B; b++)
+      if (lane == 0) part[ul][wave][b] = (accumulate ? part[ul][wave][b] : 0.f) + sum[b];
   };
   const uint32_t last = n_mine - 1;
   for (uint32_t ul = 0;; ul += 2) {
@@ -678,11 +737,13 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
 #pragma unroll
     for (int bb = 0; bb < B; bb++) v[bb] = 0.f;
     if (row_end) {
+      float in[B];
 #pragma unroll
       for (int bb = 0; bb < B; bb++) {
-        v[bb] = wave_sum(acc[bb][0] + acc[bb][1]);
+        in[bb] = acc[bb][0] + acc[bb][1];
         acc[bb][0] = acc[bb][1] = 0.f;
       }
+      wave_sums<B>(in, v, lane);
     }
     // GATED: the gate row's sums wait in gsum; the up row's end stores
     // silu(gate) * up into h
