@@ -365,8 +365,11 @@ __device__ __forceinline__ void run_segment(const GemvGroup& G, uint32_t u_lo, u
   }
 }
 
+// Batch 5..8 (one tile a K slice) is held to 128 VGPRs, four waves per SIMD:
+// batch 8 would take 129 and drop to three (the layer at batch 8: 119 -> 110 us).
 template <int B, int SMAX>
-__global__ __launch_bounds__(kGemvWaves * kWave) void k_gemv(GemvLaunch L) {
+__global__ __launch_bounds__(kGemvWaves * kWave) __attribute__((amdgpu_waves_per_eu(B >= 5 ? 4 : 1)))
+void k_gemv(GemvLaunch L) {
   __shared__ float part[kSubUnits][kGemvWaves][B];
   __shared__ uint8_t esc_sh[kEscShared];
   __shared__ uint8_t esc_wave[kGemvWaves][kTile];
