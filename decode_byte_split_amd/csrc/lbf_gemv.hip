@@ -884,11 +884,12 @@ hipError_t launch_gemv(const GemvGroup* groups, int n_groups, int batch, int y_d
   const hipError_t e = launch_ring(groups, n_groups, batch, y_dtype, used, s);
   if (used || e != hipSuccess) return e;
   // tiles a wave's K slice holds per pass: x of the slice sits in registers
-  // (smax * batch * 8 VGPRs), so fewer tiles means more waves per SIMD; at
+  // (smax * batch * 8 VGPRs), so fewer tiles means more waves per SIMD (batch
+  // 1: two tiles, 92 instead of 147 VGPRs, 64 experts 176 -> 146 us); at
   // batch 4, one tile when no row is wider than 4 tiles (64 experts of 4096
   // columns: 187 -> 168 us at five waves per SIMD instead of three), two
   // otherwise (a 14-tile down_proj is faster with two)
-  static const int smax_of[9] = {0, 4, 2, 2, 2, 1, 1, 1, 1};
+  static const int smax_of[9] = {0, 2, 2, 2, 2, 1, 1, 1, 1};
   uint32_t t_max = 0;
   for (int g = 0; g < n_groups; g++) t_max = std::max(t_max, groups[g].cols >> 10);
   const uint32_t smax = batch == 4 && t_max <= 4 ? 1u : (uint32_t)smax_of[batch];
@@ -912,7 +913,7 @@ hipError_t launch_gemv(const GemvGroup* groups, int n_groups, int batch, int y_d
   }
   L.total_cost = cost;
   switch (batch) {
-    case 1: return run<1, 4>(L, s);
+    case 1: return run<1, 2>(L, s);
     case 2: return run<2, 2>(L, s);
     case 3: return run<3, 2>(L, s);
     case 4: return smax == 1 ? run<4, 1>(L, s) : run<4, 2>(L, s);
