@@ -293,3 +293,24 @@ def test_gemv_tiny_groups_share_x(env, batch):
         check_product(y, y_ref, a_ref, False)
     y_ref, a_ref = O.matvec(Ws[31], x_big)
     check_product(ys[31], y_ref, a_ref, False)
+
+
+@pytest.mark.parametrize("batch", [1, 4])
+def test_gemv_layer_twice_static_kernel(env, batch):
+    """The layer's seven tensors twice in one call, each time with its own x
+    (14 distinct x arrays: 152 KB at batch 1, too much for LDS, so the static
+    kernel runs, with 4- and 14-tile rows mixed): row ranges at the start,
+    middle and end of every output match the oracle."""
+    torch, lbf = env
+    Ws = [synth.layer_tensor(m) for m in range(len(synth.LAYER))]
+    blobs = [lbf.encode(dev(torch, W)) for W in Ws]
+    rng = np.random.default_rng([11, batch])
+    xs = [synth.activations(rng, batch, W.shape[1]) for W in Ws + Ws]
+    ys = lbf.gemv(blobs + blobs, [dev(torch, x) for x in xs], lbf.LBF_F32)
+    torch.cuda.synchronize()
+    for i, (W, x, y) in enumerate(zip(Ws + Ws, xs, ys)):
+        R = W.shape[0]
+        for r0 in (0, R // 2 - 64, R - 128):
+            y_ref, a_ref = O.matvec(W, x, rows=(r0, r0 + 128))
+            check_product(y[:, r0:r0 + 128], y_ref, a_ref, False)
+        say("layer twice, batch %d, tensor %d ok" % (batch, i))
