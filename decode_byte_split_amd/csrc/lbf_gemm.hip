@@ -29,8 +29,10 @@
 //    slot 15 and needs no ranking; otherwise the lane ranks its escapes
 //    across the 4 lanes of its row with ds_bpermute and patches them from LDS;
 //  - x is staged per step (256 columns of every batch row) in LDS, loaded
-//    straight into it (buffer_load_dwordx4 ... lds: no registers): with up
-//    to 32 columns two steps at a time into four buffers, a barrier every
+//    straight into it (buffer_load_dwordx4 ... lds: no registers): with 16
+//    columns and K in two parts, every step's x at once before the loop when
+//    it fits (a 4096-column tensor: 128 KB), and no barrier after; otherwise
+//    up to 32 columns two steps at a time into four buffers, a barrier every
 //    second step; above, one step ahead into two buffers, a barrier every
 //    step (LDS holds no more at the occupancy the kernel runs at); each
 //    row's 16-byte column chunks sit in slots XOR-swizzled by the row so the
@@ -60,11 +62,13 @@ constexpr int kStepK = 256;                    // columns per pipeline step
 constexpr int kXStride = kStepK * 2;           // LDS bytes per staged x row (16-byte chunks swizzled)
 constexpr uint32_t kEscCap = 2048;             // escape bytes per wave held in LDS
 constexpr uint32_t kOOB = 0x80000000u;         // a buffer offset past every range used here (all < 2^31)
+constexpr uint32_t kFullXLds = 160 * 1024;     // LDS of one workgroup a CU
 
 struct GemmLaunch {
   GemvGroup g[LBF_MAX_GROUPS];
   uint32_t wg_begin[LBF_MAX_GROUPS + 1];  // first workgroup of each group
   uint32_t idx_bytes;                     // LDS bytes per wave for index words
+  uint32_t x_steps;                       // XB == 0: x buffers (steps) staged up front
   int n_groups, batch, y_bf16;
 };
 
@@ -95,7 +99,8 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
 
   constexpr uint32_t kXBuf = NB * 16 * kXStride;  // one K part's x of one step
   uint8_t* xs = smem;                             // [XB buffers][S parts][NB * 16 rows][kXStride]
-  uint8_t* wl = smem + XB * S * kXBuf + rb * (L.idx_bytes + kEscCap);  // shared by the row block's waves
+  const uint32_t n_xbuf = XB ? (uint32_t)XB : L.x_steps;
+  uint8_t* wl = smem + n_xbuf * S * kXBuf + rb * (L.idx_bytes + kEscCap);  // shared by the row block's waves
   uint32_t* idx_l = reinterpret_cast<uint32_t*>(wl);
   uint8_t* esc_l = wl + L.idx_bytes;
 
@@ -153,8 +158,12 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
 
   // issue order (loads retire in order): x of step 0, coded data 2 steps ahead
   GSlot s0, s1, s2, s3;
-  dma_x(0, 0);
-  if (XB == 4 && 1 < n_steps) dma_x(1, 1);
+  if (XB == 0) {  // every step's x, once
+    for (uint32_t k = 0; k < n_steps; k++) dma_x(k, k);
+  } else {
+    dma_x(0, 0);
+    if (XB == 4 && 1 < n_steps) dma_x(1, 1);
+  }
   load_step(s0, 0);
   load_step(s1, 1);
 
@@ -220,7 +229,8 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
       // of steps k + 2 and k + 3 into the buffers read in steps k - 2 and
       // k - 1; barriers only after odd steps.  Then coded data of step k + 2.
       const bool more = k + 1 < n_steps;
-      if constexpr (XB == 2) {
+      if constexpr (XB == 0) {
+      } else if constexpr (XB == 2) {
         if (more) dma_x(k + 1, (k + 1) & 1u);
       } else {
         if ((k & 1u) == 0) {
@@ -248,7 +258,7 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
         run = 0;
       }
       const Lut lut{G.lut[0], G.lut[1], G.lut[2], t3};
-      const uint8_t* xb = xs + ((k % XB) * S + kh) * kXBuf + li * kXStride;
+      const uint8_t* xb = xs + ((XB ? k % XB : k) * S + kh) * kXBuf + li * kXStride;
 #pragma unroll
       for (int j = 0; j < 4; j++) {
         uint32_t E[4];
@@ -296,7 +306,9 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
       }
       // this wave's x of step k + 1 has landed (only the 8 coded loads of
       // step k + 2 are younger); the barrier makes every wave's visible
-      if constexpr (XB == 2) {
+      if constexpr (XB == 0) {
+        (void)more;
+      } else if constexpr (XB == 2) {
         if (more) __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8), expcnt/lgkmcnt not waited
         __syncthreads();
       } else if (k & 1u) {
@@ -324,6 +336,7 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
   // through LDS (the x buffers are free after the last barrier), which adds
   // them in part order
   if constexpr (S > 1) {
+    if constexpr (XB == 0) __syncthreads();  // no wave still reads the x buffers the sums go into
     f32x4* red = reinterpret_cast<f32x4*>(smem);
     if (kh > 0) {
 #pragma unroll
@@ -369,14 +382,14 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
 }
 
 // Largest dynamic LDS size each kernel instance was opened up to (x buffers:
-// four up to 32 columns, two above).
-static std::atomic<int> g_lds_set[4][2];
+// one per step (XB = 0), four up to 32 columns, two above).
+static std::atomic<int> g_lds_set[4][2][2];
 
-template <int NB, int S>
+template <int NB, int S, int XB = (NB <= 2 ? 4 : 2)>
 static hipError_t run_gemm(const GemmLaunch& L, uint32_t grid, hipStream_t s) {
-  constexpr int XB = NB <= 2 ? 4 : 2;
-  const int lds = XB * S * NB * 16 * kXStride + kGemmWaves * (int)(L.idx_bytes + kEscCap);
-  std::atomic<int>& set = g_lds_set[NB - 1][S - 1];
+  const int n_xbuf = XB ? XB : (int)L.x_steps;
+  const int lds = n_xbuf * S * NB * 16 * kXStride + kGemmWaves * (int)(L.idx_bytes + kEscCap);
+  std::atomic<int>& set = g_lds_set[NB - 1][S - 1][XB == 0];
   if (set.load(std::memory_order_relaxed) < lds) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<NB, S, XB>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -416,9 +429,20 @@ hipError_t launch_gemm(const GemvGroup* groups, int n_groups, int batch, int y_d
     // 16-row blocks to fill the chip otherwise (at 64 columns the split
     // takes gate_proj from 46 to 37 us)
     const bool split = t_min >= 2;
+    L.x_steps = 0;
+    const bool full_x = 4u * ((t_max + 1) / 2) * 2 * 16 * kXStride + kGemmWaves * (L.idx_bytes + kEscCap) <= kFullXLds;
     hipError_t e;
     switch ((nb + 15) / 16) {
-      case 1: e = split ? run_gemm<1, 2>(L, wg, s) : run_gemm<1, 1>(L, wg, s); break;
+      case 1:
+        // 16 columns, K split in two: every step's x staged once when it fits
+        // beside the escape staging (4096 columns: 128 KB), no barriers after
+        if (split && full_x) {
+          L.x_steps = 4 * ((t_max + 1) / 2);
+          e = run_gemm<1, 2, 0>(L, wg, s);
+        } else {
+          e = split ? run_gemm<1, 2>(L, wg, s) : run_gemm<1, 1>(L, wg, s);
+        }
+        break;
       case 2: e = split ? run_gemm<2, 2>(L, wg, s) : run_gemm<2, 1>(L, wg, s); break;
       case 3: e = split ? run_gemm<3, 2>(L, wg, s) : run_gemm<3, 1>(L, wg, s); break;
       default: e = split ? run_gemm<4, 2>(L, wg, s) : run_gemm<4, 1>(L, wg, s); break;
