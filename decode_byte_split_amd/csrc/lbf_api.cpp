@@ -6,6 +6,9 @@
 #include <algorithm>
 #include <cstddef>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <tuple>
 #include <vector>
 
 #include "lbf.h"
@@ -37,21 +40,74 @@ Layout layout_of(uint64_t rows, uint64_t cols, uint64_t n_esc) {
   return L;
 }
 
+// Launch facts per device.  One lock guards the three tables; every entry is
+// computed at most once per device (per kernel and block size), so the lock
+// is taken on the host side of a launch only, never while a kernel waits.
+namespace {
+std::mutex g_facts_mu;
+std::map<int, int> g_cus;                                    // device -> CUs
+std::map<std::tuple<const void*, int, int>, int> g_per_cu;   // (kernel, device, block) -> blocks a CU
+std::map<std::pair<const void*, int>, int> g_lds;            // (kernel, device) -> dynamic LDS opened
+}  // namespace
+
+hipError_t device_cus(int* cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_facts_mu);
+  auto it = g_cus.find(dev);
+  if (it == g_cus.end()) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      return hipErrorUnknown;
+    it = g_cus.emplace(dev, n).first;
+  }
+  *cus = it->second;
+  return hipSuccess;
+}
+
+hipError_t blocks_per_cu(const void* fn, int block, int* n) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_facts_mu);
+  const auto key = std::make_tuple(fn, dev, block);
+  auto it = g_per_cu.find(key);
+  if (it == g_per_cu.end()) {
+    int v = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, fn, block, 0) != hipSuccess || v < 1) v = 1;
+    it = g_per_cu.emplace(key, v).first;
+  }
+  *n = it->second;
+  return hipSuccess;
+}
+
+hipError_t open_dynamic_lds(const void* fn, int bytes) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_facts_mu);
+  int& have = g_lds[std::make_pair(fn, dev)];
+  if (have >= bytes) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
+  have = bytes;
+  return hipSuccess;
+}
+
 // CRC-32 (IEEE 802.3), table driven.
 uint32_t crc32(const void* data, size_t len) {
-  static uint32_t table[256];
-  static bool ready = false;  // benign race: every writer stores the same table
-  if (!ready) {
-    for (uint32_t i = 0; i < 256; i++) {
-      uint32_t c = i;
-      for (int k = 0; k < 8; k++) c = (c >> 1) ^ (0xEDB88320u & (0u - (c & 1u)));
-      table[i] = c;
+  struct Table {
+    uint32_t t[256];
+    Table() {
+      for (uint32_t i = 0; i < 256; i++) {
+        uint32_t c = i;
+        for (int k = 0; k < 8; k++) c = (c >> 1) ^ (0xEDB88320u & (0u - (c & 1u)));
+        t[i] = c;
+      }
     }
-    ready = true;
-  }
+  };
+  static const Table table;  // built once; C++ makes the first use thread-safe
   const uint8_t* p = static_cast<const uint8_t*>(data);
   uint32_t c = 0xFFFFFFFFu;
-  for (size_t i = 0; i < len; i++) c = table[(c ^ p[i]) & 0xFFu] ^ (c >> 8);
+  for (size_t i = 0; i < len; i++) c = table.t[(c ^ p[i]) & 0xFFu] ^ (c >> 8);
   return c ^ 0xFFFFFFFFu;
 }
 

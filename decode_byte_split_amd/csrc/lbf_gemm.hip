@@ -44,7 +44,6 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <atomic>
 #include <type_traits>
 
 #include "lbf_device.h"
@@ -258,7 +257,7 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
         run = 0;
       }
       const Lut lut{G.lut[0], G.lut[1], G.lut[2], t3};
-      const uint8_t* xb = xs + ((XB ? k % XB : k) * S + kh) * kXBuf + li * kXStride;
+      const uint8_t* xb = xs + ((XB ? k % (XB ? XB : 1) : k) * S + kh) * kXBuf + li * kXStride;
 #pragma unroll
       for (int j = 0; j < 4; j++) {
         uint32_t E[4];
@@ -381,21 +380,12 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
   }
 }
 
-// Largest dynamic LDS size each kernel instance was opened up to (x buffers:
-// one per step (XB = 0), four up to 32 columns, two above).
-static std::atomic<int> g_lds_set[4][2][2];
-
 template <int NB, int S, int XB = (NB <= 2 ? 4 : 2)>
 static hipError_t run_gemm(const GemmLaunch& L, uint32_t grid, hipStream_t s) {
   const int n_xbuf = XB ? XB : (int)L.x_steps;
   const int lds = n_xbuf * S * NB * 16 * kXStride + kGemmWaves * (int)(L.idx_bytes + kEscCap);
-  std::atomic<int>& set = g_lds_set[NB - 1][S - 1][XB == 0];
-  if (set.load(std::memory_order_relaxed) < lds) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<NB, S, XB>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    set.store(lds, std::memory_order_relaxed);
-  }
+  const hipError_t e = open_dynamic_lds(reinterpret_cast<const void*>(&k_gemm<NB, S, XB>), lds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_gemm<NB, S, XB>), dim3(grid), dim3(kGemmWaves * S * kWave), lds, s, L);
   return hipGetLastError();
 }

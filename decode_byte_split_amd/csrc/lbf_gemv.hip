@@ -28,7 +28,6 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <atomic>
 
 #include "lbf_device.h"
 #include "lbf_internal.h"
@@ -403,16 +402,11 @@ static uint32_t geometry(uint32_t T, uint32_t smax) {
 
 template <int B, int SMAX>
 static hipError_t run(GemvLaunch& L, hipStream_t s) {
-  static int per_cu = 0, cus = 0;
-  if (!per_cu) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return hipErrorUnknown;
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_gemv<B, SMAX>, kGemvWaves * kWave, 0) != hipSuccess || n < 1)
-      n = 1;
-    per_cu = n;
-  }
+  int per_cu = 0, cus = 0;
+  hipError_t e = device_cus(&cus);
+  if (e == hipSuccess)
+    e = blocks_per_cu(reinterpret_cast<const void*>(&k_gemv<B, SMAX>), kGemvWaves * kWave, &per_cu);
+  if (e != hipSuccess) return e;
   uint64_t units = 0;
   for (int g = 0; g < L.n_groups; g++) units += L.g[g].n_units;
   const uint64_t grid = std::min<uint64_t>((uint64_t)per_cu * cus, units);
@@ -786,17 +780,11 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
 template <int B, bool GATED = false>
 static hipError_t run_ring_kernel(RingLaunch& L, hipStream_t s) {
   constexpr int W = kRingWaves, C = kRingTiles, N = kRingSlots;
-  static std::atomic<int> ready{0};  // attribute set for this instance (per process)
   const uint32_t lds = kRingXMax + W * kTile + 16;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return hipErrorUnknown;
-  if (!ready.load(std::memory_order_acquire)) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_ring<B, W, GATED, C, N>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    ready.store(1, std::memory_order_release);
-  }
+  int cus = 0;
+  hipError_t e = device_cus(&cus);
+  if (e == hipSuccess) e = open_dynamic_lds(reinterpret_cast<const void*>(&k_gemv_ring<B, W, GATED, C, N>), (int)lds);
+  if (e != hipSuccess) return e;
   const uint32_t grid = (uint32_t)std::min<uint64_t>((uint64_t)cus, L.n_rows);
   hipLaunchKernelGGL((k_gemv_ring<B, W, GATED, C, N>), dim3(grid), dim3(W * kWave), lds, s, L);
   return hipGetLastError();

@@ -627,9 +627,8 @@ hipError_t launch_hpack(const lbf_desc& d, const uint8_t* blob, const HCode& cod
 hipError_t launch_hdecode(const lbf_hdesc& h, const HCode& code, const uint8_t* blob, uint16_t* out, hipStream_t s) {
   const HLayout L = hlayout_of(h.rows, h.cols, h.n_esc, h.stream_words);
   if (!L.n_tiles) return hipSuccess;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return hipErrorUnknown;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return hipErrorUnknown;
+  int cus = 0;
+  if (const hipError_t e = device_cus(&cus); e != hipSuccess) return e;
   const KLut k = klut_from(h.lut, h.n_codes);
   HDecArgs a;
   a.raw = blob + L.off_raw;
@@ -649,10 +648,9 @@ hipError_t launch_hdecode(const lbf_hdesc& h, const HCode& code, const uint8_t* 
   for (int c = 0; c < 16; c++) a.sym[c] = code.sym[c];
   // a persistent grid: exactly the workgroups that can be resident at once
   int per_cu = 0;
-  const hipError_t occ =
-      k.contiguous ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_hdecode<true>, kHDecWaves * kWave, 0)
-                   : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_hdecode<false>, kHDecWaves * kWave, 0);
-  if (occ != hipSuccess) return occ;
+  const void* fn = k.contiguous ? reinterpret_cast<const void*>(&k_hdecode<true>)
+                                : reinterpret_cast<const void*>(&k_hdecode<false>);
+  if (const hipError_t occ = blocks_per_cu(fn, kHDecWaves * kWave, &per_cu); occ != hipSuccess) return occ;
   const uint64_t blocks = std::min<uint64_t>((L.n_tiles + kHDecWaves - 1) / kHDecWaves,
                                              (uint64_t)std::max(cus, 1) * (uint64_t)std::max(per_cu, 1));
   a.waves = (uint32_t)(blocks * kHDecWaves);

@@ -81,4 +81,16 @@ constexpr uint32_t kGemmMaxTiles = 64;
 // Workspace layout of lbf_encode: hist[256] u32, then tile counts u32[n_tiles].
 constexpr uint64_t kWorkHistBytes = 1024;
 
+// Launch facts of the current device, looked up once per device and kept for
+// the process (thread-safe; lbf_api.cpp).
+// Compute units of the current device.
+hipError_t device_cus(int* cus);
+// Resident workgroups per CU of kernel `fn` at `block` threads and no dynamic
+// LDS on the current device (at least 1).
+hipError_t blocks_per_cu(const void* fn, int block, int* n);
+// Lets kernel `fn` take `bytes` of dynamic LDS on the current device: the
+// attribute only grows, so concurrent callers that need different sizes
+// never lower it under one another.
+hipError_t open_dynamic_lds(const void* fn, int bytes);
+
 }  // namespace lbf

@@ -197,13 +197,6 @@ __global__ __launch_bounds__(kVerifyWaves * kWave) void k_verify(VerifyArgs a) {
   report(a.flags, f);
 }
 
-static hipError_t device_cus(int* cus) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return hipErrorUnknown;
-  if (hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return hipErrorUnknown;
-  return hipSuccess;
-}
-
 // Waves for a launch: about `per` units of work each, at most 16 per CU, a
 // whole number of workgroups.
 static uint32_t launch_waves(uint64_t units, uint64_t per, int cus, int per_block) {

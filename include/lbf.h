@@ -39,7 +39,10 @@
  * Conventions for every call:
  *  - d_* arguments are device pointers (or host arrays of device pointers
  *    where the type says so); the caller allocates and owns all memory.  The
- *    library allocates no device memory and keeps no mutable global state.
+ *    library allocates no device memory and keeps no mutable global state
+ *    beyond per-device launch facts (CU count, resident workgroups, each
+ *    kernel's dynamic LDS limit), looked up once per device under a lock:
+ *    calls may be made from several threads and on several devices at once.
  *  - every call checks its arguments and descriptors on the host before it
  *    launches anything and returns a negative LBF_E_* status, with no side
  *    effect, when a check fails.  A failed launch returns LBF_E_HIP.
