@@ -100,7 +100,7 @@ READ_BYTES = 1 << 30  # the read-stream ceiling runs over 1 GiB
 
 def read_ceiling(torch, reps: int = 10, nbytes: int = READ_BYTES) -> float:
     """GB/s of a plain read stream (liblbf_measure.so: 128-bit non-temporal
-    loads, XOR-reduced) over nbytes (default 1 GiB: the practical ceiling for
+    loads, XOR-reduced, one stored word per workgroup) over nbytes (default 1 GiB: the practical ceiling for
     a kernel that only reads HBM).  Smaller reads rotate over enough buffers
     to keep the working set at 1 GiB or more, past the 256 MB cache."""
     import ctypes
@@ -111,8 +111,8 @@ def read_ceiling(torch, reps: int = 10, nbytes: int = READ_BYTES) -> float:
     nbytes = max(16, nbytes // 16 * 16)
     nbuf = -(-READ_BYTES // nbytes)
     bufs = [torch.ones(nbytes // 4, dtype=torch.float32, device="cuda") for _ in range(nbuf)]
-    out = torch.zeros(1, dtype=torch.int32, device="cuda")
     blocks = torch.cuda.get_device_properties(0).multi_processor_count  # one workgroup per CU
+    out = torch.zeros(blocks, dtype=torch.int32, device="cuda")  # one word per workgroup
     s = torch.cuda.current_stream().cuda_stream
 
     def run(i):
