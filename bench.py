@@ -309,7 +309,7 @@ def main():
         return layer_step_only(args)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the fused decode-GEMV has no cross-GPU step in this build "
+        print("bench.py measures one GPU: the fused decode-GEMV runs on one GPU and has no cross-GPU step "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 

@@ -90,7 +90,7 @@ enum {
   LBF_E_DESC = -4,        /* descriptor fails validation (corrupt or foreign) */
   LBF_E_CAPACITY = -5,    /* destination or workspace buffer too small */
   LBF_E_HIP = -6,         /* a HIP runtime call or launch failed */
-  LBF_E_UNSUPPORTED = -7  /* valid request this build does not handle */
+  LBF_E_UNSUPPORTED = -7  /* valid request the library does not handle */
 };
 
 enum { LBF_F32 = 0, LBF_BF16 = 1 }; /* output element types */

@@ -22,7 +22,7 @@
  *    table (sign 1, exponent 8, mantissa 7) and the order-0 entropy used as a
  *    lower bound for any code that stores each weight independently.
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *  - only the 8-bit exponent is coded; sign and mantissa stay in the raw
  *    plane, one byte per weight: weight i's byte holds its mantissa in bits
  *    7..1 and, in bit 0, the sign of its pair partner i ^ 1 (weights pair up
@@ -460,7 +460,7 @@ double lbfo_entropy_exponent(const uint16_t* w, uint64_t n) {
  * the 4-bit K15 code of every weight (codes 0..14 for the table's exponents,
  * 15 for an escape, exactly as above) is Huffman-coded; the raw plane, the
  * escape index and the escape stream are those of format v1.
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *  - symbol counts are over the n real weights (not the tile padding);
  *  - code lengths come from Huffman's procedure run with two queues: the used
  *    symbols sorted by count, then by symbol, and the merged nodes in the
