@@ -9,7 +9,7 @@
 // compression or Q8 GGUF: which should you deploy?", on fleets whose
 // bottleneck is weight bandwidth), so both kernels here are HBM streams:
 //
-//  * k_gemv_ring (x of every tensor of the call fits in 96 KiB of LDS): one
+//  * k_gemv_ring (x of every tensor of the call fits in 128 KiB of LDS): one
 //    workgroup per CU (16 waves), rows dealt to CUs, waves take
 //    rows from an LDS counter and stream them through a three-slot register
 //    ring (details at the kernel);
@@ -436,7 +436,7 @@ constexpr int kRingWaves = 16;  // waves per workgroup (4 per SIMD), every batch
 // the per-chunk scalar work grows faster than the extra loads in flight help.
 constexpr int kRingTiles = 4;
 constexpr int kRingSlots = 3;
-constexpr uint32_t kRingXMax = 98304;
+constexpr uint32_t kRingXMax = 131072;  // x area; with the wave slots 144 KiB of the 160 KiB LDS
 
 struct RingLaunch {
   GemvGroup g[LBF_MAX_GROUPS];          // cost_begin: first global row of the group

@@ -51,7 +51,7 @@ hipError_t launch_gemv(const GemvGroup* groups, int n_groups, int batch, int y_d
 hipError_t launch_gemm(const GemvGroup* groups, int n_groups, int batch, int y_dtype, hipStream_t s);
 // h = silu(gate x) * (up x), one launch; x (batch * cols bf16) must fit the
 // ring kernel's LDS x area.
-constexpr uint64_t kGatedMaxXBytes = 98304;
+constexpr uint64_t kGatedMaxXBytes = 131072;
 hipError_t launch_gemv_gated(const GemvGroup& gate, const GemvGroup& up, int batch, void* h, int h_dtype,
                              hipStream_t s);
 

@@ -169,7 +169,7 @@ int lbf_gemv(const lbf_desc* descs, const void* const* d_blobs, int n_groups, co
  *   d_x        device bf16 [batch, cols], 16-byte aligned; batch 1..8
  *   d_h        device [batch, rows], 4-byte aligned, element type h_dtype
  *              (LBF_F32, or LBF_BF16 rounded to nearest even); overwritten
- * Requires cols % 1024 == 0 (LBF_E_SHAPE) and batch * cols * 2 <= 98304 (x is
+ * Requires cols % 1024 == 0 (LBF_E_SHAPE) and batch * cols * 2 <= 131072 (x is
  * staged once in LDS; LBF_E_UNSUPPORTED otherwise).
  */
 int lbf_gemv_swiglu(const lbf_desc* gate_desc, const void* d_gate_blob, const lbf_desc* up_desc,

@@ -295,6 +295,30 @@ def test_gemv_tiny_groups_share_x(env, batch):
     check_product(ys[31], y_ref, a_ref, False)
 
 
+@pytest.mark.parametrize("batch,cols", [(2, 32768), (4, 16384), (8, 8192)])
+def test_gemv_x_at_the_lds_limit(env, batch, cols):
+    """One tensor whose x is exactly 128 KiB, the most the ring kernel
+    stages in LDS, and the same tensor grouped with a second one of 1024
+    columns (x no longer fits: the static kernel): both match the oracle."""
+    torch, lbf = env
+    rng = np.random.default_rng([97, batch])
+    W = synth.gaussian(rng, 24, cols, 0.02, 0.002, 100.0)
+    W2 = synth.gaussian(rng, 16, 1024, 0.02, 0.002, 100.0)
+    x = synth.activations(rng, batch, cols)
+    x2 = synth.activations(rng, batch, 1024)
+    say("gemv x at the LDS limit B=%d cols=%d" % (batch, cols))
+    b, b2 = lbf.from_host_blob(O.encode(W)), lbf.from_host_blob(O.encode(W2))
+    y_ref, a_ref = O.matvec(W, x)
+    y = lbf.gemv(b, dev(torch, x), lbf.LBF_F32)
+    torch.cuda.synchronize()
+    check_product(y, y_ref, a_ref, False)
+    ys = lbf.gemv([b, b2], [dev(torch, x), dev(torch, x2)], lbf.LBF_F32)
+    torch.cuda.synchronize()
+    check_product(ys[0], y_ref, a_ref, False)
+    y2_ref, a2_ref = O.matvec(W2, x2)
+    check_product(ys[1], y2_ref, a2_ref, False)
+
+
 @pytest.mark.parametrize("batch", [1, 4])
 def test_gemv_layer_twice_static_kernel(env, batch):
     """The layer's seven tensors twice in one call, each time with its own x

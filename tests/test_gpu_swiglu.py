@@ -48,6 +48,25 @@ def test_swiglu_small(env, batch, bf16_out):
     check_h(h, O.swiglu(G, U, x), bf16_out)
 
 
+def test_swiglu_x_at_the_lds_limit(env):
+    """x of exactly 128 KiB (batch 8 x 8192 columns), the largest the fused
+    launch stages in LDS, and one column more is refused."""
+    torch, lbf = env
+    rng = np.random.default_rng(96)
+    rows, cols = 40, 8192
+    G = synth.gaussian(rng, rows, cols, 1 / 90, 0.002, 50.0)
+    U = synth.gaussian(rng, rows, cols, 1 / 90, 0.002, 50.0)
+    x = synth.activations(rng, 8, cols)
+    gb, ub = lbf.encode(dev(torch, G)), lbf.encode(dev(torch, U))
+    h = lbf.swiglu(gb, ub, dev(torch, x), lbf.LBF_F32)
+    check_h(h, O.swiglu(G, U, x), False)
+    W2 = synth.gaussian(rng, 8, cols + 1024, 1 / 90, 0.002, 50.0)
+    b2 = lbf.encode(dev(torch, W2))
+    with pytest.raises(lbf.LbfError) as refused:
+        lbf.swiglu(b2, b2, dev(torch, synth.activations(rng, 8, cols + 1024)), lbf.LBF_F32)
+    assert refused.value.status == lbf.LBF_E_UNSUPPORTED
+
+
 def test_swiglu_one_hot_columns(env):
     torch, lbf = env
     rng = np.random.default_rng(96)
