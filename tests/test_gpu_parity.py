@@ -295,6 +295,30 @@ def test_gemv_tiny_groups_share_x(env, batch):
     check_product(ys[31], y_ref, a_ref, False)
 
 
+@pytest.mark.parametrize("batch", [1, 3, 8])
+def test_gemv_same_x_pointer_different_widths(env, batch):
+    """Two groups given the same x pointer with different column counts read
+    different [batch, cols] views of that memory (row stride = cols), so the
+    launcher must not stage them as one x; a third group shares the first
+    group's x exactly.  Every output matches the oracle on its own view."""
+    torch, lbf = env
+    rng = np.random.default_rng([98, batch])
+    Wa = synth.gaussian(rng, 37, 1024, 0.02, 0.002, 100.0)
+    Wb = synth.gaussian(rng, 29, 2048, 0.02, 0.002, 100.0)
+    Wc = synth.gaussian(rng, 18, 1024, 0.02, 0.002, 100.0)
+    flat = synth.activations(rng, 1, batch * 2048).reshape(-1)
+    xt = dev(torch, flat.reshape(batch, 2048))
+    xa = xt.view(-1)[: batch * 1024].view(batch, 1024)  # same pointer, 1024-column view
+    say("gemv same x pointer, widths 1024/2048, B=%d" % batch)
+    blobs = [lbf.from_host_blob(O.encode(W)) for W in (Wa, Wb, Wc)]
+    ys = lbf.gemv(blobs, [xa, xt, xa], lbf.LBF_F32)
+    torch.cuda.synchronize()
+    for W, y, x in ((Wa, ys[0], flat[: batch * 1024].reshape(batch, 1024)), (Wb, ys[1], flat.reshape(batch, 2048)),
+                    (Wc, ys[2], flat[: batch * 1024].reshape(batch, 1024))):
+        y_ref, a_ref = O.matvec(W, x)
+        check_product(y, y_ref, a_ref, False)
+
+
 @pytest.mark.parametrize("batch,cols", [(2, 32768), (4, 16384), (8, 8192)])
 def test_gemv_x_at_the_lds_limit(env, batch, cols):
     """One tensor whose x is exactly 128 KiB, the most the ring kernel
