@@ -14,7 +14,10 @@
 //              alignment gaps after the index and the escape stream
 //   k_escapes  one wave per tile with escapes: writes the tile's escape bytes
 //              at idx[t] + (rank among the tile's escapes), so the stream is in
-//              element order without atomics
+//              element order without atomics; positions at or past the
+//              descriptor's escape count are dropped, so weights that no longer
+//              match phase 1 can never write past the blob (the index then
+//              disagrees with the header and lbf_verify reports it)
 #include <hip/hip_runtime.h>
 
 #include "lbf_device.h"
@@ -172,6 +175,7 @@ struct EscArgs {
   const uint32_t* idx;
   uint8_t* esc;
   uint32_t n, n_tiles;
+  uint32_t n_esc;  // escape bytes the blob holds (from the phase-1 descriptor)
   uint32_t inv[64];
 };
 
@@ -190,7 +194,8 @@ __global__ __launch_bounds__(kEncWaves * kWave) void k_escapes(EscArgs a) {
   uint32_t j = first + wave_excl_scan_small((uint32_t)__builtin_popcount(esc_mask));
   while (esc_mask) {
     const uint32_t i = (uint32_t)__builtin_ctz(esc_mask);
-    a.esc[j++] = (uint8_t)((a.w[e0 + i] >> 7) & 0xFFu);
+    if (j < a.n_esc) a.esc[j] = (uint8_t)((a.w[e0 + i] >> 7) & 0xFFu);
+    j++;
     esc_mask &= esc_mask - 1;
   }
 }
@@ -232,6 +237,7 @@ hipError_t launch_pack(const uint16_t* w, const lbf_desc& d, uint8_t* blob, uint
     e.esc = blob + L.off_esc;
     e.n = (uint32_t)L.n;
     e.n_tiles = (uint32_t)L.n_tiles;
+    e.n_esc = (uint32_t)L.n_esc;
     for (int q = 0; q < 64; q++) e.inv[q] = p.inv[q];
     hipLaunchKernelGGL(k_escapes, dim3(grid), dim3(kEncWaves * kWave), 0, s, e);
   }

@@ -179,6 +179,25 @@ def _stream(stream=None) -> int:
     return int(s.cuda_stream)
 
 
+def _order_after_current(stream) -> None:
+    """Work this module enqueues on an explicit ``stream`` reads tensors that
+    were made (copies, fresh allocations) on the current stream: make
+    ``stream`` wait for everything enqueued there so far."""
+    if stream is not None:
+        torch = _torch()
+        cur = torch.cuda.current_stream(stream.device)
+        if cur != stream:
+            stream.wait_stream(cur)
+
+
+def _keep_for(stream, *tensors) -> None:
+    """Tensors used by work on an explicit ``stream`` stay allocated until
+    that work is done, whatever happens to them on the current stream."""
+    if stream is not None:
+        for t in tensors:
+            t.record_stream(stream)
+
+
 def _ptr(t) -> int:
     return int(t.data_ptr())
 
@@ -244,14 +263,14 @@ def encode(w, stream=None) -> Blob:
     s = _stream(stream)
     wb = int(L.lbf_encode_work_bytes(rows, cols))
     work = torch.empty(max(wb, 256), dtype=torch.uint8, device=w.device)
+    _order_after_current(stream)  # the contiguous copy and the workspace come from the current stream
     d = Desc()
     _check(L.lbf_encode(_ptr(w), rows, cols, _ptr(work), work.numel(), None, 0, ctypes.byref(d), s), "lbf_encode phase 1")
     blob = torch.empty(int(d.blob_bytes), dtype=torch.uint8, device=w.device)
+    _order_after_current(stream)
     _check(L.lbf_encode(_ptr(w), rows, cols, _ptr(work), work.numel(), _ptr(blob), blob.numel(), ctypes.byref(d), s),
            "lbf_encode phase 2")
-    if stream is not None:  # keep the workspace alive until the stream has used it
-        work.record_stream(stream)
-        blob.record_stream(stream)
+    _keep_for(stream, w, work, blob)
     return Blob(d, blob)
 
 
@@ -272,7 +291,9 @@ def decode(blob: Blob, out=None, stream=None):
         out = torch.empty((blob.rows, blob.cols), dtype=torch.bfloat16, device=blob.data.device)
     _check_blob(blob)
     _check_tensor(out, blob.rows * blob.cols, torch.bfloat16, "out")
+    _order_after_current(stream)
     _check(lib().lbf_decode(ctypes.byref(blob.desc), _ptr(blob.data), _ptr(out), _stream(stream)), "lbf_decode")
+    _keep_for(stream, out)
     return out
 
 
@@ -289,8 +310,10 @@ def swiglu(gate: Blob, up: Blob, x, h_dtype: int = LBF_F32, out=None, stream=Non
     _check_blob(gate)
     _check_blob(up)
     _check_tensor(out, batch * gate.rows, hdt, "out")
+    _order_after_current(stream)  # x may be a fresh contiguous copy
     _check(lib().lbf_gemv_swiglu(ctypes.byref(gate.desc), _ptr(gate.data), ctypes.byref(up.desc), _ptr(up.data),
                                  _ptr(x), batch, _ptr(out), h_dtype, _stream(stream)), "lbf_gemv_swiglu")
+    _keep_for(stream, x, out)
     return out
 
 
@@ -332,15 +355,15 @@ def hencode(blob: Blob, stream=None) -> HBlob:
     if wb == 0:
         raise LbfError(LBF_E_DESC, "lbf_hencode_work_bytes")
     work = torch.empty(wb, dtype=torch.uint8, device=blob.data.device)
+    _order_after_current(stream)
     h = HDesc()
     _check(L.lbf_hencode(ctypes.byref(blob.desc), _ptr(blob.data), _ptr(work), wb, None, 0, ctypes.byref(h), s),
            "lbf_hencode phase 1")
     out = torch.empty(int(h.blob_bytes), dtype=torch.uint8, device=blob.data.device)
+    _order_after_current(stream)
     _check(L.lbf_hencode(ctypes.byref(blob.desc), _ptr(blob.data), _ptr(work), wb, _ptr(out), out.numel(),
                          ctypes.byref(h), s), "lbf_hencode phase 2")
-    if stream is not None:
-        work.record_stream(stream)
-        out.record_stream(stream)
+    _keep_for(stream, work, out)
     return HBlob(h, out)
 
 
@@ -360,7 +383,9 @@ def hdecode(blob: HBlob, out=None, stream=None):
         out = torch.empty((blob.rows, blob.cols), dtype=torch.bfloat16, device=blob.data.device)
     _check_blob(blob)
     _check_tensor(out, blob.rows * blob.cols, torch.bfloat16, "out")
+    _order_after_current(stream)
     _check(lib().lbf_hdecode(ctypes.byref(blob.desc), _ptr(blob.data), _ptr(out), _stream(stream)), "lbf_hdecode")
+    _keep_for(stream, out)
     return out
 
 
@@ -383,7 +408,10 @@ def verify(blob: Blob, desc: Desc | None = None, stream=None) -> int:
     Waits for the stream."""
     torch = _torch()
     flags = torch.empty(1, dtype=torch.int32, device=blob.data.device)
+    _order_after_current(stream)
     verify_into(blob, flags, desc, stream)
+    if stream is not None:
+        stream.synchronize()
     return int(flags.item()) & 0xFFFFFFFF
 
 
@@ -403,7 +431,10 @@ def crc32(t, stream=None) -> int:
     if not t.is_cuda or not t.is_contiguous():
         raise ValueError("crc32 takes a contiguous tensor on the GPU")
     out = torch.empty(1, dtype=torch.int32, device=t.device)
+    _order_after_current(stream)
     crc32_into(t, out, stream)
+    if stream is not None:
+        stream.synchronize()
     return int(out.item()) & 0xFFFFFFFF
 
 
@@ -432,6 +463,10 @@ class Prepared:
             raise ValueError("one output per blob")
         for y, b in zip(outs, blobs):
             _check_tensor(y, batch * b.rows, tdt, "each output")
+        # x copies and fresh outputs were made on the current stream: the
+        # launch stream waits for them once, and keeps them while it uses them
+        _order_after_current(stream)
+        _keep_for(stream, *xs, *outs)
         self._keep = (list(blobs), xs, outs)
         self.outs = outs
         self._fn, self._what = fn, what

@@ -107,6 +107,11 @@ int lbf_desc_check(const lbf_desc* desc);
 
 /*
  * lbf_encode — code a BF16 tensor into a blob (two phases).
+ * The coding step of "Lossless LLM Weight Compression vs 8-bit GGUF", section
+ * "What did the GLM-5.2 experiment actually prove?": a histogram of the
+ * exponent field picks the symbols that get short fixed-width codes (here
+ * the 15 most frequent exponents, 4 bits each); every other exponent is sent
+ * verbatim through the escape stream, while sign and mantissa stay raw.
  *   d_w        device, bf16 bit patterns [rows, cols], row-major, 16-byte aligned
  *   d_work     device workspace of at least lbf_encode_work_bytes(rows, cols)
  *              bytes, 256-byte aligned; its contents on entry do not matter
@@ -117,7 +122,11 @@ int lbf_desc_check(const lbf_desc* desc);
  * Phase 2 (d_blob != NULL): writes the whole blob (header included) on `s`;
  *   desc must be the unchanged phase-1 result for the same d_w.  d_blob must
  *   be 256-byte aligned and blob_cap >= desc->blob_bytes (else
- *   LBF_E_CAPACITY).
+ *   LBF_E_CAPACITY).  Phase 2 never writes outside [d_blob, d_blob +
+ *   desc->blob_bytes): if d_w changed between the phases (more or fewer
+ *   escapes than desc->n_esc), the escape bytes past desc->n_esc are dropped
+ *   and the blob is not a valid coding — its index disagrees with the header,
+ *   which lbf_verify reports (LBF_VERIFY_INDEX).
  * Shapes: any rows, cols with rows * cols < 2^32 (LBF_E_SHAPE otherwise).
  */
 int lbf_encode(const void* d_w, uint64_t rows, uint64_t cols, void* d_work, uint64_t work_bytes,
@@ -125,6 +134,11 @@ int lbf_encode(const void* d_w, uint64_t rows, uint64_t cols, void* d_work, uint
 
 /*
  * lbf_decode — rebuild the exact BF16 tensor from a blob.
+ * Lossless means the decoded bits equal the source bits, and that is what
+ * this call delivers ("Lossless LLM Weight Compression vs 8-bit GGUF",
+ * section "What does 'lossless' mean for LLM weights?"): per weight, the
+ * exponent is lut[code] or, for code 15, the tile's next escape byte, and
+ * sign and mantissa come back from the raw byte.
  *   desc       host copy of the blob's header (checked with lbf_desc_check)
  *   d_blob     device, 256-byte aligned, desc->blob_bytes long
  *   d_w_out    device, bf16 [rows, cols], 16-byte aligned; fully overwritten
