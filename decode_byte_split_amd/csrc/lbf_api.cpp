@@ -233,7 +233,7 @@ static void fill_desc(const uint32_t hist[256], uint64_t rows, uint64_t cols, lb
 
 // Per-group kernel records for the product calls; checks every group.
 static int build_groups(const lbf_desc* descs, const void* const* d_blobs, int n_groups, const void* const* d_x,
-                        void* const* d_y, std::vector<GemvGroup>& out) {
+                        void* const* d_y, std::vector<GroupArg>& out) {
   if (!descs || !d_blobs || !d_x || !d_y || n_groups < 1) return LBF_E_INVAL;
   out.resize((size_t)n_groups);
   for (int g = 0; g < n_groups; g++) {
@@ -243,21 +243,14 @@ static int build_groups(const lbf_desc* descs, const void* const* d_blobs, int n
     if (!d_blobs[g] || !d_x[g] || !d_y[g]) return LBF_E_INVAL;
     if (!aligned(d_blobs[g], 256) || !aligned(d_x[g], 16) || !aligned(d_y[g], 4)) return LBF_E_ALIGN;
     if (d.rows == 0 || d.cols == 0 || d.cols % LBF_TILE != 0) return LBF_E_SHAPE;
-    const KLut k = klut_of(d);
-    GemvGroup& G = out[(size_t)g];
+    GroupArg& G = out[(size_t)g];
     G.blob = static_cast<const uint8_t*>(d_blobs[g]);
     G.x = static_cast<const uint16_t*>(d_x[g]);
     G.y = d_y[g];
     G.rows = (uint32_t)d.rows;
-    G.cols = (uint32_t)d.cols;
+    G.tiles = (uint32_t)(d.cols / LBF_TILE);
     G.n_esc = (uint32_t)d.n_esc;
-    for (int q = 0; q < 4; q++) G.lut[q] = k.t[q];
-    G.base4 = k.base4;
-    G.flags = k.contiguous ? 1u : 0u;
-    G.geom = 0;
-    G.cost_begin = 0;
-    G.unit_cost = 0;
-    G.n_units = 0;
+    G.aux = klut_of(d).contiguous ? kAuxContig : 0u;
   }
   return LBF_OK;
 }
@@ -463,12 +456,12 @@ static int product(bool mfma, const lbf_desc* descs, const void* const* d_blobs,
                    const void* const* d_x, int batch, void* const* d_y, int y_dtype, hipStream_t s) {
   if (y_dtype != LBF_F32 && y_dtype != LBF_BF16) return LBF_E_INVAL;
   if (mfma ? (batch < 9 || batch > 256) : (batch < 1 || batch > 8)) return LBF_E_INVAL;
-  std::vector<GemvGroup> groups;
+  std::vector<GroupArg> groups;
   const int rc = build_groups(descs, d_blobs, n_groups, d_x, d_y, groups);
   if (rc) return rc;
   if (mfma)
-    for (const GemvGroup& G : groups)
-      if (G.cols / LBF_TILE > kGemmMaxTiles) return LBF_E_UNSUPPORTED;
+    for (const GroupArg& G : groups)
+      if (G.tiles > kGemmMaxTiles) return LBF_E_UNSUPPORTED;
   for (int g0 = 0; g0 < n_groups; g0 += LBF_MAX_GROUPS) {
     const int cnt = std::min(LBF_MAX_GROUPS, n_groups - g0);
     const hipError_t e = mfma ? launch_gemm(groups.data() + g0, cnt, batch, y_dtype, s)
@@ -486,7 +479,7 @@ int lbf_gemv_swiglu(const lbf_desc* gate_desc, const void* d_gate_blob, const lb
   const void* blobs[2] = {d_gate_blob, d_up_blob};
   const void* xs[2] = {d_x, d_x};
   void* hs[2] = {d_h, d_h};
-  std::vector<GemvGroup> groups;
+  std::vector<GroupArg> groups;
   const int rc = build_groups(descs, blobs, 2, xs, hs, groups);
   if (rc) return rc;
   if (gate_desc->rows != up_desc->rows || gate_desc->cols != up_desc->cols) return LBF_E_SHAPE;

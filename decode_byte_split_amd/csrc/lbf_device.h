@@ -208,6 +208,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
 }
 
+// The code table of a blob, from its header copy (lut[16] at byte 72).  The
+// header does not change while a kernel runs, so it is read through the
+// constant address space: with a uniform blob pointer, one scalar load into
+// SGPRs and no vector registers.
+typedef __attribute__((address_space(4))) const u32x4 ConstU32x4;
+__device__ __forceinline__ Lut header_lut(const uint8_t* blob) {
+  const u32x4 h = *reinterpret_cast<ConstU32x4*>(reinterpret_cast<uintptr_t>(blob + 72));
+  return Lut{h.x, h.y, h.z, h.w};
+}
+
 // fp32 -> bf16, round to nearest even; NaN stays NaN (quiet, sign kept).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   const uint32_t u = __builtin_bit_cast(uint32_t, f);

@@ -64,12 +64,13 @@ constexpr uint32_t kOOB = 0x80000000u;         // a buffer offset past every ran
 constexpr uint32_t kFullXLds = 160 * 1024;     // LDS of one workgroup a CU
 
 struct GemmLaunch {
-  GemvGroup g[LBF_MAX_GROUPS];
+  GroupArg g[LBF_MAX_GROUPS];
   uint32_t wg_begin[LBF_MAX_GROUPS + 1];  // first workgroup of each group
   uint32_t idx_bytes;                     // LDS bytes per wave for index words
   uint32_t x_steps;                       // XB == 0: x buffers (steps) staged up front
   int n_groups, batch, y_bf16;
 };
+static_assert(sizeof(GemmLaunch) <= 3072, "kernel arguments stay well inside the 4 KiB limit");
 
 struct GSlot {
   u32x4 raw[4];
@@ -87,8 +88,11 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
 
   uint32_t g = 0;
   while (g + 1 < (uint32_t)L.n_groups && L.wg_begin[g + 1] <= blockIdx.x) g++;
-  const GemvGroup& G = L.g[g];
-  const uint32_t T = G.cols >> 10;
+  const GroupArg& G = L.g[g];
+  const uint32_t T = G.tiles;
+  const uint32_t cols = T << 10;
+  const Lut hl = header_lut(G.blob);  // the code table, from the blob's header copy
+  const uint32_t lut0 = hl.t0, lut1 = hl.t1, lut2 = hl.t2, lut3 = hl.t3;
   const uint64_t n_tiles = (uint64_t)G.rows * T;
   const Planes P = planes_of(G.blob, n_tiles);
   const uint32_t r0 = (blockIdx.x - L.wg_begin[g]) * kGemmRows + rb * 16u;
@@ -108,7 +112,7 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
   const uint32_t n_steps = 4 * ((T + S - 1) / S);
   const __amdgpu_buffer_rsrc_t rr = make_rsrc(P.raw + t_first * kTile, tiles_here * kTile);
   const __amdgpu_buffer_rsrc_t rn = make_rsrc(P.nib + t_first * (kTile / 2), tiles_here * (kTile / 2));
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(G.x, (uint32_t)L.batch * G.cols * 2);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(G.x, (uint32_t)L.batch * cols * 2);
 
   // coded chunks of step k: lane (li, lq), chunk j -> tile c = (k / 4) S + kh
   // of row li, 16-weight chunk 16 (k % 4) + 4 j + lq.  The lane part of the
@@ -135,7 +139,7 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
   // x of step k for every K part, loaded straight into LDS (no registers):
   // chunk P = 256 S m + threadIdx.x (16 bytes) is part h = P / (512 NB),
   // batch row (P / 32) % (16 NB) and slot s = P % 32 of that row, which holds
-  // column chunk s ^ (row & 7) of the step's 256 columns; one instruction
+  // column chunk s ^ (row & 15) of the step's 256 columns; one instruction
   // fills 64 consecutive slots.  A part past the row's tiles gets zeros.
   auto dma_x = [&](uint32_t k, uint32_t buf) {
 #pragma unroll
@@ -146,7 +150,7 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
       const uint32_t c = (k >> 2) * S + h;
       uint8_t* dst = xs + (buf * S + h) * kXBuf + (p0 % (512u * NB)) * 16u;
       if (c < T) {
-        const uint32_t vo = row * G.cols * 2 + (slot ^ (row & 15u)) * 16u;
+        const uint32_t vo = row * cols * 2 + (slot ^ (row & 15u)) * 16u;
         const uint32_t so = (c * kTile + (k & 3u) * kStepK) * 2;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)dst, 16, vo, so, 0, 0);
       } else {
@@ -203,7 +207,7 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
 
   // per tile: first escape (absolute), count, the lane's LUT word 3 and
   // whether any row of the wave needs ranked escapes
-  uint32_t t_ia = 0, t_cnt = 0, t3 = G.lut[3], run = 0;
+  uint32_t t_ia = 0, t_cnt = 0, t3 = lut3, run = 0;
   bool any_slow = false, fast = true;
   // The main loop, instantiated twice: waves whose escape slice fits in LDS
   // read escapes there only; the rest ("dense" slices) read them from
@@ -252,11 +256,11 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
         const uint32_t e1 = t_cnt ? esc_at(ia) : 0u;
         const uint32_t e2 = t_cnt > 1 ? esc_at(ia + 1) : e1;
         fast = t_cnt == 0 || (t_cnt <= 2 && e1 == e2);
-        t3 = fast ? ((G.lut[3] & 0x00FFFFFFu) | (e1 << 24)) : G.lut[3];
+        t3 = fast ? ((lut3 & 0x00FFFFFFu) | (e1 << 24)) : lut3;
         any_slow = __builtin_amdgcn_ballot_w64(!fast) != 0;
         run = 0;
       }
-      const Lut lut{G.lut[0], G.lut[1], G.lut[2], t3};
+      const Lut lut{lut0, lut1, lut2, t3};
       const uint8_t* xb = xs + ((XB ? k % (XB ? XB : 1) : k) * S + kh) * kXBuf + li * kXStride;
 #pragma unroll
       for (int j = 0; j < 4; j++) {
@@ -392,7 +396,7 @@ static hipError_t run_gemm(const GemmLaunch& L, uint32_t grid, hipStream_t s) {
 
 // Batch columns go in slabs of up to 64 (each slab re-reads the coded
 // weights); a slab of m columns runs ceil(m / 16) MFMA column blocks.
-hipError_t launch_gemm(const GemvGroup* groups, int n_groups, int batch, int y_dtype, hipStream_t s) {
+hipError_t launch_gemm(const GroupArg* groups, int n_groups, int batch, int y_dtype, hipStream_t s) {
   const uint32_t eb = y_dtype == LBF_BF16 ? 2u : 4u;
   for (int b0 = 0; b0 < batch; b0 += kGemmBatch) {
     const int nb = std::min(kGemmBatch, batch - b0);
@@ -402,15 +406,15 @@ hipError_t launch_gemm(const GemvGroup* groups, int n_groups, int batch, int y_d
     L.y_bf16 = y_dtype == LBF_BF16;
     uint32_t wg = 0, t_max = 1, t_min = kGemmMaxTiles;
     for (int g = 0; g < n_groups; g++) {
-      GemvGroup G = groups[g];
-      if ((G.cols >> 10) > kGemmMaxTiles) return hipErrorNotSupported;
-      G.x += (size_t)b0 * G.cols;
+      GroupArg G = groups[g];
+      if (G.tiles > kGemmMaxTiles) return hipErrorNotSupported;
+      G.x += (size_t)b0 * G.tiles * kTile;
       G.y = static_cast<uint8_t*>(G.y) + (size_t)b0 * G.rows * eb;
       L.g[g] = G;
       L.wg_begin[g] = wg;
       wg += (G.rows + kGemmRows - 1) / kGemmRows;
-      t_max = std::max(t_max, G.cols >> 10);
-      t_min = std::min(t_min, G.cols >> 10);
+      t_max = std::max(t_max, G.tiles);
+      t_min = std::min(t_min, G.tiles);
     }
     L.wg_begin[n_groups] = wg;
     L.idx_bytes = (4 * (16 * t_max + 1) + 15) & ~15u;

@@ -39,11 +39,41 @@ constexpr int kSubUnits = 64;     // units whose partial sums share one LDS batc
 constexpr int kEscShared = 8192;  // escape bytes a workgroup preloads per tensor range
 
 struct GemvLaunch {
-  GemvGroup g[LBF_MAX_GROUPS];
-  uint64_t total_cost;
+  GroupArg g[LBF_MAX_GROUPS];
+  uint64_t total_cost;  // sum over groups of n_units * unit_cost (unit_info)
   int n_groups;
   int y_bf16;
 };
+static_assert(sizeof(GemvLaunch) <= 3072, "kernel arguments stay well inside the 4 KiB limit");
+
+// Work units of one group in the static kernel: K slices (1, 2 or 4 per row,
+// each at most smax tiles per pass), row phases (waves per slice, 4 /
+// slices), units (phases consecutive rows, all K) and the cost of a unit in
+// 1/16 tiles: 16 per tile plus the escape work, ~1/8 per escape.  The
+// launcher puts log2(slices) and the per-tile cost factor into the record's
+// aux word (bits 16..17 and 8..15), from which host and device derive the
+// rest the same way.
+struct UnitInfo {
+  uint32_t nks, phases, n_units, unit_cost;
+};
+static uint32_t static_aux(const GroupArg& G, uint32_t smax) {
+  uint32_t lg = 0;
+  while ((1u << lg) < (uint32_t)kGemvWaves && (G.tiles + (1u << lg) - 1) >> lg > smax) lg++;
+  const uint64_t n_tiles = (uint64_t)G.rows * G.tiles;
+  const uint64_t ept = (G.n_esc + n_tiles - 1) / n_tiles;
+  const uint32_t f = 16u + (uint32_t)(ept < 1024 ? ept : 1024) / 8u;  // <= 144
+  return (G.aux & kAuxContig) | (f << 8) | (lg << 16);
+}
+__host__ __device__ inline UnitInfo unit_info(const GroupArg& G) {
+  UnitInfo u;
+  const uint32_t lg = (G.aux >> 16) & 3u;
+  u.nks = 1u << lg;
+  u.phases = (uint32_t)kGemvWaves >> lg;
+  u.n_units = (G.rows + u.phases - 1) >> (2u - lg);
+  u.unit_cost = u.phases * G.tiles * ((G.aux >> 8) & 0xFFu);
+  return u;
+}
+
 
 // Sum of v over the 64 lanes, the same value in every lane, in a fixed order.
 __device__ __forceinline__ float wave_sum(float v) {
@@ -270,11 +300,12 @@ __device__ __forceinline__ void run_rows(RowBuf<SMAX>& A, const uint8_t* raw_p, 
 
 // One workgroup's units [u_lo, u_hi) of group G.
 template <int B, int SMAX, bool CONTIG>
-__device__ __forceinline__ void run_segment(const GemvGroup& G, uint32_t u_lo, uint32_t u_hi, bool y_bf16,
-                                            float (*part)[kGemvWaves][B], uint8_t* esc_sh, uint8_t* esc_wave,
-                                            uint32_t wave, int lane) {
-  const uint32_t T = G.cols >> 10;
-  const uint32_t nks = G.geom & 0xFu, phases = (G.geom >> 4) & 0xFu;
+__device__ __forceinline__ void run_segment(const GroupArg& G, const UnitInfo& U, uint32_t u_lo, uint32_t u_hi,
+                                            bool y_bf16, float (*part)[kGemvWaves][B], uint8_t* esc_sh,
+                                            uint8_t* esc_wave, uint32_t wave, int lane) {
+  const uint32_t T = G.tiles;
+  const uint32_t cols = T << 10;
+  const uint32_t nks = U.nks, phases = U.phases;
   const uint32_t slice = wave % nks, phase = wave / nks;
   const uint64_t n_tiles = (uint64_t)G.rows * T;
   const uint8_t* raw_p = G.blob + LBF_HEADER_BYTES;
@@ -288,8 +319,8 @@ __device__ __forceinline__ void run_segment(const GemvGroup& G, uint32_t u_lo, u
   C.esc_p = esc_p;
   C.esc_sh = esc_sh;
   C.esc_wave = esc_wave;
-  C.lut = Lut{G.lut[0], G.lut[1], G.lut[2], G.lut[3]};
-  C.base4 = G.base4;
+  C.lut = header_lut(G.blob);
+  C.base4 = (C.lut.t0 & 0xFFu) * 0x01010101u;
   // escape range of the whole segment (scalar loads, waited for only after
   // the first row's loads are on their way)
   const uint32_t seg_hi = idx_p[(uint64_t)r_hi * T];
@@ -319,7 +350,7 @@ __device__ __forceinline__ void run_segment(const GemvGroup& G, uint32_t u_lo, u
         const uint32_t tj = tl + min((uint32_t)j, SL - 1);
 #pragma unroll
         for (int b = 0; b < B; b++) {
-          const u32x4* xp = reinterpret_cast<const u32x4*>(G.x + (size_t)b * G.cols + (size_t)tj * kTile) + lane * 2;
+          const u32x4* xp = reinterpret_cast<const u32x4*>(G.x + (size_t)b * cols + (size_t)tj * kTile) + lane * 2;
           const u32x4 a0 = xp[0], a1 = xp[1];
           xr[j][b][0] = a0.x; xr[j][b][1] = a0.y; xr[j][b][2] = a0.z; xr[j][b][3] = a0.w;
           xr[j][b][4] = a1.x; xr[j][b][5] = a1.y; xr[j][b][6] = a1.z; xr[j][b][7] = a1.w;
@@ -377,27 +408,24 @@ void k_gemv(GemvLaunch L) {
   // this workgroup's share of the total cost: units whose start cost is in [c_lo, c_hi)
   const uint64_t c_lo = L.total_cost * blockIdx.x / gridDim.x;
   const uint64_t c_hi = L.total_cost * (blockIdx.x + 1) / gridDim.x;
+  uint64_t g_lo = 0;  // cost of all earlier groups' units
   for (int gi = 0; gi < L.n_groups; gi++) {
-    const GemvGroup& G = L.g[gi];
-    const uint64_t g_lo = G.cost_begin, g_hi = G.cost_begin + (uint64_t)G.n_units * G.unit_cost;
-    if (g_hi <= c_lo) continue;
+    const GroupArg& G = L.g[gi];
+    const UnitInfo U = unit_info(G);
+    const uint64_t g_hi = g_lo + (uint64_t)U.n_units * U.unit_cost;
     if (g_lo >= c_hi) break;
-    const uint32_t u_lo = c_lo > g_lo ? (uint32_t)((c_lo - g_lo + G.unit_cost - 1) / G.unit_cost) : 0u;
-    const uint32_t u_hi = (uint32_t)min((uint64_t)G.n_units, (c_hi - g_lo + G.unit_cost - 1) / G.unit_cost);
-    if (u_lo >= u_hi) continue;
-    if (G.flags & 1u)
-      run_segment<B, SMAX, true>(G, u_lo, u_hi, L.y_bf16, part, esc_sh, esc_wave[wave], wave, lane);
-    else
-      run_segment<B, SMAX, false>(G, u_lo, u_hi, L.y_bf16, part, esc_sh, esc_wave[wave], wave, lane);
+    if (g_hi > c_lo) {
+      const uint32_t u_lo = c_lo > g_lo ? (uint32_t)((c_lo - g_lo + U.unit_cost - 1) / U.unit_cost) : 0u;
+      const uint32_t u_hi = (uint32_t)min((uint64_t)U.n_units, (c_hi - g_lo + U.unit_cost - 1) / U.unit_cost);
+      if (u_lo < u_hi) {
+        if (G.aux & kAuxContig)
+          run_segment<B, SMAX, true>(G, U, u_lo, u_hi, L.y_bf16, part, esc_sh, esc_wave[wave], wave, lane);
+        else
+          run_segment<B, SMAX, false>(G, U, u_lo, u_hi, L.y_bf16, part, esc_sh, esc_wave[wave], wave, lane);
+      }
+    }
+    g_lo = g_hi;
   }
-}
-
-// Unit geometry of one group: K slices (1, 2 or 4 per row, each at most
-// smax tiles per pass) and row phases (waves per slice, 4 / slices).
-static uint32_t geometry(uint32_t T, uint32_t smax) {
-  uint32_t nks = 1;
-  while (nks < (uint32_t)kGemvWaves && (T + nks - 1) / nks > smax) nks *= 2;
-  return nks | ((kGemvWaves / nks) << 4);
 }
 
 template <int B, int SMAX>
@@ -408,7 +436,7 @@ static hipError_t run(GemvLaunch& L, hipStream_t s) {
     e = blocks_per_cu(reinterpret_cast<const void*>(&k_gemv<B, SMAX>), kGemvWaves * kWave, &per_cu);
   if (e != hipSuccess) return e;
   uint64_t units = 0;
-  for (int g = 0; g < L.n_groups; g++) units += L.g[g].n_units;
+  for (int g = 0; g < L.n_groups; g++) units += unit_info(L.g[g]).n_units;
   const uint64_t grid = std::min<uint64_t>((uint64_t)per_cu * cus, units);
   hipLaunchKernelGGL((k_gemv<B, SMAX>), dim3((unsigned)grid), dim3(kGemvWaves * kWave), 0, s, L);
   return hipGetLastError();
@@ -416,7 +444,7 @@ static hipError_t run(GemvLaunch& L, hipStream_t s) {
 
 // ---- Ring GEMV (x of every tensor fits in LDS) ------------------------------
 //
-// The fastest form, used for batch 1..4 when x of every tensor of the call
+// The fastest form, used for batch 1..8 when x of every tensor of the call
 // fits in LDS.  One 1024-thread workgroup per CU.  The unit of work is one
 // row; rows of all tensors are dealt to the CUs cyclically (CU w takes rows
 // w, w + #CUs, ...), so every CU gets the same mix, and inside a CU the 16
@@ -438,14 +466,19 @@ constexpr int kRingTiles = 4;
 constexpr int kRingSlots = 3;
 constexpr uint32_t kRingXMax = 131072;  // x area; with the wave slots 144 KiB of the 160 KiB LDS
 
+// Ring launch: the group records, rows dealt in record order (the launcher
+// puts the longest rows first).  In each record's aux word, bit 1 marks the
+// first group of each distinct x array (staged once) and bits 8..31 hold the
+// LDS byte offset of the group's x.
+constexpr uint32_t kAuxStageX = 2u;
 struct RingLaunch {
-  GemvGroup g[LBF_MAX_GROUPS];          // cost_begin: first global row of the group
-  uint32_t x_off[LBF_MAX_GROUPS];       // LDS offset of each group's x
-  uint32_t xsrc_group[LBF_MAX_GROUPS];  // groups whose x arrays are staged (distinct pointers)
-  uint32_t n_rows, n_xsrc;
+  GroupArg g[LBF_MAX_GROUPS];
+  uint32_t n_rows;
   int n_groups, y_bf16;
   void* h;  // gated product (g[0] = gate, g[1] = up): h[b, r] = silu(gate) * up
 };
+static_assert(sizeof(RingLaunch) <= 3072, "kernel arguments stay well inside the 4 KiB limit");
+static_assert(LBF_MAX_GROUPS <= 64, "the ring kernel keeps one group per lane");
 
 template <int C>
 struct Slot {
@@ -461,37 +494,42 @@ struct Pos {
   bool valid;
 };
 
-__device__ __forceinline__ Planes ptrs_of(const GemvGroup& G) {
-  return planes_of(G.blob, (uint64_t)G.rows * (G.cols >> 10));
+__device__ __forceinline__ Planes ptrs_of(const GroupArg& G) {
+  return planes_of(G.blob, (uint64_t)G.rows * G.tiles);
 }
 
-// Group table in two VGPRs, lane g for group g (loaded once per kernel):
-// first global row (all ones past the last group) and tiles per row.
-struct GroupRegs {
-  uint32_t first_row, tiles;
-};
+// Group table in one VGPR, lane g for group g (built once per kernel): the
+// group's first global row (an exclusive prefix sum of the groups' rows) in
+// bits 6..31 and its tiles per row minus one in bits 0..5; all ones past the
+// last group.  The ring launcher guarantees tiles <= 64 (x fits in LDS) and
+// fewer than 2^26 rows.
+constexpr uint32_t kRingMaxRows = 1u << 26;
 
-__device__ __forceinline__ GroupRegs group_regs(const RingLaunch& L, int lane) {
-  GroupRegs v;
+__device__ __forceinline__ uint32_t group_regs(const RingLaunch& L, int lane) {
   const bool in = lane < L.n_groups;
-  const GemvGroup& G = L.g[in ? lane : 0];
-  v.first_row = in ? (uint32_t)G.cost_begin : ~0u;
-  v.tiles = G.cols >> 10;
-  return v;
+  const GroupArg& G = L.g[in ? lane : 0];
+  uint32_t pre = in ? G.rows : 0u;  // inclusive scan over the lanes, then minus own
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const uint32_t o = (uint32_t)__shfl_up((int)pre, (unsigned)d, kWave);
+    pre += lane >= d ? o : 0u;
+  }
+  return in ? ((pre - G.rows) << 6) | (G.tiles - 1u) : ~0u;
 }
 
 // Unit q of the launch: a row of one group, or (GATED) row q of the gate
 // tensor followed by row q of the up tensor.  The group is the last one whose
 // first row is at or before q (a ballot over the group table, no memory).
 template <bool GATED, int C>
-__device__ __forceinline__ Pos row_pos(const RingLaunch& L, const GroupRegs& GR, uint32_t q) {
+__device__ __forceinline__ Pos row_pos(const RingLaunch& L, uint32_t GR, uint32_t q) {
   Pos p;
   p.valid = q < L.n_rows;
   const uint32_t qq = p.valid ? q : L.n_rows - 1;
-  const uint32_t g = GATED ? 0u : (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(GR.first_row <= qq)) - 1u;
+  const uint32_t g = GATED ? 0u : (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64((GR >> 6) <= qq)) - 1u;
+  const uint32_t e = GATED ? 0u : (uint32_t)__builtin_amdgcn_readlane((int)GR, (int)g);
   p.g = g;
-  p.r = GATED ? qq : qq - (uint32_t)__builtin_amdgcn_readlane((int)GR.first_row, (int)g);
-  p.T = GATED ? L.g[0].cols >> 10 : (uint32_t)__builtin_amdgcn_readlane((int)GR.tiles, (int)g);
+  p.r = GATED ? qq : qq - (e >> 6);
+  p.T = GATED ? L.g[0].tiles : (e & 63u) + 1u;
   p.c = 0;
   p.S = p.valid ? min((uint32_t)C, p.T) : 0u;
   return p;
@@ -510,7 +548,7 @@ __device__ __forceinline__ void load_idx(Slot<C>& s, const RingLaunch& L, const 
 template <int C>
 __device__ __forceinline__ void load_data(Slot<C>& s, const RingLaunch& L, const Pos& p, uint32_t& e_first,
                                           uint32_t& e_cnt, int lane) {
-  const GemvGroup& G = L.g[p.g];
+  const GroupArg& G = L.g[p.g];
   const Planes P = ptrs_of(G);
   const uint32_t hi = min((uint32_t)__builtin_amdgcn_readlane((int)s.idxv, (int)p.S), G.n_esc);
   e_first = min((uint32_t)__builtin_amdgcn_readlane((int)s.idxv, 0), hi);
@@ -530,20 +568,18 @@ __device__ __forceinline__ void load_data(Slot<C>& s, const RingLaunch& L, const
 // Exponent bytes of tile j of a chunk; the chunk's escapes are in escv (and,
 // for the patch path, in the wave's LDS slot) unless the chunk holds more
 // than 64 of them (dense: each tile's slice is staged from memory).
-__device__ __forceinline__ void ring_exponents(u32x2 nib, const GemvGroup& G, uint32_t ia, uint32_t ib, uint32_t escv,
-                                               uint32_t e_first, uint32_t e_cnt, const uint8_t* esc_p, uint8_t* slot,
-                                               uint32_t E[4]) {
-  const Lut lut{G.lut[0], G.lut[1], G.lut[2], G.lut[3]};
-  const bool contig = G.flags & 1u;
+__device__ __forceinline__ void ring_exponents(u32x2 nib, const Lut& lut, uint32_t base4, bool contig, uint32_t n_esc,
+                                               uint32_t ia, uint32_t ib, uint32_t escv, uint32_t e_first,
+                                               uint32_t e_cnt, const uint8_t* esc_p, uint8_t* slot, uint32_t E[4]) {
   const bool dense = e_cnt > 64u;
-  const uint32_t lo = dense ? 0u : e_first, hi = dense ? G.n_esc : e_first + e_cnt;
+  const uint32_t lo = dense ? 0u : e_first, hi = dense ? n_esc : e_first + e_cnt;
   const uint32_t first = min(max(ia, lo), hi);
   const uint32_t cnt = min(min(max(ib, first), hi) - first, (uint32_t)kTile);
   if (cnt == 0) {
     if (contig)
-      exponents16<true>(nib, lut, G.base4, E);
+      exponents16<true>(nib, lut, base4, E);
     else
-      exponents16<false>(nib, lut, G.base4, E);
+      exponents16<false>(nib, lut, base4, E);
     return;
   }
   if (!dense) {
@@ -552,14 +588,14 @@ __device__ __forceinline__ void ring_exponents(u32x2 nib, const GemvGroup& G, ui
     const uint32_t e2 = cnt == 2 ? (uint32_t)__builtin_amdgcn_readlane((int)escv, (int)min(o + 1, 63u)) : e1;
     if (cnt <= 2 && e1 == e2) {
       const Lut L2{lut.t0, lut.t1, lut.t2, (lut.t3 & 0x00FFFFFFu) | (e1 << 24)};
-      exponents16<false>(nib, L2, G.base4, E);
+      exponents16<false>(nib, L2, base4, E);
       return;
     }
   }
   if (contig)
-    exponents16<true>(nib, lut, G.base4, E);
+    exponents16<true>(nib, lut, base4, E);
   else
-    exponents16<false>(nib, lut, G.base4, E);
+    exponents16<false>(nib, lut, base4, E);
   if (!dense) {
     uint64_t m0, m1;
     const uint32_t rk = escape_rank(nib, m0, m1);
@@ -588,7 +624,7 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const uint32_t wave = uniform(threadIdx.x >> 6);
   const int lane = lane_id();
-  const GroupRegs GR = GATED ? GroupRegs{0u, 0u} : group_regs(L, lane);  // the gated launch has one row space
+  const uint32_t GR = GATED ? 0u : group_regs(L, lane);  // the gated launch has one row space
   uint8_t* slot_lds = smem + kRingXMax + wave * kTile;
   uint32_t* lctr = reinterpret_cast<uint32_t*>(smem + kRingXMax + W * kTile);
 
@@ -644,10 +680,11 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
   for (int i = 0; i < N - 2; i++) load_data(sl[i], L, pp[i], ef[i], en[i], lane);
   // stage every distinct x array while the first loads are in flight:
   // element (b, t, lane, half) at x_off + ((b*T + t)*2 + half)*1024 + lane*16
-  for (uint32_t k = 0; k < L.n_xsrc; k++) {
-    const GemvGroup& G = L.g[L.xsrc_group[k]];
-    const uint32_t T = G.cols >> 10;
-    uint8_t* xd = smem + L.x_off[L.xsrc_group[k]];
+  for (int k = 0; k < L.n_groups; k++) {
+    const GroupArg& G = L.g[k];
+    if (!(G.aux & kAuxStageX)) continue;
+    const uint32_t T = G.tiles;
+    uint8_t* xd = smem + (G.aux >> 8);
     const uint32_t nx = (uint32_t)B * T * kWave * 2;
     for (uint32_t i = threadIdx.x; i < nx; i += W * kWave) {
       const uint32_t half = i & 1u, ln = (i >> 1) & 63u, bt = i >> 7;
@@ -673,9 +710,11 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
     Slot<C>& cur = sl[K];
     const Pos& p0 = pp[K];
     const uint32_t f0 = ef[K], n0 = en[K];
-    const GemvGroup& G = L.g[p0.g];
+    const GroupArg& G = L.g[p0.g];
     const Planes P = ptrs_of(G);
-    const uint8_t* x_g = smem + L.x_off[p0.g];
+    const uint8_t* x_g = smem + (G.aux >> 8);
+    const Lut lut = header_lut(G.blob);
+    const uint32_t base4 = (lut.t0 & 0xFFu) * 0x01010101u;
     slot_lds[lane] = (uint8_t)cur.escv;  // the chunk's escapes, for the patch path
     wave_lds_sync();
     // bit j: the index gives tile j escapes (lane j compares idx[t0 + j] with
@@ -683,7 +722,7 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
     // escapes decode with no per-tile scalar work
     const uint32_t idx_up = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)cur.idxv, 0x101, 0xF, 0xF, false);
     const uint64_t esc_tiles = __builtin_amdgcn_ballot_w64((uint32_t)lane < p0.S && idx_up != cur.idxv);
-    const bool contig = G.flags & 1u;
+    const bool contig = G.aux & kAuxContig;
 #pragma unroll
     for (int j = 0; j < C; j++) {
       if ((uint32_t)j < p0.S) {
@@ -704,11 +743,11 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
         if ((esc_tiles >> j) & 1u) {
           const uint32_t ia = (uint32_t)__builtin_amdgcn_readlane((int)cur.idxv, j);
           const uint32_t ib = (uint32_t)__builtin_amdgcn_readlane((int)cur.idxv, j + 1);
-          ring_exponents(cur.nib[j], G, ia, ib, cur.escv, f0, n0, P.esc, slot_lds, E);
+          ring_exponents(cur.nib[j], lut, base4, contig, G.n_esc, ia, ib, cur.escv, f0, n0, P.esc, slot_lds, E);
         } else if (contig) {
-          exponents16<true>(cur.nib[j], Lut{G.lut[0], G.lut[1], G.lut[2], G.lut[3]}, G.base4, E);
+          exponents16<true>(cur.nib[j], lut, base4, E);
         } else {
-          exponents16<false>(cur.nib[j], Lut{G.lut[0], G.lut[1], G.lut[2], G.lut[3]}, G.base4, E);
+          exponents16<false>(cur.nib[j], lut, base4, E);
         }
         uint32_t w[8];
         assemble16(cur.raw[j], E, w);
@@ -790,17 +829,15 @@ static hipError_t run_ring_kernel(RingLaunch& L, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_gemv_gated(const GemvGroup& gate, const GemvGroup& up, int batch, void* h, int h_dtype,
+hipError_t launch_gemv_gated(const GroupArg& gate, const GroupArg& up, int batch, void* h, int h_dtype,
                              hipStream_t s) {
   static_assert(kGatedMaxXBytes == kRingXMax, "the gated launch stages x in the ring kernel's LDS area");
-  if ((uint64_t)batch * gate.cols * 2 > kRingXMax) return hipErrorInvalidValue;  // x must fit in LDS
+  if ((uint64_t)batch * gate.tiles * kTile * 2 > kRingXMax) return hipErrorInvalidValue;  // x must fit in LDS
   RingLaunch L;
   L.g[0] = gate;
   L.g[1] = up;
-  L.g[0].cost_begin = L.g[1].cost_begin = 0;
-  L.x_off[0] = L.x_off[1] = 0;
-  L.xsrc_group[0] = 0;  // one x for both
-  L.n_xsrc = 1;
+  L.g[0].aux = (gate.aux & kAuxContig) | kAuxStageX;  // one x for both, at LDS offset 0
+  L.g[1].aux = up.aux & kAuxContig;
   L.n_rows = gate.rows;
   L.n_groups = 2;
   L.y_bf16 = h_dtype == LBF_BF16;
@@ -818,38 +855,35 @@ hipError_t launch_gemv_gated(const GemvGroup& gate, const GemvGroup& up, int bat
 }
 
 // Ring path if x of all groups (distinct arrays) fits in LDS.
-static hipError_t launch_ring(const GemvGroup* groups, int n_groups, int batch, int y_dtype, bool& used,
+static hipError_t launch_ring(const GroupArg* groups, int n_groups, int batch, int y_dtype, bool& used,
                               hipStream_t s) {
   used = false;
   RingLaunch L;
-  uint32_t x_bytes = 0;
-  L.n_xsrc = 0;
+  uint64_t x_bytes = 0;  // 64-bit: batch * cols * 2 can pass 2^32 for one very wide row
   uint64_t rows = 0;
   // longest rows first: rows are handed out in this order, so the coarsest
   // units are taken early and the last ones are the shortest
   int order[LBF_MAX_GROUPS];
   for (int g = 0; g < n_groups; g++) order[g] = g;
-  std::stable_sort(order, order + n_groups, [&](int a, int b) { return groups[a].cols > groups[b].cols; });
+  std::stable_sort(order, order + n_groups, [&](int a, int b) { return groups[a].tiles > groups[b].tiles; });
   for (int g = 0; g < n_groups; g++) {
-    const GemvGroup& G = groups[order[g]];
-    int same = -1;
-    for (uint32_t k = 0; k < L.n_xsrc; k++) {
-      const GemvGroup& H = L.g[L.xsrc_group[k]];
-      if (H.x == G.x && H.cols == G.cols) same = (int)L.xsrc_group[k];
-    }
-    if (same >= 0) {
-      L.x_off[g] = L.x_off[same];
-    } else {
-      L.x_off[g] = x_bytes;
-      L.xsrc_group[L.n_xsrc++] = (uint32_t)g;
-      x_bytes += (uint32_t)batch * G.cols * 2;
-      if (x_bytes > kRingXMax) return hipSuccess;
-    }
+    const GroupArg& G = groups[order[g]];
+    int same = -1;  // an earlier group with the same x array (pointer and width)
+    for (int k = 0; k < g && same < 0; k++)
+      if ((L.g[k].aux & kAuxStageX) && L.g[k].x == G.x && L.g[k].tiles == G.tiles) same = k;
     L.g[g] = G;
-    L.g[g].cost_begin = rows;
+    L.g[g].aux = G.aux & kAuxContig;
+    if (same >= 0) {
+      L.g[g].aux |= L.g[same].aux & ~0xFFu;
+    } else {
+      const uint64_t xb = (uint64_t)batch * G.tiles * kTile * 2;
+      if (x_bytes + xb > kRingXMax) return hipSuccess;
+      L.g[g].aux |= kAuxStageX | (uint32_t)(x_bytes << 8);
+      x_bytes += xb;
+    }
     rows += G.rows;
   }
-  if (rows >= (1ull << 31)) return hipSuccess;
+  if (rows >= kRingMaxRows) return hipSuccess;
   L.n_rows = (uint32_t)rows;
   L.n_groups = n_groups;
   L.y_bf16 = y_dtype == LBF_BF16;
@@ -867,7 +901,7 @@ static hipError_t launch_ring(const GemvGroup* groups, int n_groups, int batch, 
   }
 }
 
-hipError_t launch_gemv(const GemvGroup* groups, int n_groups, int batch, int y_dtype, hipStream_t s) {
+hipError_t launch_gemv(const GroupArg* groups, int n_groups, int batch, int y_dtype, hipStream_t s) {
   bool used = false;
   const hipError_t e = launch_ring(groups, n_groups, batch, y_dtype, used, s);
   if (used || e != hipSuccess) return e;
@@ -879,25 +913,17 @@ hipError_t launch_gemv(const GemvGroup* groups, int n_groups, int batch, int y_d
   // otherwise (a 14-tile down_proj is faster with two)
   static const int smax_of[9] = {0, 2, 2, 2, 2, 1, 1, 1, 1};
   uint32_t t_max = 0;
-  for (int g = 0; g < n_groups; g++) t_max = std::max(t_max, groups[g].cols >> 10);
+  for (int g = 0; g < n_groups; g++) t_max = std::max(t_max, groups[g].tiles);
   const uint32_t smax = batch == 4 && t_max <= 4 ? 1u : (uint32_t)smax_of[batch];
   GemvLaunch L;
   L.n_groups = n_groups;
   L.y_bf16 = y_dtype == LBF_BF16;
   uint64_t cost = 0;
   for (int g = 0; g < n_groups; g++) {
-    GemvGroup G = groups[g];
-    const uint32_t T = G.cols >> 10;
-    G.geom = geometry(T, smax);
-    const uint32_t phases = (G.geom >> 4) & 0xFu;
-    G.n_units = (G.rows + phases - 1) / phases;
-    // cost of a tile in 1/16 units: 16 plus the escape work, ~1/8 per escape
-    const uint64_t n_tiles = (uint64_t)G.rows * T;
-    const uint32_t esc_per_tile = (uint32_t)std::min<uint64_t>(1024, (G.n_esc + n_tiles - 1) / n_tiles);
-    G.unit_cost = phases * T * (16u + esc_per_tile / 8u);
-    G.cost_begin = cost;
-    cost += (uint64_t)G.n_units * G.unit_cost;
-    L.g[g] = G;
+    L.g[g] = groups[g];
+    L.g[g].aux = static_aux(groups[g], smax);
+    const UnitInfo U = unit_info(L.g[g]);
+    cost += (uint64_t)U.n_units * U.unit_cost;
   }
   L.total_cost = cost;
   switch (batch) {

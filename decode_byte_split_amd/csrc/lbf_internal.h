@@ -34,25 +34,30 @@ hipError_t launch_crc32(const uint8_t* data, uint64_t n, uint32_t* crc, hipStrea
 hipError_t launch_hist(const uint16_t* w, uint64_t n, uint32_t* hist, hipStream_t s);
 hipError_t launch_pack(const uint16_t* w, const lbf_desc& d, uint8_t* blob, uint32_t* tile_cnt, hipStream_t s);
 
-struct GemvGroup {
+// Per-tensor record of a product launch (40 bytes, 64 per launch): the three
+// pointers and one 16-byte word of geometry taken from the host-checked
+// descriptor, so every bound a kernel uses comes from a validated source.
+// The code table is not here: each kernel reads it from the blob's own
+// header copy (bytes 72..87), where a corrupt value can only give wrong
+// weights, never an access outside the blob.
+struct GroupArg {
   const uint8_t* blob;
   const uint16_t* x;
   void* y;
-  uint32_t rows, cols, n_esc;
-  uint32_t flags;  // bit 0: contiguous table (lut[c] = lut[0] + c)
-  uint32_t lut[4];
-  uint32_t base4;       // lut[0] * 0x01010101
-  uint32_t geom;        // set by the launcher: K slices (bits 0..3) | row phases (bits 4..7)
-  uint64_t cost_begin;  // set by the launcher: cost of all earlier groups' units
-  uint32_t unit_cost;   // set by the launcher: cost of one unit of this group
-  uint32_t n_units;     // set by the launcher
+  uint32_t rows;
+  uint32_t tiles;  // cols / 1024
+  uint32_t n_esc;
+  uint32_t aux;    // bit 0: contiguous table (lut[c] = lut[0] + c); the rest is launcher-specific
 };
-hipError_t launch_gemv(const GemvGroup* groups, int n_groups, int batch, int y_dtype, hipStream_t s);
-hipError_t launch_gemm(const GemvGroup* groups, int n_groups, int batch, int y_dtype, hipStream_t s);
+static_assert(sizeof(GroupArg) == 40, "group record");
+constexpr uint32_t kAuxContig = 1u;
+
+hipError_t launch_gemv(const GroupArg* groups, int n_groups, int batch, int y_dtype, hipStream_t s);
+hipError_t launch_gemm(const GroupArg* groups, int n_groups, int batch, int y_dtype, hipStream_t s);
 // h = silu(gate x) * (up x), one launch; x (batch * cols bf16) must fit the
 // ring kernel's LDS x area.
 constexpr uint64_t kGatedMaxXBytes = 131072;
-hipError_t launch_gemv_gated(const GemvGroup& gate, const GemvGroup& up, int batch, void* h, int h_dtype,
+hipError_t launch_gemv_gated(const GroupArg& gate, const GroupArg& up, int batch, void* h, int h_dtype,
                              hipStream_t s);
 
 // K15H (entropy-coded variant): layout, code, and launchers (lbf_huff.hip).

@@ -29,7 +29,7 @@ LBF_E_UNSUPPORTED = -7
 LBF_F32 = 0
 LBF_BF16 = 1
 TILE = 1024
-MAX_GROUPS = 32
+MAX_GROUPS = 64
 
 
 class Desc(ctypes.Structure):

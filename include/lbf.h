@@ -66,7 +66,7 @@ extern "C" {
 #define LBF_TILE_LOG2 10
 #define LBF_TILE 1024
 #define LBF_HEADER_BYTES 256
-#define LBF_MAX_GROUPS 32 /* groups per kernel launch; larger calls are split */
+#define LBF_MAX_GROUPS 64 /* groups per kernel launch; larger calls are split */
 
 /* Host copy of a blob's header; byte-for-byte the first 96 bytes of the blob. */
 typedef struct lbf_desc {
@@ -163,6 +163,11 @@ int lbf_decode(const lbf_desc* desc, const void* d_blob, void* d_w_out, hipStrea
  * Requires cols_g % 1024 == 0 (LBF_E_SHAPE otherwise).  n_groups >= 1; calls
  * with more than LBF_MAX_GROUPS groups are issued as several launches.
  * Every group runs in the same launch when n_groups <= LBF_MAX_GROUPS.
+ * A launch passes each kernel 40 bytes per group (blob, x and y pointers and
+ * the checked rows, tiles and escape count); every workgroup takes the code
+ * table from the blob's own header copy, so the device header must equal
+ * descs[g] (as lbf_encode writes it; lbf_verify checks it).  A device header
+ * that differs can give wrong outputs but no access outside the buffers.
  */
 int lbf_gemv(const lbf_desc* descs, const void* const* d_blobs, int n_groups, const void* const* d_x,
              int batch, void* const* d_y, int y_dtype, hipStream_t s);
