@@ -283,8 +283,8 @@ uint64_t lbf_encode_work_bytes(uint64_t rows, uint64_t cols) {
 
 int lbf_desc_check(const lbf_desc* desc) { return check(desc); }
 
-int lbf_encode(const void* d_w, uint64_t rows, uint64_t cols, void* d_work, uint64_t work_bytes, void* d_blob,
-               uint64_t blob_cap, lbf_desc* desc, hipStream_t s) {
+static int encode(const void* d_w, uint64_t rows, uint64_t cols, void* d_work, uint64_t work_bytes, void* d_blob,
+                  uint64_t blob_cap, lbf_desc* desc, hipStream_t s) {
   if (!desc || !d_work) return LBF_E_INVAL;
   if (!shape_ok(rows, cols)) return LBF_E_SHAPE;
   const uint64_t n = rows * cols;
@@ -317,6 +317,21 @@ int lbf_encode(const void* d_w, uint64_t rows, uint64_t cols, void* d_work, uint
   if (launch_pack(static_cast<const uint16_t*>(d_w), *desc, static_cast<uint8_t*>(d_blob), tile_cnt, s) != hipSuccess)
     return LBF_E_HIP;
   return LBF_OK;
+}
+
+int lbf_encode(const void* d_w, uint64_t rows, uint64_t cols, void* d_work, uint64_t work_bytes, void* d_blob,
+               uint64_t blob_cap, lbf_desc* desc, hipStream_t s) {
+  return encode(d_w, rows, cols, d_work, work_bytes, d_blob, blob_cap, desc, s);
+}
+
+int lbf_encode_noalloc(const void* d_w, uint64_t rows, uint64_t cols, void* d_blob, uint64_t blob_cap, lbf_desc* desc,
+                       hipStream_t s) {
+  if (!desc) return LBF_E_INVAL;
+  if (!shape_ok(rows, cols)) return LBF_E_SHAPE;
+  if (lbf_encode_work_bytes(rows, cols) > LBF_NOALLOC_SCRATCH_BYTES) return LBF_E_CAPACITY;
+  void* work = nullptr;
+  if (encode_scratch(&work) != hipSuccess) return LBF_E_HIP;
+  return encode(d_w, rows, cols, work, LBF_NOALLOC_SCRATCH_BYTES, d_blob, blob_cap, desc, s);
 }
 
 int lbf_hdesc_check(const lbf_hdesc* hdesc) { return hcheck(hdesc); }

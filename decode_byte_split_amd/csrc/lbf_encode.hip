@@ -20,6 +20,9 @@
 //              disagrees with the header and lbf_verify reports it)
 #include <hip/hip_runtime.h>
 
+#include <map>
+#include <mutex>
+
 #include "lbf_device.h"
 #include "lbf_internal.h"
 
@@ -198,6 +201,36 @@ __global__ __launch_bounds__(kEncWaves * kWave) void k_escapes(EscArgs a) {
     j++;
     esc_mask &= esc_mask - 1;
   }
+}
+
+// ---- Encoder workspace held by the library (lbf_encode_noalloc) ------------
+//
+// Callers that cannot allocate device memory (code under graph capture, tight
+// serving loops, harnesses that forbid it) get the encoder's workspace from
+// this file-scope device array instead of an argument.  Every GPU the library
+// runs on holds its own copy until the process ends.  In host code the
+// array's name is only a stand-in, never a device address: its address on the
+// current device comes from hipGetSymbolAddress, looked up once per device
+// (with that device current) and kept.
+static __device__ __align__(256) uint8_t scratch[LBF_NOALLOC_SCRATCH_BYTES];
+
+hipError_t encode_scratch(void** ptr) {
+  static std::mutex mu;
+  static std::map<int, void*> per_device;
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = per_device.find(dev);
+  if (it == per_device.end()) {
+    void* p = nullptr;
+    const hipError_t r = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (r != hipSuccess) return r;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    it = per_device.emplace(dev, p).first;
+  }
+  *ptr = it->second;
+  return hipSuccess;
 }
 
 hipError_t launch_pack(const uint16_t* w, const lbf_desc& d, uint8_t* blob, uint32_t* tile_cnt, hipStream_t s) {

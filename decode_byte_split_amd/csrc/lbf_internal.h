@@ -85,6 +85,9 @@ constexpr uint32_t kGemmMaxTiles = 64;
 
 // Workspace layout of lbf_encode: hist[256] u32, then tile counts u32[n_tiles].
 constexpr uint64_t kWorkHistBytes = 1024;
+// Device address, on the current device, of the library's own encoder
+// workspace (LBF_NOALLOC_SCRATCH_BYTES, lbf_encode.hip).
+hipError_t encode_scratch(void** ptr);
 
 // Launch facts of the current device, looked up once per device and kept for
 // the process (thread-safe; lbf_api.cpp).

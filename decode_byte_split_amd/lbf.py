@@ -30,6 +30,7 @@ LBF_F32 = 0
 LBF_BF16 = 1
 TILE = 1024
 MAX_GROUPS = 64
+NOALLOC_SCRATCH_BYTES = 1 << 20  # LBF_NOALLOC_SCRATCH_BYTES: lbf_encode_noalloc's workspace
 
 
 class Desc(ctypes.Structure):
@@ -129,6 +130,8 @@ def lib():
         L.lbf_desc_check.argtypes = [dp]
         L.lbf_encode.restype = i32
         L.lbf_encode.argtypes = [vp, u64, u64, vp, u64, vp, u64, dp, vp]
+        L.lbf_encode_noalloc.restype = i32
+        L.lbf_encode_noalloc.argtypes = [vp, u64, u64, vp, u64, dp, vp]
         L.lbf_decode.restype = i32
         L.lbf_decode.argtypes = [dp, vp, vp, vp]
         L.lbf_verify.restype = i32
@@ -154,7 +157,8 @@ def lib():
     return _lib
 
 
-EXPORTS = ("lbf_strerror", "lbf_encode_work_bytes", "lbf_desc_check", "lbf_encode", "lbf_decode", "lbf_verify",
+EXPORTS = ("lbf_strerror", "lbf_encode_work_bytes", "lbf_desc_check", "lbf_encode", "lbf_encode_noalloc",
+           "lbf_decode", "lbf_verify",
            "lbf_crc32", "lbf_gemv", "lbf_gemm", "lbf_gemv_swiglu", "lbf_hdesc_check", "lbf_hencode_work_bytes", "lbf_hencode",
            "lbf_hdecode")
 

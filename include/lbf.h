@@ -133,6 +133,26 @@ int lbf_encode(const void* d_w, uint64_t rows, uint64_t cols, void* d_work, uint
                void* d_blob, uint64_t blob_cap, lbf_desc* desc, hipStream_t s);
 
 /*
+ * lbf_encode_noalloc — lbf_encode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same two phases, arguments and results as
+ * lbf_encode, but the workspace is the library's own device array of
+ * LBF_NOALLOC_SCRATCH_BYTES, one per GPU, kept until the process ends.
+ * The call allocates nothing.
+ *  - tensors whose lbf_encode_work_bytes(rows, cols) exceeds
+ *    LBF_NOALLOC_SCRATCH_BYTES (more than 261,888 tiles, about 268 million
+ *    weights) are refused with LBF_E_CAPACITY before anything runs;
+ *  - every call on one GPU shares that GPU's array, and each call clears
+ *    what it needs cleared (the histogram) itself: calls that overlap on one
+ *    GPU (other streams or threads, or a phase 1 enqueued before another
+ *    call's phase 2 has run) race and may write a wrong blob.  Serialize
+ *    them, or use lbf_encode with a workspace per caller.
+ */
+#define LBF_NOALLOC_SCRATCH_BYTES (1u << 20)
+int lbf_encode_noalloc(const void* d_w, uint64_t rows, uint64_t cols, void* d_blob, uint64_t blob_cap,
+                       lbf_desc* desc, hipStream_t s);
+
+/*
  * lbf_decode — rebuild the exact BF16 tensor from a blob.
  * Lossless means the decoded bits equal the source bits, and that is what
  * this call delivers ("Lossless LLM Weight Compression vs 8-bit GGUF",

@@ -239,3 +239,24 @@ def test_swiglu_validates_before_touching_the_gpu():
     assert L.lbf_gemv_swiglu(r(wide), 256, r(wide), 256, 256, 2, 256, 0, None) == lbf.LBF_E_UNSUPPORTED
     small, _ = _oracle_desc(np.zeros((3, 5), dtype=np.uint16))
     assert L.lbf_gemv_swiglu(r(small), 256, r(small), 256, 256, 1, 256, 0, None) == lbf.LBF_E_SHAPE
+
+
+def test_binding_constants_match_the_header():
+    lbf = _lbf()
+    with open(os.path.join(ROOT, "include", "lbf.h")) as f:
+        text = f.read()
+    assert re.search(r"#define LBF_MAX_GROUPS (\d+)", text).group(1) == str(lbf.MAX_GROUPS)
+    m = re.search(r"#define LBF_NOALLOC_SCRATCH_BYTES \(1u << (\d+)\)", text)
+    assert 1 << int(m.group(1)) == lbf.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_encode_refuses_before_touching_the_gpu():
+    """Sizes past the library's array and bad arguments are refused on the
+    host (no GPU in this process)."""
+    lbf = _lbf()
+    L = lbf.lib()
+    d = lbf.Desc()
+    big = (lbf.NOALLOC_SCRATCH_BYTES - 1024) // 4 + 1
+    assert L.lbf_encode_noalloc(None, big, 1024, None, 0, ctypes.byref(d), None) == lbf.LBF_E_CAPACITY
+    assert L.lbf_encode_noalloc(None, 1 << 20, 1 << 20, None, 0, ctypes.byref(d), None) == lbf.LBF_E_SHAPE
+    assert L.lbf_encode_noalloc(None, 4, 1024, None, 0, None, None) == lbf.LBF_E_INVAL
