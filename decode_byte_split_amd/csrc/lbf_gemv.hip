@@ -471,8 +471,11 @@ constexpr uint32_t kRingXMax = 131072;  // x area; with the wave slots 144 KiB o
 // first group of each distinct x array (staged once) and bits 8..31 hold the
 // LDS byte offset of the group's x.
 constexpr uint32_t kAuxStageX = 2u;
+constexpr uint8_t kNoBlock = 0xFF;
 struct RingLaunch {
   GroupArg g[LBF_MAX_GROUPS];
+  uint32_t gtab[LBF_MAX_GROUPS];   // group table entry of each group (group_entry)
+  uint32_t xblk[kRingXMax / 4096];  // group whose x fills each 1 KiB block of the LDS x area, 4 blocks a word (stage_x)
   uint32_t n_rows;
   int n_groups, y_bf16;
   void* h;  // gated product (g[0] = gate, g[1] = up): h[b, r] = silu(gate) * up
@@ -498,23 +501,16 @@ __device__ __forceinline__ Planes ptrs_of(const GroupArg& G) {
   return planes_of(G.blob, (uint64_t)G.rows * G.tiles);
 }
 
-// Group table in one VGPR, lane g for group g (built once per kernel): the
-// group's first global row (an exclusive prefix sum of the groups' rows) in
-// bits 6..31 and its tiles per row minus one in bits 0..5; all ones past the
-// last group.  The ring launcher guarantees tiles <= 64 (x fits in LDS) and
-// fewer than 2^26 rows.
+// Group table in one VGPR, lane g for group g (loaded once per kernel): the
+// group's first global row (the launcher's prefix sum of the groups' rows)
+// in bits 6..31 and its tiles per row minus one in bits 0..5; all ones past
+// the last group.  The ring launcher guarantees tiles <= 64 (x fits in LDS)
+// and fewer than 2^26 rows.
 constexpr uint32_t kRingMaxRows = 1u << 26;
+constexpr uint32_t group_entry(uint32_t first_row, uint32_t tiles) { return (first_row << 6) | (tiles - 1u); }
 
 __device__ __forceinline__ uint32_t group_regs(const RingLaunch& L, int lane) {
-  const bool in = lane < L.n_groups;
-  const GroupArg& G = L.g[in ? lane : 0];
-  uint32_t pre = in ? G.rows : 0u;  // inclusive scan over the lanes, then minus own
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const uint32_t o = (uint32_t)__shfl_up((int)pre, (unsigned)d, kWave);
-    pre += lane >= d ? o : 0u;
-  }
-  return in ? ((pre - G.rows) << 6) | (G.tiles - 1u) : ~0u;
+  return lane < L.n_groups ? L.gtab[lane] : ~0u;
 }
 
 // Unit q of the launch: a row of one group, or (GATED) row q of the gate
@@ -544,10 +540,10 @@ __device__ __forceinline__ void load_idx(Slot<C>& s, const RingLaunch& L, const 
   s.idxv = __builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)lane * 4, 0, 0);
 }
 
-// Escape slice of the chunk (from its index, already loaded) and its planes.
+// Escape slice of the chunk, from its index (already loaded).
 template <int C>
-__device__ __forceinline__ void load_data(Slot<C>& s, const RingLaunch& L, const Pos& p, uint32_t& e_first,
-                                          uint32_t& e_cnt, int lane) {
+__device__ __forceinline__ void load_esc(Slot<C>& s, const RingLaunch& L, const Pos& p, uint32_t& e_first,
+                                         uint32_t& e_cnt, int lane) {
   const GroupArg& G = L.g[p.g];
   const Planes P = ptrs_of(G);
   const uint32_t hi = min((uint32_t)__builtin_amdgcn_readlane((int)s.idxv, (int)p.S), G.n_esc);
@@ -555,6 +551,12 @@ __device__ __forceinline__ void load_data(Slot<C>& s, const RingLaunch& L, const
   e_cnt = p.valid ? hi - e_first : 0u;
   const __amdgpu_buffer_rsrc_t re = make_rsrc(P.esc + e_first, min(e_cnt, 64u));
   s.escv = __builtin_amdgcn_raw_buffer_load_b8(re, (uint32_t)lane, 0, 0);
+}
+
+// Raw and nibble planes of the chunk (2 C loads; they need no index).
+template <int C>
+__device__ __forceinline__ void load_planes(Slot<C>& s, const RingLaunch& L, const Pos& p, int lane) {
+  const Planes P = ptrs_of(L.g[p.g]);
   const uint64_t t0 = tile_of(p);
   const __amdgpu_buffer_rsrc_t rr = make_rsrc(P.raw + t0 * kTile, p.S * kTile);
   const __amdgpu_buffer_rsrc_t rn = make_rsrc(P.nib + t0 * (kTile / 2), p.S * (kTile / 2));
@@ -562,6 +564,50 @@ __device__ __forceinline__ void load_data(Slot<C>& s, const RingLaunch& L, const
   for (int j = 0; j < C; j++) {
     s.raw[j] = __builtin_amdgcn_raw_buffer_load_b128(rr, (uint32_t)lane * 16 + j * kTile, 0, kNonTemporal);
     s.nib[j] = __builtin_amdgcn_raw_buffer_load_b64(rn, (uint32_t)lane * 8 + j * (kTile / 2), 0, kNonTemporal);
+  }
+}
+
+template <int C>
+__device__ __forceinline__ void load_data(Slot<C>& s, const RingLaunch& L, const Pos& p, uint32_t& e_first,
+                                          uint32_t& e_cnt, int lane) {
+  load_esc(s, L, p, e_first, e_cnt, lane);
+  load_planes(s, L, p, lane);
+}
+
+// s_waitcnt with only the vector-memory count limited (gfx9 encoding: vmcnt
+// in bits 3..0 and 15..14; expcnt 6..4 and lgkmcnt 11..8 left at their maxima).
+constexpr int waitcnt_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+// x of every group whose aux word says so, from memory straight into LDS
+// (buffer loads to LDS: no registers, one wait before the barrier).  The
+// staged x arrays lie back to back in the LDS x area in 1 KiB blocks: block
+// j is bytes [1024 j, 1024 j + 1024), and L.xblk[j] names the group whose x
+// it holds (kNoBlock past the last).  In a group's x area, element (b, t,
+// lane, half) is at ((b T + t) 2 + half) 1024 + 16 lane: block (b, t, half)
+// is one load instruction of a wave, lane l bringing the 16 bytes at
+// x + b cols + t 1024 + 16 l + 8 half (bf16 elements).  Block j is loaded by
+// wave j % W.  EXACT: every wave issues exactly kRingXMax / 1024 / W loads
+// (unrolled), so the number of loads in flight is known at compile time: one
+// with no block gets a zero-length range (no memory access) and lands in
+// `spare`, 1 KiB of LDS nothing reads before the barrier.  Otherwise a
+// rolled loop issues only the blocks there are (fewer registers; used where
+// x is loaded before everything else and waited for with all of it).
+template <int B, int W, bool EXACT>
+__device__ __forceinline__ void stage_x(const RingLaunch& L, uint8_t* smem, uint8_t* spare, uint32_t wave, int lane) {
+  constexpr int kXLoads = (int)(kRingXMax / kTile) / W;
+  constexpr int kUnroll = EXACT ? kXLoads : 1;
+#pragma unroll kUnroll
+  for (int i = 0; i < kXLoads; i++) {
+    const uint32_t j = wave + (uint32_t)(W * i);
+    const uint32_t k = (L.xblk[j >> 2] >> (8u * (j & 3u))) & 0xFFu;  // a word: one scalar load
+    const bool have = k != kNoBlock;  // uniform
+    if (!EXACT && !have) break;  // blocks are filled from 0 up
+    const GroupArg& G = L.g[have ? k : 0u];
+    const uint32_t jj = have ? j - (G.aux >> 18) : 0u;  // block within the group's x (x_off / 1024)
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(G.x, have ? (uint32_t)B * G.tiles * 2u * kTile : 0u);
+    uint8_t* dst = have ? smem + (size_t)j * kTile : spare;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)dst, 16,
+                                             (uint32_t)lane * 32u + (jj & 1u) * 16u, (jj >> 1) * 2048u, 0, 0);
   }
 }
 
@@ -624,9 +670,13 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const uint32_t wave = uniform(threadIdx.x >> 6);
   const int lane = lane_id();
-  const uint32_t GR = GATED ? 0u : group_regs(L, lane);  // the gated launch has one row space
   uint8_t* slot_lds = smem + kRingXMax + wave * kTile;
   uint32_t* lctr = reinterpret_cast<uint32_t*>(smem + kRingXMax + W * kTile);
+  // x first: it depends on nothing but the launch record, and every wave
+  // waits for it before its first product
+  stage_x<B, W, false>(L, smem, slot_lds, wave, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  const uint32_t GR = GATED ? 0u : group_regs(L, lane);  // the gated launch has one row space
 
   // rows of this CU: blockIdx.x + k * gridDim.x; the wave's first two come
   // from k = wave, wave + 16, the rest from the LDS counter (starts at 32)
@@ -671,29 +721,32 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
   Slot<C> sl[N];
   Pos pp[N];
   uint32_t ef[N], en[N];  // escape slice (first, count) of each slot's chunk
-  pp[0] = next_row();
-#pragma unroll
-  for (int i = 1; i < N - 1; i++) pp[i] = advance(pp[i - 1]);
-#pragma unroll
-  for (int i = 0; i < N - 1; i++) load_idx(sl[i], L, pp[i], lane);
-#pragma unroll
-  for (int i = 0; i < N - 2; i++) load_data(sl[i], L, pp[i], ef[i], en[i], lane);
-  // stage every distinct x array while the first loads are in flight:
-  // element (b, t, lane, half) at x_off + ((b*T + t)*2 + half)*1024 + lane*16
-  for (int k = 0; k < L.n_groups; k++) {
-    const GroupArg& G = L.g[k];
-    if (!(G.aux & kAuxStageX)) continue;
-    const uint32_t T = G.tiles;
-    uint8_t* xd = smem + (G.aux >> 8);
-    const uint32_t nx = (uint32_t)B * T * kWave * 2;
-    for (uint32_t i = threadIdx.x; i < nx; i += W * kWave) {
-      const uint32_t half = i & 1u, ln = (i >> 1) & 63u, bt = i >> 7;
-      const u32x4 v = reinterpret_cast<const u32x4*>(G.x)[(size_t)bt * 128 + ln * 2 + half];
-      *reinterpret_cast<u32x4*>(xd + (size_t)(bt * 2 + half) * kTile + ln * 16) = v;
-    }
-  }
+  static_assert(N == 3, "the start-up below fills a ring of three slots");
+  // Start-up.  x is what every wave waits for first, and all CUs start at
+  // once: requested together with the planes, x would queue behind the whole
+  // chip's plane traffic (6-9 us).  So x (issued above, before the group
+  // table) is awaited alone; then the index words and planes of the first
+  // chunks go out together, and the escape slices once the index words are
+  // in.  At batch 1 two chunks per wave are filled; larger batches have no
+  // registers for a second one, which comes with the first step.
+  constexpr int F = B == 1 ? 2 : 1;  // chunks filled at start-up
+  pp[0] = next_row();  // the group table load is waited for here; x has had the same time
+  pp[1] = advance(pp[0]);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's x is in LDS
+  __builtin_amdgcn_sched_barrier(0);
+  load_idx(sl[0], L, pp[0], lane);
+  load_idx(sl[1], L, pp[1], lane);
+  load_planes(sl[0], L, pp[0], lane);
+  __builtin_amdgcn_sched_barrier(0);
   if (threadIdx.x == 0) *lctr = 2u * W;
   __syncthreads();
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * C));  // the index words are in
+  __builtin_amdgcn_sched_barrier(0);
+  // escapes before the second chunk's planes: loads complete in order, and
+  // the first step needs only chunk 0
+#pragma unroll
+  for (int i = 0; i < F; i++) load_esc(sl[i], L, pp[i], ef[i], en[i], lane);
+  if constexpr (F == 2) load_planes(sl[1], L, pp[1], lane);
 
   float acc[B][2];
   float gsum[B];  // GATED: the finished gate sums of the current row
@@ -701,12 +754,13 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
   for (int bb = 0; bb < B; bb++) acc[bb][0] = acc[bb][1] = gsum[bb] = 0.f;
 
   // one step: chunk p0 in `cur` is decoded; the next chunk p1 (index in
-  // `nx1` already) gets its escapes and planes; the one after, p2, its index
-  auto step = [&](auto rot) -> bool {
+  // already) gets its escapes and planes (unless the start-up issued them);
+  // the one after, p2, its index
+  auto step = [&](auto rot, auto started) -> bool {
     constexpr int K = decltype(rot)::value, I1 = (K + N - 1) % N, I2 = (K + N - 2) % N;
     pp[I1] = advance(pp[I2]);
     load_idx(sl[I1], L, pp[I1], lane);
-    load_data(sl[I2], L, pp[I2], ef[I2], en[I2], lane);
+    if constexpr (!decltype(started)::value) load_data(sl[I2], L, pp[I2], ef[I2], en[I2], lane);
     Slot<C>& cur = sl[K];
     const Pos& p0 = pp[K];
     const uint32_t f0 = ef[K], n0 = en[K];
@@ -808,9 +862,16 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
     wave_lds_sync();  // the slot is rewritten by the next chunk
     return pp[(K + 1) % N].valid;
   };
-  if (pp[0].valid)
-    while (ring_round<0, N>(step)) {
-    }
+  auto steady = [&](auto rot) -> bool { return step(rot, std::false_type{}); };
+  if constexpr (F == 2) {
+    if (pp[0].valid && step(std::integral_constant<int, 0>{}, std::true_type{}) && ring_round<1, N>(steady))
+      while (ring_round<0, N>(steady)) {
+      }
+  } else {
+    if (pp[0].valid)
+      while (ring_round<0, N>(steady)) {
+      }
+  }
 }
 
 // 16 waves a workgroup (4 per SIMD, <= 128 VGPRs each) for every batch:
@@ -838,6 +899,10 @@ hipError_t launch_gemv_gated(const GroupArg& gate, const GroupArg& up, int batch
   L.g[1] = up;
   L.g[0].aux = (gate.aux & kAuxContig) | kAuxStageX;  // one x for both, at LDS offset 0
   L.g[1].aux = up.aux & kAuxContig;
+  L.gtab[0] = L.gtab[1] = 0u;  // one row space (unused)
+  const uint32_t blocks = (uint32_t)batch * gate.tiles * 2u;
+  for (uint32_t j = 0; j < kRingXMax / 4096; j++) L.xblk[j] = 0u;
+  for (uint32_t j = blocks; j < kRingXMax / 1024; j++) L.xblk[j >> 2] |= (uint32_t)kNoBlock << (8 * (j & 3));
   L.n_rows = gate.rows;
   L.n_groups = 2;
   L.y_bf16 = h_dtype == LBF_BF16;
@@ -861,6 +926,7 @@ static hipError_t launch_ring(const GroupArg* groups, int n_groups, int batch, i
   RingLaunch L;
   uint64_t x_bytes = 0;  // 64-bit: batch * cols * 2 can pass 2^32 for one very wide row
   uint64_t rows = 0;
+  for (uint32_t j = 0; j < kRingXMax / 4096; j++) L.xblk[j] = 0xFFFFFFFFu;  // kNoBlock in every byte
   // longest rows first: rows are handed out in this order, so the coarsest
   // units are taken early and the last ones are the shortest
   int order[LBF_MAX_GROUPS];
@@ -879,8 +945,12 @@ static hipError_t launch_ring(const GroupArg* groups, int n_groups, int batch, i
       const uint64_t xb = (uint64_t)batch * G.tiles * kTile * 2;
       if (x_bytes + xb > kRingXMax) return hipSuccess;
       L.g[g].aux |= kAuxStageX | (uint32_t)(x_bytes << 8);
+      for (uint64_t j = x_bytes / 1024; j < (x_bytes + xb) / 1024; j++)
+        L.xblk[j >> 2] = (L.xblk[j >> 2] & ~(0xFFu << (8 * (j & 3)))) | ((uint32_t)g << (8 * (j & 3)));
       x_bytes += xb;
     }
+    if (rows + G.rows >= kRingMaxRows) return hipSuccess;
+    L.gtab[g] = group_entry((uint32_t)rows, G.tiles);
     rows += G.rows;
   }
   if (rows >= kRingMaxRows) return hipSuccess;
