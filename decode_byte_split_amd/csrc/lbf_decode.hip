@@ -29,7 +29,7 @@ struct DecodeArgs {
 
 template <bool CONTIG>
 __global__ __launch_bounds__(kDecodeWaves * kWave) void k_decode(DecodeArgs a) {
-  __shared__ uint8_t esc_lds[kDecodeWaves][kTile];
+  __shared__ __attribute__((aligned(16))) uint8_t esc_lds[kDecodeWaves][kEscSlot];
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const uint32_t t = uniform(blockIdx.x * kDecodeWaves + (uint32_t)wave);

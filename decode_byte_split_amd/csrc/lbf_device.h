@@ -153,18 +153,42 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// LDS bytes of a wave's escape staging slot: a tile's slice (<= 1024 bytes)
+// from its 4-byte aligned start, in five 256-byte loads.
+constexpr uint32_t kEscSlot = 1280;
+
 // Escape placement for one tile held by one wave (called by all 64 lanes,
-// only when the tile has escapes).  The tile's escape slice
-// esc[first, first + cnt) is staged in this wave's LDS slot (cnt <= 1024),
-// then each lane patches its exponent bytes in element order.
+// only when the tile has escapes).  The tile's escape slice esc[first,
+// first + cnt) (cnt <= 1024) is copied into this wave's LDS slot (kEscSlot
+// bytes, 4-byte aligned) by five 4-byte buffer loads per lane that write
+// straight into LDS, all issued before a single wait; the slice then starts
+// at slot[first & 3] (bytes past it read as zeros, with no memory access).
+// Each lane patches its exponent bytes in element order.
 __device__ __forceinline__ void place_escapes(u32x2 nib, const uint8_t* __restrict__ esc, uint32_t first,
-                                              uint32_t cnt, uint8_t* lds_slot, uint32_t E[4]) {
-  const int lane = lane_id();
-  for (uint32_t p = (uint32_t)lane; p < cnt; p += kWave) lds_slot[p] = esc[first + p];
+                                              uint32_t cnt, uint8_t* slot, uint32_t E[4]) {
+  const uint32_t lane = (uint32_t)lane_id();
+  const uint32_t a0 = first & ~3u, nb = first + cnt - a0;  // bytes from the aligned start
+  // one range over the slice, rounded up to whole dwords (the range check is
+  // per dword; the escape plane starts on a 256-byte boundary and the blob's
+  // size is a multiple of 256, so that dword is inside the blob); loads past
+  // it read as zeros.  Load i takes the 256 bytes from a0 + 256 i into slot +
+  // 256 i.  The lane offset is made opaque here so that the five offsets are
+  // formed on this (rare) path instead of being kept in registers for the
+  // whole kernel.
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(esc + a0), (short)0,
+                                                                     (int)((nb + 3u) & ~3u), 0x00020000);
+  uint32_t vo = 4 * lane;
+  asm volatile("" : "+v"(vo));
+  static_assert(kEscSlot == 5 * 256, "five loads of 256 bytes");
+#pragma unroll
+  for (uint32_t i = 0; i < 5; i++)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(slot + 256 * i), 4,
+                                             vo + 256 * i, 0, 0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the slice is in LDS
   wave_lds_sync();
   uint64_t m0, m1;
   const uint32_t j = escape_rank(nib, m0, m1);
-  patch_escapes(lds_slot, j, cnt, m0, m1, E);
+  patch_escapes(slot + (first & 3u), j, cnt, m0, m1, E);
   wave_lds_sync();  // the slot is rewritten for the next tile
 }
 
@@ -184,6 +208,12 @@ __device__ __forceinline__ u32x4 load_nt(const u32x4* p) { return __builtin_nont
 __device__ __forceinline__ u32x2 load_nt(const u32x2* p) { return __builtin_nontemporal_load(p); }
 
 __device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// s_waitcnt operand that limits only the vector-memory count to n (0..63):
+// gfx9 encoding, vmcnt in bits 3..0 and 15..14, expcnt (6..4) and lgkmcnt
+// (11..8) left at their maxima so nothing else is waited for.
+constexpr int waitcnt_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+static_assert(waitcnt_vm(8) == 0x0F78 && waitcnt_vm(16) == 0x4F70, "vmcnt encoding");
 
 // Plane addresses of a format-v1 blob with n_tiles tiles (header 256 bytes,
 // raw and nibble planes back to back, index, escapes at the next 256 boundary).

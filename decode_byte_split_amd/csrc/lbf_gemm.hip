@@ -312,12 +312,12 @@ __global__ __launch_bounds__(kGemmWaves * S * kWave) void k_gemm(GemmLaunch L) {
       if constexpr (XB == 0) {
         (void)more;
       } else if constexpr (XB == 2) {
-        if (more) __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8), expcnt/lgkmcnt not waited
+        if (more) __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
         __syncthreads();
       } else if (k & 1u) {
         // x of steps k + 1, k + 2 issued at step k - 1, before the coded
         // loads of steps k + 1 and k + 2 (16 younger loads)
-        if (more) __builtin_amdgcn_s_waitcnt(0x0F70 | 16);  // vmcnt(16)
+        if (more) __builtin_amdgcn_s_waitcnt(waitcnt_vm(16));
         __syncthreads();
       }
     };

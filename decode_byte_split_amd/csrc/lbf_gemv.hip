@@ -191,7 +191,7 @@ __device__ __forceinline__ void load_row(RowBuf<SMAX>& R, const uint8_t* raw_p, 
 struct SegCtx {
   const uint8_t* esc_p;  // escape stream of the tensor
   const uint8_t* esc_sh; // LDS copy of escapes [e_lo, e_hi) when preloaded
-  uint8_t* esc_wave;     // this wave's 1 KiB staging slot otherwise
+  uint8_t* esc_wave;     // this wave's staging slot (kEscSlot bytes) otherwise
   uint32_t e_lo, e_hi;   // escape range of the workgroup's rows (clamped)
   Lut lut;
   uint32_t base4;
@@ -402,7 +402,7 @@ __global__ __launch_bounds__(kGemvWaves * kWave) __attribute__((amdgpu_waves_per
 void k_gemv(GemvLaunch L) {
   __shared__ float part[kSubUnits][kGemvWaves][B];
   __shared__ uint8_t esc_sh[kEscShared];
-  __shared__ uint8_t esc_wave[kGemvWaves][kTile];
+  __shared__ __attribute__((aligned(16))) uint8_t esc_wave[kGemvWaves][kEscSlot];
   const uint32_t wave = uniform(threadIdx.x >> 6);
   const int lane = lane_id();
   // this workgroup's share of the total cost: units whose start cost is in [c_lo, c_hi)
@@ -574,10 +574,6 @@ __device__ __forceinline__ void load_data(Slot<C>& s, const RingLaunch& L, const
   load_planes(s, L, p, lane);
 }
 
-// s_waitcnt with only the vector-memory count limited (gfx9 encoding: vmcnt
-// in bits 3..0 and 15..14; expcnt 6..4 and lgkmcnt 11..8 left at their maxima).
-constexpr int waitcnt_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
-
 // x of every group whose aux word says so, from memory straight into LDS
 // (buffer loads to LDS: no registers, one wait before the barrier).  The
 // staged x arrays lie back to back in the LDS x area in 1 KiB blocks: block
@@ -670,8 +666,8 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const uint32_t wave = uniform(threadIdx.x >> 6);
   const int lane = lane_id();
-  uint8_t* slot_lds = smem + kRingXMax + wave * kTile;
-  uint32_t* lctr = reinterpret_cast<uint32_t*>(smem + kRingXMax + W * kTile);
+  uint8_t* slot_lds = smem + kRingXMax + wave * kEscSlot;
+  uint32_t* lctr = reinterpret_cast<uint32_t*>(smem + kRingXMax + W * kEscSlot);
   // x first: it depends on nothing but the launch record, and every wave
   // waits for it before its first product
   stage_x<B, W, false>(L, smem, slot_lds, wave, lane);
@@ -880,7 +876,7 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
 template <int B, bool GATED = false>
 static hipError_t run_ring_kernel(RingLaunch& L, hipStream_t s) {
   constexpr int W = kRingWaves, C = kRingTiles, N = kRingSlots;
-  const uint32_t lds = kRingXMax + W * kTile + 16;
+  const uint32_t lds = kRingXMax + W * kEscSlot + 16;
   int cus = 0;
   hipError_t e = device_cus(&cus);
   if (e == hipSuccess) e = open_dynamic_lds(reinterpret_cast<const void*>(&k_gemv_ring<B, W, GATED, C, N>), (int)lds);
