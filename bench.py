@@ -9,9 +9,13 @@ copies of the coded layer (4 GB) so the working set cannot sit in the
 
 Printed: one JSON line with the metric (BF16-equivalent weight GB/s), the
 roofline of the GEMV kernel (algorithmic bytes per launch / mean launch time
-from HIP events on the launch stream, against 8 TB/s HBM), the HBM traffic
-read from the committed rocprofv3 counter summary (null if the kernel source
-changed since), and the CPU oracle timed on this host as a baseline.
+from HIP events on the launch stream, against 8 TB/s HBM; also the median of
+10-launch batch means), the HBM traffic read from the committed rocprofv3
+counter summary (null if the kernel source changed since), the other
+workloads' own roofline fractions under "configs" (gate_proj alone at batch
+1, 8, 16, 64 and the 64 experts at batch 4), and the CPU oracle timed on
+this host as a baseline, on the headline layer and per workload, on one core
+and on all cores.
 """
 from __future__ import annotations
 
@@ -79,9 +83,30 @@ def time_region(torch, fn, steps: int, warmup: int) -> float:
     return t0.elapsed_time(t1) / steps
 
 
+def time_batches(torch, fn, batches: int, per_batch: int, warmup: int):
+    """Back-to-back launches timed in batches: each batch is per_batch calls
+    between two HIP events; returns the per-call mean of every batch (ms).
+    Same quantity as time_region, so its median and min describe the spread
+    of the back-to-back figure across the run."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(batches + 1)]
+    ev[0].record()
+    k = warmup
+    for j in range(batches):
+        for _ in range(per_batch):
+            fn(k)
+            k += 1
+        ev[j + 1].record()
+    torch.cuda.synchronize()
+    return [ev[j].elapsed_time(ev[j + 1]) / per_batch for j in range(batches)]
+
+
 def time_each(torch, fn, steps: int, warmup: int):
     """Per-launch durations (ms): each call between its own pair of HIP
-    events on the launch stream; returns (median, min)."""
+    events on the launch stream (the event pair adds its own overhead to
+    every launch); returns (median, min)."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -180,34 +205,6 @@ def summarize_counters(fetch_csv: str, write_csv: str, kernel_key: str, alg_byte
     return out
 
 
-def cpu_baseline(Ws, xs, min_seconds: float, workers: int = 0):
-    """The oracle (plain scalar C, one thread) on this host: decode the
-    layer's blobs and run the float64 matvec, repeated until min_seconds.
-    With workers > 1, also the same oracle calls in that many processes at
-    once (one tensor pass per job), the host's all-cores figure."""
-    from oracle import oracle as O
-
-    blobs = [O.encode(W) for W in Ws]  # untimed: the baseline is decode + product
-    n = sum(W.size for W in Ws)
-    passes = 0
-    t = 0.0
-    while passes == 0 or t < min_seconds:
-        t0 = time.perf_counter()
-        for blob, x in zip(blobs, xs):
-            W = O.decode(blob)
-            O.matvec(W, x)
-        t += time.perf_counter() - t0
-        passes += 1
-    gbs = 2.0 * n * passes / t / 1e9
-    out = {"value": gbs, "unit": "GB/s", "cores": 1, "kind": "oracle",
-           "sample": "full 8B-shaped layer (7 tensors, %d weights) x %d pass(es): oracle decode of each "
-                     "oracle-coded blob + float64 matvec at batch 1, %.1f s" % (n, passes, t),
-           "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
-    if workers > 1:
-        out["all_cores"] = oracle_all_cores(blobs, xs, min_seconds, workers)
-    return out
-
-
 def _oracle_worker_init():
     from oracle import oracle as O
 
@@ -215,54 +212,130 @@ def _oracle_worker_init():
 
 
 def _oracle_job(item):
-    """One oracle pass over one tensor (a worker process): decode + matvec."""
+    """One oracle job (in this process or a worker): ("dm", blob file, x
+    file) decodes an oracle-coded blob and runs the float64 matvec of its
+    batch; ("enc", weights file) encodes a tensor.  Returns the weights
+    processed."""
     from oracle import oracle as O
 
-    blob_path, x_path = item
+    if item[0] == "enc":
+        W = np.load(item[1], mmap_mode="r")
+        O.encode(np.ascontiguousarray(W))
+        return W.size
+    _, blob_path, x_path = item
     W = O.decode(np.load(blob_path, mmap_mode="r"))
     O.matvec(W, np.load(x_path))
     return W.size
 
 
-def oracle_all_cores(blobs, xs, min_seconds: float, workers: int):
-    """The same oracle calls as cpu_baseline in `workers` processes at once:
-    jobs are (tensor, pass) pairs, the blobs are shared through memory-mapped
-    files, and the figure is weights processed over wall time.  A worker that
-    dies or a job slower than a minute ends this leg with an error entry,
-    never the benchmark."""
-    import concurrent.futures as cf
-    import multiprocessing as mp
+def _write_jobs(d, name, jobs, coded):
+    """Arrays of a leg's jobs -> file-based job tuples (memory-mapped by the
+    workers).  ("dm", W, x): W is coded by the oracle first (untimed; one blob
+    file per distinct W, kept in `coded`); ("enc", W): W itself."""
+    from oracle import oracle as O
+
+    out = []
+    for i, j in enumerate(jobs):
+        if j[0] == "enc":
+            wp = os.path.join(d, "%s_w%d.npy" % (name, i))
+            np.save(wp, j[1])
+            out.append(("enc", wp))
+            continue
+        key = id(j[1])
+        if key not in coded:
+            bp = os.path.join(d, "blob%d.npy" % len(coded))
+            np.save(bp, O.encode(j[1]))
+            coded[key] = (bp, j[1])  # keeps W alive so its id stays unique
+        xp = os.path.join(d, "%s_x%d.npy" % (name, i))
+        np.save(xp, j[2])
+        out.append(("dm", coded[key][0], xp))
+    return out
+
+
+def _one_core(jobs, min_seconds):
+    weights, t, passes = 0, 0.0, 0
+    while passes == 0 or t < min_seconds:
+        t0 = time.perf_counter()
+        for j in jobs:
+            weights += _oracle_job(j)
+        t += time.perf_counter() - t0
+        passes += 1
+    return weights, t, passes
+
+
+def _all_cores(pool, jobs, min_seconds, workers):
+    def run(js):
+        return sum(f.result(timeout=120.0) for f in [pool.submit(_oracle_job, j) for j in js])
+
+    per_round = max(1, -(-workers // len(jobs)))  # at least one job per worker a round
+    weights, t, rounds = 0, 0.0, 0
+    while rounds == 0 or t < min_seconds:
+        t0 = time.perf_counter()
+        weights += run(jobs * per_round)
+        t += time.perf_counter() - t0
+        rounds += 1
+    return weights, t
+
+
+def cpu_baseline(Ws, xs, min_seconds: float, workers: int = 0, legs=None, leg_seconds: float = 1.0):
+    """The oracle (plain scalar C, one thread) on this host.  Headline: decode
+    the layer's oracle-coded blobs and run the float64 matvec at batch 1,
+    repeated until min_seconds.  legs: more workloads, {name: (description,
+    [("dm", W, x) | ("enc", W), ...])}, each timed for leg_seconds (at
+    least one pass).  With workers > 1, every leg is also run in that many
+    processes at once (jobs shared out, files memory-mapped): the host's
+    all-cores figure.  BF16-equivalent GB/s = 2 bytes per weight processed."""
     import shutil
     import tempfile
 
     d = tempfile.mkdtemp(prefix="lbf_oracle_")
     try:
-        items = []
-        for m, (b, x) in enumerate(zip(blobs, xs)):
-            bp, xp = os.path.join(d, "blob%d.npy" % m), os.path.join(d, "x%d.npy" % m)
-            np.save(bp, b)
-            np.save(xp, x)
-            items.append((bp, xp))
+        coded = {}
+        head = _write_jobs(d, "layer", [("dm", W, x) for W, x in zip(Ws, xs)], coded)
+        legs = legs or {}
+        leg_jobs = {name: (desc, _write_jobs(d, name, jobs, coded)) for name, (desc, jobs) in legs.items()}
+        n = sum(W.size for W in Ws)
+        w, t, passes = _one_core(head, min_seconds)
+        out = {"value": 2.0 * w / t / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": "full 8B-shaped layer (7 tensors, %d weights) x %d pass(es): oracle decode of each "
+                         "oracle-coded blob + float64 matvec at batch 1, %.1f s" % (n, passes, t),
+               "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
+        configs = {}
+        for name, (desc, jobs) in leg_jobs.items():
+            w, t, passes = _one_core(jobs, leg_seconds)
+            configs[name] = {"one_core_GBs": round(2.0 * w / t / 1e9, 4), "sample": "%s; %d pass(es), %.1f s on 1 core"
+                             % (desc, passes, t)}
+        if workers > 1:
+            out["all_cores"] = _all_cores_legs(head, leg_jobs, configs, min_seconds, leg_seconds, workers)
+        if configs:
+            out["configs"] = configs
+        return out
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
+
+
+def _all_cores_legs(head, leg_jobs, configs, min_seconds, leg_seconds, workers):
+    """The same jobs in `workers` processes at once.  A worker that dies or a
+    job slower than two minutes ends this part with an error entry, never the
+    benchmark."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+
+    try:
         # fresh interpreters (spawn): nothing of this process's GPU state
         with cf.ProcessPoolExecutor(workers, mp_context=mp.get_context("spawn"),
                                     initializer=_oracle_worker_init) as pool:
-            def run(jobs):
-                return sum(f.result(timeout=60.0) for f in [pool.submit(_oracle_job, j) for j in jobs])
-
-            run([items[1]] * workers)  # every worker up and warm
-            per_round = max(1, 4 * workers // len(items))
-            weights, t, rounds = 0, 0.0, 0
-            while rounds == 0 or t < min_seconds:
-                t0 = time.perf_counter()
-                weights += run(items * per_round)
-                t += time.perf_counter() - t0
-                rounds += 1
+            list(pool.map(_oracle_job, [head[-1]] * workers))  # every worker up and warm
+            w, t = _all_cores(pool, head, min_seconds, workers)
+            res = {"value": 2.0 * w / t / 1e9, "unit": "GB/s", "cores": workers, "kind": "oracle",
+                   "sample": "the same layer passes in %d processes at once: %d weights in %.1f s" % (workers, w, t)}
+            for name, (_, jobs) in leg_jobs.items():
+                w, t = _all_cores(pool, jobs, leg_seconds, workers)
+                configs[name]["all_cores_GBs"] = round(2.0 * w / t / 1e9, 4)
+                configs[name]["all_cores"] = workers
+            return res
     except Exception as e:  # noqa: BLE001 - reported in the JSON line instead
         return {"error": "%s: %s" % (type(e).__name__, e), "cores": workers}
-    finally:
-        shutil.rmtree(d, ignore_errors=True)
-    return {"value": 2.0 * weights / t / 1e9, "unit": "GB/s", "cores": workers, "kind": "oracle",
-            "sample": "the same layer passes in %d processes at once: %d weights in %.1f s" % (workers, weights, t)}
 
 
 def main():
@@ -270,7 +343,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=6.0)
+    ap.add_argument("--no-configs", action="store_true", help="only the headline layer line (no gate_proj / expert "
+                    "keys and no per-config CPU oracle legs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--extras", action="store_true", help="also time decode, the batch sweep, the experts, "
                     "raw BF16 and a copy ceiling")
@@ -340,7 +415,8 @@ def main():
     calls = [lbf.prepare(r, xd, lbf.LBF_F32, outs=ys) for r in rot]
     step = lambda i: calls[i % copies]()
     ms_step = time_region(torch, step, args.steps, args.warmup)
-    ms_median, ms_min = time_each(torch, step, max(args.steps // 2, 10), 3)
+    batch_ms = time_batches(torch, step, max(args.steps // 10, 5), 10, 3)
+    ms_single, _ = time_each(torch, step, max(args.steps // 2, 10), 3)
     alg = sum(algorithmic_bytes(b, 1, 4) for b in blobs)
     achieved = alg / (ms_step * 1e-3) / 1e9
     value = 2.0 * n_weights / (ms_step * 1e-3) / 1e9
@@ -387,8 +463,13 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": KERNEL, "algorithmic_bytes_per_launch": alg,
-                     "launch_ms_mean": round(ms_step, 5), "launch_ms_median": round(ms_median, 5),
-                     "launch_ms_min": round(ms_min, 5), "read_stream_ceiling": round(ceiling, 1),
+                     "launch_us_mean": round(ms_step * 1e3, 2),
+                     "batch_mean_us_median": round(float(np.median(batch_ms)) * 1e3, 2),
+                     "batch_mean_us_min": round(float(np.min(batch_ms)) * 1e3, 2),
+                     "frac_batch_median": round(alg / (float(np.median(batch_ms)) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "batches": "%d batches of 10 back-to-back launches" % len(batch_ms),
+                     "single_launch_event_us_median": round(ms_single * 1e3, 2),
+                     "read_stream_ceiling": round(ceiling, 1),
                      "frac_of_read_stream_ceiling": round(achieved / ceiling, 4),
                      "read_stream_same_bytes_us": round(same_us, 2),
                      "speed_vs_same_bytes_read": round(same_us / (ms_step * 1e3), 4)},
@@ -397,6 +478,8 @@ def main():
                        "read_stream_ceiling_GBs": round(ceiling, 1)},
     }
 
+    if not args.no_configs:
+        out["configs"] = config_keys(torch, lbf, synth, Ws, blobs, rot, copies)
     if args.extras:
         out["extra"] = extras(torch, lbf, synth, Ws, blobs, rot, copies, args)
         out["extra"]["k15h_layer"] = k15h(torch, lbf, Ws, blobs)
@@ -407,9 +490,79 @@ def main():
         out.setdefault("extra", {})["model_sweep"] = model_sweep(torch, lbf, synth)
 
     if not args.no_cpu:
-        log("timing the CPU oracle (~%.0f s)" % args.cpu_seconds)
-        out["cpu_baseline"] = cpu_baseline(Ws, xs, args.cpu_seconds, min(16, os.cpu_count() or 1))
+        log("timing the CPU oracle (~%.0f s)" % (3 * args.cpu_seconds))
+        out["cpu_baseline"] = cpu_baseline(Ws, xs, args.cpu_seconds, min(16, os.cpu_count() or 1),
+                                           legs=None if args.no_configs else cpu_legs(synth, Ws),
+                                           leg_seconds=0.5)
     print(json.dumps(out))
+
+
+def _timed(torch, calls, alg, steps=50):
+    """Back-to-back mean and the median of 10-launch batch means (us), and the
+    fractions of 8 TB/s they give for alg bytes a launch."""
+    n = len(calls)
+    ms = time_region(torch, lambda i: calls[i % n](), steps, 5)
+    bm = float(np.median(time_batches(torch, lambda i: calls[i % n](), 5, 10, 2)))
+    return {"us": round(ms * 1e3, 2), "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "batch_median_us": round(bm * 1e3, 2), "frac_batch_median": round(alg / (bm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": alg}
+
+
+def config_keys(torch, lbf, synth, Ws, blobs, rot, copies):
+    """The other workloads beside the headline, each with its own roofline
+    fraction (algorithmic bytes / time against 8 TB/s): gate_proj (14336 x
+    4096) alone at batch 1, 8 (fused GEMV) and 16, 64 (fused GEMM on MFMA),
+    bf16 output, with torch's F.linear on the uncompressed tensor beside it;
+    and the 64 expert tensors (1536 x 4096, escape-rate stress) in one grouped
+    call at batch 4, fp32 output.  Rotation copies keep the working set past
+    the 256 MB cache."""
+    g = synth.GATE
+    res = {}
+    wraw = [dev(torch, Ws[g]) for _ in range(4)]
+    for batch in (1, 8, 16, 64):
+        x = dev(torch, synth.gate_batch_x(batch))
+        y = torch.empty((batch, blobs[g].rows), dtype=torch.bfloat16, device="cuda")
+        calls = [lbf.prepare(r[g], x, lbf.LBF_BF16, outs=y) for r in rot]
+        r = _timed(torch, calls, algorithmic_bytes(blobs[g], batch, 2))
+        r["path"] = "gemv" if batch <= 8 else "gemm_mfma_16x16x32_bf16"
+        r["raw_bf16_linear_us"] = round(time_region(torch, lambda i: torch.nn.functional.linear(x, wraw[i % 4]), 30, 5)
+                                        * 1e3, 2)
+        res["gate_proj_b%d" % batch] = r
+        log("gate_proj batch %d: %.2f us (%.3f of 8 TB/s), raw BF16 F.linear %.2f us"
+            % (batch, r["us"], r["frac"], r["raw_bf16_linear_us"]))
+    del wraw
+    Wx = [synth.expert_tensor(e) for e in range(64)]
+    ex = [lbf.encode(dev(torch, W)) for W in Wx]
+    exr = [ex] + [[lbf.Blob(b.desc, b.data.clone()) for b in ex] for _ in range(3)]
+    xe = [dev(torch, synth.expert_x(e)) for e in range(64)]
+    ye = [torch.empty((4, b.rows), dtype=torch.float32, device="cuda") for b in ex]
+    calls = [lbf.prepare(r, xe, lbf.LBF_F32, outs=ye) for r in exr]
+    r = _timed(torch, calls, sum(algorithmic_bytes(b, 4, 4) for b in ex), 20)
+    r.update({"groups": 64, "launches": 1, "coded_bytes": sum(b.nbytes for b in ex), "escapes": sum(b.n_esc for b in ex)})
+    res["experts64_b4"] = r
+    log("64 experts at batch 4: %.2f us (%.3f of 8 TB/s)" % (r["us"], r["frac"]))
+    del ex, exr, calls, Wx
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_legs(synth, Ws):
+    """The CPU oracle's workloads beside the headline: the single 1024 x 1024
+    tensor, gate_proj at every batch of the sweep, a sample of the 64 experts
+    at batch 4 (every fourth Gaussian expert plus the Laplace and all-patterns
+    ones), and encoding the layer."""
+    W0, x0 = synth.single_tensor()
+    g = Ws[synth.GATE]
+    legs = {"single_1024x1024_b1": ("single 1024x1024 tensor: oracle decode + float64 matvec at batch 1",
+                                    [("dm", W0, x0)])}
+    for b in (1, 2, 4, 8, 16, 32, 64):
+        legs["gate_proj_b%d" % b] = ("gate_proj 14336x4096: oracle decode + float64 matvec at batch %d" % b,
+                                     [("dm", g, synth.gate_batch_x(b))])
+    es = list(range(0, 62, 4)) + [62, 63]
+    legs["experts64_b4_sample"] = ("%d of the 64 experts (1536x4096): oracle decode + float64 matvec at batch 4"
+                                   % len(es), [("dm", synth.expert_tensor(e), synth.expert_x(e)) for e in es])
+    legs["encode_layer"] = ("oracle encode of the 7 layer tensors", [("enc", W) for W in Ws])
+    return legs
 
 
 def extras(torch, lbf, synth, Ws, blobs, rot, copies, args):
