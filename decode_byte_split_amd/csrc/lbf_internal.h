@@ -79,9 +79,9 @@ hipError_t launch_hpack(const lbf_desc& d, const uint8_t* blob, const HCode& cod
 hipError_t launch_hfill(const lbf_hdesc& h, uint8_t* blob, hipStream_t s);
 hipError_t launch_hdecode(const lbf_hdesc& h, const HCode& code, const uint8_t* blob, uint16_t* out, hipStream_t s);
 
-// lbf_gemm stages each wave's tile index words (16 rows x cols / 1024 tiles)
-// in LDS; rows longer than this many tiles are not supported.
-constexpr uint32_t kGemmMaxTiles = 64;
+// lbf_gemm keeps the byte offsets of 16 rows (or x rows) of a tensor in 32
+// bits; rows longer than this many tiles (16,777,216 columns) are not supported.
+constexpr uint32_t kGemmMaxTiles = 16384;
 
 // Workspace layout of lbf_encode: hist[256] u32, then tile counts u32[n_tiles].
 constexpr uint64_t kWorkHistBytes = 1024;

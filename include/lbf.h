@@ -221,7 +221,7 @@ int lbf_gemv_swiglu(const lbf_desc* gate_desc, const void* d_gate_blob, const lb
  * "How does this compare with prior lossless systems?": a fused
  * decompression-GEMM.)  Arguments and layouts as lbf_gemv; batch 9..256
  * (LBF_E_INVAL otherwise).  Requires cols_g % 1024 == 0 (LBF_E_SHAPE) and
- * cols_g <= 65536 (LBF_E_UNSUPPORTED).  Batches above 64 run as several
+ * cols_g <= 16777216 (LBF_E_UNSUPPORTED).  Batches above 64 run as several
  * launches of up to 64 columns, each reading the coded weights once.
  */
 int lbf_gemm(const lbf_desc* descs, const void* const* d_blobs, int n_groups, const void* const* d_x,
