@@ -9,10 +9,12 @@
 // compression or Q8 GGUF: which should you deploy?", on fleets whose
 // bottleneck is weight bandwidth), so both kernels here are HBM streams:
 //
-//  * k_gemv_ring (x of every tensor of the call fits in 128 KiB of LDS): one
-//    workgroup per CU (16 waves), rows dealt to CUs, waves take
-//    rows from an LDS counter and stream them through a three-slot register
-//    ring (details at the kernel);
+//  * k_gemv_ring (x of each tensor fits in 128 KiB of LDS): one workgroup
+//    per CU (16 waves); the tensors are cut into teams whose x fits in LDS
+//    together (one team when all of it does), each team gets CUs in
+//    proportion to its coded bytes, its rows are dealt to those CUs, and
+//    waves take rows from an LDS counter and stream them through a
+//    three-slot register ring (details at the kernel);
 //  * k_gemv (everything else): persistent workgroups, each taking one
 //    contiguous, cost-balanced range of work units across the launch's
 //    tensors; a unit is `phases` consecutive rows of one tensor, all K; each
@@ -467,20 +469,24 @@ constexpr int kRingSlots = 3;
 constexpr uint32_t kRingXMax = 131072;  // x area; with the wave slots 144 KiB of the 160 KiB LDS
 
 // Ring launch: the group records, rows dealt in record order (the launcher
-// puts the longest rows first).  In each record's aux word, bit 1 marks the
-// first group of each distinct x array (staged once) and bits 8..31 hold the
-// LDS byte offset of the group's x.
+// puts the longest rows first).  Team t is groups [team_g0[t],
+// team_g0[t + 1]) and workgroups [wg_begin[t], wg_begin[t + 1]); its rows
+// are a contiguous range of the launch's row space, dealt over its
+// workgroups only, and each of its workgroups stages the x of its groups
+// alone.  In each record's aux word, bit 1 marks the team's first group of
+// each distinct x array (staged once) and bits 8..31 hold the LDS byte
+// offset of the group's x (a multiple of 1024).
 constexpr uint32_t kAuxStageX = 2u;
-constexpr uint8_t kNoBlock = 0xFF;
 struct RingLaunch {
   GroupArg g[LBF_MAX_GROUPS];
-  uint32_t gtab[LBF_MAX_GROUPS];   // group table entry of each group (group_entry)
-  uint32_t xblk[kRingXMax / 4096];  // group whose x fills each 1 KiB block of the LDS x area, 4 blocks a word (stage_x)
+  uint32_t gtab[LBF_MAX_GROUPS];  // group table entry of each group (group_entry)
+  void* h;                        // gated product (g[0] = gate, g[1] = up): h[b, r] = silu(gate) * up
   uint32_t n_rows;
-  int n_groups, y_bf16;
-  void* h;  // gated product (g[0] = gate, g[1] = up): h[b, r] = silu(gate) * up
+  int n_groups, n_teams, y_bf16;
+  uint32_t wg_begin[LBF_MAX_GROUPS + 1];
+  uint32_t team_g0[LBF_MAX_GROUPS + 1];
 };
-static_assert(sizeof(RingLaunch) <= 3072, "kernel arguments stay well inside the 4 KiB limit");
+static_assert(sizeof(RingLaunch) <= 3584, "kernel arguments stay inside the 4 KiB limit");
 static_assert(LBF_MAX_GROUPS <= 64, "the ring kernel keeps one group per lane");
 
 template <int C>
@@ -574,36 +580,28 @@ __device__ __forceinline__ void load_data(Slot<C>& s, const RingLaunch& L, const
   load_planes(s, L, p, lane);
 }
 
-// x of every group whose aux word says so, from memory straight into LDS
-// (buffer loads to LDS: no registers, one wait before the barrier).  The
-// staged x arrays lie back to back in the LDS x area in 1 KiB blocks: block
-// j is bytes [1024 j, 1024 j + 1024), and L.xblk[j] names the group whose x
-// it holds (kNoBlock past the last).  In a group's x area, element (b, t,
-// lane, half) is at ((b T + t) 2 + half) 1024 + 16 lane: block (b, t, half)
-// is one load instruction of a wave, lane l bringing the 16 bytes at
-// x + b cols + t 1024 + 16 l + 8 half (bf16 elements).  Block j is loaded by
-// wave j % W.  EXACT: every wave issues exactly kRingXMax / 1024 / W loads
-// (unrolled), so the number of loads in flight is known at compile time: one
-// with no block gets a zero-length range (no memory access) and lands in
-// `spare`, 1 KiB of LDS nothing reads before the barrier.  Otherwise a
-// rolled loop issues only the blocks there are (fewer registers; used where
-// x is loaded before everything else and waited for with all of it).
-template <int B, int W, bool EXACT>
-__device__ __forceinline__ void stage_x(const RingLaunch& L, uint8_t* smem, uint8_t* spare, uint32_t wave, int lane) {
-  constexpr int kXLoads = (int)(kRingXMax / kTile) / W;
-  constexpr int kUnroll = EXACT ? kXLoads : 1;
-#pragma unroll kUnroll
-  for (int i = 0; i < kXLoads; i++) {
-    const uint32_t j = wave + (uint32_t)(W * i);
-    const uint32_t k = (L.xblk[j >> 2] >> (8u * (j & 3u))) & 0xFFu;  // a word: one scalar load
-    const bool have = k != kNoBlock;  // uniform
-    if (!EXACT && !have) break;  // blocks are filled from 0 up
-    const GroupArg& G = L.g[have ? k : 0u];
-    const uint32_t jj = have ? j - (G.aux >> 18) : 0u;  // block within the group's x (x_off / 1024)
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(G.x, have ? (uint32_t)B * G.tiles * 2u * kTile : 0u);
-    uint8_t* dst = have ? smem + (size_t)j * kTile : spare;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)dst, 16,
-                                             (uint32_t)lane * 32u + (jj & 1u) * 16u, (jj >> 1) * 2048u, 0, 0);
+// x of every group of [g_lo, g_hi) whose aux word says so, from memory
+// straight into LDS (buffer loads to LDS: no registers, one wait before the
+// barrier), at the LDS offset in its aux word.  In a group's x area, element
+// (b, t, lane, half) is at ((b T + t) 2 + half) 1024 + 16 lane: 1 KiB block
+// jj = (b T + t) 2 + half is one load instruction of a wave, lane l bringing
+// the 16 bytes at x + b cols + t 1024 + 16 l + 8 half (bf16 elements).  The
+// blocks of the range's x arrays, counted one after the other, go to the
+// waves in turn.
+template <int B, int W>
+__device__ __forceinline__ void stage_x(const RingLaunch& L, uint8_t* smem, uint32_t g_lo, uint32_t g_hi,
+                                        uint32_t wave, int lane) {
+  uint32_t base = 0;  // blocks of the arrays before this one
+  for (uint32_t g = g_lo; g < g_hi; g++) {
+    const GroupArg& G = L.g[g];
+    if (!(G.aux & kAuxStageX)) continue;  // uniform
+    const uint32_t nb = (uint32_t)B * G.tiles * 2u;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(G.x, nb * (uint32_t)kTile);
+    uint8_t* const dst = smem + (G.aux >> 8);
+    for (uint32_t jj = (wave + W - base % W) % W; jj < nb; jj += W)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)(dst + (size_t)jj * kTile),
+                                               16, (uint32_t)lane * 32u + (jj & 1u) * 16u, (jj >> 1) * 2048u, 0, 0);
+    base += nb;
   }
 }
 
@@ -661,21 +659,37 @@ __device__ __forceinline__ bool ring_round(F& f) {
   }
 }
 
-template <int B, int W, bool GATED, int C, int N>
+template <int B, int W, bool GATED, int C, int N, bool TEAMS>
 __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const uint32_t wave = uniform(threadIdx.x >> 6);
   const int lane = lane_id();
   uint8_t* slot_lds = smem + kRingXMax + wave * kEscSlot;
   uint32_t* lctr = reinterpret_cast<uint32_t*>(smem + kRingXMax + W * kEscSlot);
+  // TEAMS: this workgroup's team, its groups, workgroups and rows (teams
+  // ending at or before this workgroup counted by a ballot: a search loop
+  // here costs the main loop registers).  Otherwise one team: every group,
+  // every workgroup, every row.
+  uint32_t g_lo = 0, g_hi = (uint32_t)L.n_groups, q0 = 0, n_wg = gridDim.x, row_hi = L.n_rows;
+  if constexpr (TEAMS) {
+    const uint32_t WB = lane < L.n_teams ? L.wg_begin[lane + 1] : ~0u;
+    const uint32_t t = (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(WB <= blockIdx.x));
+    g_lo = L.team_g0[t];
+    g_hi = L.team_g0[t + 1];
+    const uint32_t wg0 = L.wg_begin[t];
+    n_wg = L.wg_begin[t + 1] - wg0;
+    row_hi = g_hi >= (uint32_t)L.n_groups ? L.n_rows : L.gtab[g_hi] >> 6;
+    q0 = (L.gtab[g_lo] >> 6) + blockIdx.x - wg0;
+  }
   // x first: it depends on nothing but the launch record, and every wave
   // waits for it before its first product
-  stage_x<B, W, false>(L, smem, slot_lds, wave, lane);
+  stage_x<B, W>(L, smem, g_lo, g_hi, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
   const uint32_t GR = GATED ? 0u : group_regs(L, lane);  // the gated launch has one row space
 
-  // rows of this CU: blockIdx.x + k * gridDim.x; the wave's first two come
-  // from k = wave, wave + 16, the rest from the LDS counter (starts at 32)
+  // rows of this CU: the team's row_lo + b + k * n_wg (b: the workgroup
+  // within the team); the wave's first two come from k = wave, wave + 16,
+  // the rest from the LDS counter (starts at 32)
   uint32_t k_static = 0;
   auto next_row = [&]() -> Pos {
     uint32_t k;
@@ -686,12 +700,17 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
       if (lane == 0) v = atomicAdd(lctr, 1u);
       k = uniform(v);
     }
-    // workgroups go round-robin over the 8 XCDs: give each XCD a contiguous
-    // block of gridDim.x / 8 consecutive rows per round
-    const uint32_t b = blockIdx.x, per = gridDim.x >> 3;
-    const uint32_t cu = (gridDim.x & 7u) ? b : (b & 7u) * per + (b >> 3);
-    const uint64_t q = cu + (uint64_t)k * gridDim.x;
-    return row_pos<GATED, C>(L, GR, q < L.n_rows ? (uint32_t)q : L.n_rows);
+    uint64_t q;
+    if constexpr (TEAMS) {
+      q = q0 + (uint64_t)k * n_wg;
+    } else {
+      // workgroups go round-robin over the 8 XCDs: give each XCD a contiguous
+      // block of gridDim.x / 8 consecutive rows per round
+      const uint32_t b = blockIdx.x, per = gridDim.x >> 3;
+      const uint32_t cu = (gridDim.x & 7u) ? b : (b & 7u) * per + (b >> 3);
+      q = cu + (uint64_t)k * gridDim.x;
+    }
+    return row_pos<GATED, C>(L, GR, q < row_hi ? (uint32_t)q : L.n_rows);
   };
   auto advance = [&](const Pos& p) -> Pos {
     if (p.valid && p.c + C < p.T) {
@@ -873,16 +892,23 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
 // 16 waves a workgroup (4 per SIMD, <= 128 VGPRs each) for every batch:
 // above batch 4 only two batch rows of x are read before a tile's decode and
 // the others one at a time after it, which keeps batch 8 within 128 VGPRs.
-template <int B, bool GATED = false>
+template <int B, bool GATED = false, bool TEAMS = false>
 static hipError_t run_ring_kernel(RingLaunch& L, hipStream_t s) {
   constexpr int W = kRingWaves, C = kRingTiles, N = kRingSlots;
   const uint32_t lds = kRingXMax + W * kEscSlot + 16;
   int cus = 0;
   hipError_t e = device_cus(&cus);
-  if (e == hipSuccess) e = open_dynamic_lds(reinterpret_cast<const void*>(&k_gemv_ring<B, W, GATED, C, N>), (int)lds);
+  if (e == hipSuccess) e = open_dynamic_lds(reinterpret_cast<const void*>(&k_gemv_ring<B, W, GATED, C, N, TEAMS>), (int)lds);
   if (e != hipSuccess) return e;
-  const uint32_t grid = (uint32_t)std::min<uint64_t>((uint64_t)cus, L.n_rows);
-  hipLaunchKernelGGL((k_gemv_ring<B, W, GATED, C, N>), dim3(grid), dim3(W * kWave), lds, s, L);
+  if (L.n_teams == 0) {  // one team: every group, one workgroup per CU
+    L.n_teams = 1;
+    L.team_g0[0] = 0;
+    L.team_g0[1] = (uint32_t)L.n_groups;
+    L.wg_begin[0] = 0;
+    L.wg_begin[1] = (uint32_t)std::min<uint64_t>((uint64_t)cus, L.n_rows);
+  }
+  const uint32_t grid = L.wg_begin[L.n_teams];
+  hipLaunchKernelGGL((k_gemv_ring<B, W, GATED, C, N, TEAMS>), dim3(grid), dim3(W * kWave), lds, s, L);
   return hipGetLastError();
 }
 
@@ -896,11 +922,9 @@ hipError_t launch_gemv_gated(const GroupArg& gate, const GroupArg& up, int batch
   L.g[0].aux = (gate.aux & kAuxContig) | kAuxStageX;  // one x for both, at LDS offset 0
   L.g[1].aux = up.aux & kAuxContig;
   L.gtab[0] = L.gtab[1] = 0u;  // one row space (unused)
-  const uint32_t blocks = (uint32_t)batch * gate.tiles * 2u;
-  for (uint32_t j = 0; j < kRingXMax / 4096; j++) L.xblk[j] = 0u;
-  for (uint32_t j = blocks; j < kRingXMax / 1024; j++) L.xblk[j >> 2] |= (uint32_t)kNoBlock << (8 * (j & 3));
   L.n_rows = gate.rows;
   L.n_groups = 2;
+  L.n_teams = 0;
   L.y_bf16 = h_dtype == LBF_BF16;
   L.h = h;
   switch (batch) {
@@ -915,46 +939,104 @@ hipError_t launch_gemv_gated(const GroupArg& gate, const GroupArg& up, int batch
   }
 }
 
-// Ring path if x of all groups (distinct arrays) fits in LDS.
+// Ring path if x of each group fits in LDS.  Groups, longest rows first,
+// are cut into teams whose distinct x arrays fit in LDS together (one team
+// when all of them do; as few as possible otherwise: a team's time is set
+// by its workgroup count, and one workgroup more or less matters less the
+// more a team has).  Each team gets workgroups in proportion to its cost
+// (coded bytes, escapes counted twice: they are read and placed), at least
+// one and at most one a row; one workgroup per CU in all.
 static hipError_t launch_ring(const GroupArg* groups, int n_groups, int batch, int y_dtype, bool& used,
                               hipStream_t s) {
   used = false;
   RingLaunch L;
-  uint64_t x_bytes = 0;  // 64-bit: batch * cols * 2 can pass 2^32 for one very wide row
   uint64_t rows = 0;
-  for (uint32_t j = 0; j < kRingXMax / 4096; j++) L.xblk[j] = 0xFFFFFFFFu;  // kNoBlock in every byte
   // longest rows first: rows are handed out in this order, so the coarsest
   // units are taken early and the last ones are the shortest
   int order[LBF_MAX_GROUPS];
   for (int g = 0; g < n_groups; g++) order[g] = g;
   std::stable_sort(order, order + n_groups, [&](int a, int b) { return groups[a].tiles > groups[b].tiles; });
+  int cus = 0;
+  if (const hipError_t e = device_cus(&cus); e != hipSuccess) return e;
+  int n_teams = 0;
+  uint64_t x_bytes = 0;  // 64-bit: batch * cols * 2 can pass 2^32 for one very wide row
+  uint64_t team_work[LBF_MAX_GROUPS] = {}, team_rows[LBF_MAX_GROUPS] = {};
   for (int g = 0; g < n_groups; g++) {
     const GroupArg& G = groups[order[g]];
-    int same = -1;  // an earlier group with the same x array (pointer and width)
-    for (int k = 0; k < g && same < 0; k++)
+    const uint64_t xb = (uint64_t)batch * G.tiles * kTile * 2;
+    if (xb > kRingXMax) return hipSuccess;  // this x alone does not fit
+    int same = -1;  // an earlier group of the current team with the same x array (pointer and width)
+    for (int k = n_teams ? L.team_g0[n_teams - 1] : 0; k < g && same < 0; k++)
       if ((L.g[k].aux & kAuxStageX) && L.g[k].x == G.x && L.g[k].tiles == G.tiles) same = k;
+    if (n_teams == 0 || (same < 0 && x_bytes + xb > kRingXMax)) {  // a new team
+      L.team_g0[n_teams++] = (uint32_t)g;
+      x_bytes = 0;
+      same = -1;
+    }
     L.g[g] = G;
     L.g[g].aux = G.aux & kAuxContig;
     if (same >= 0) {
       L.g[g].aux |= L.g[same].aux & ~0xFFu;
     } else {
-      const uint64_t xb = (uint64_t)batch * G.tiles * kTile * 2;
-      if (x_bytes + xb > kRingXMax) return hipSuccess;
       L.g[g].aux |= kAuxStageX | (uint32_t)(x_bytes << 8);
-      for (uint64_t j = x_bytes / 1024; j < (x_bytes + xb) / 1024; j++)
-        L.xblk[j >> 2] = (L.xblk[j >> 2] & ~(0xFFu << (8 * (j & 3)))) | ((uint32_t)g << (8 * (j & 3)));
       x_bytes += xb;
     }
     if (rows + G.rows >= kRingMaxRows) return hipSuccess;
     L.gtab[g] = group_entry((uint32_t)rows, G.tiles);
     rows += G.rows;
+    team_work[n_teams - 1] += (uint64_t)G.rows * G.tiles * (kTile + kTile / 2) + 2ull * G.n_esc;
+    team_rows[n_teams - 1] += G.rows;
   }
-  if (rows >= kRingMaxRows) return hipSuccess;
+  if (rows >= kRingMaxRows || rows == 0) return hipSuccess;
+  L.team_g0[n_teams] = (uint32_t)n_groups;
+  L.n_teams = n_teams;
+  // workgroups: the CUs shared by cost, each team at least one and at most
+  // one a row; what rounding leaves goes to the largest remainders
+  uint64_t total = 0;
+  for (int t = 0; t < n_teams; t++) total += team_work[t];
+  uint32_t n_wg[LBF_MAX_GROUPS];
+  uint64_t rem[LBF_MAX_GROUPS];
+  uint64_t given = 0;
+  for (int t = 0; t < n_teams; t++) {
+    const uint64_t share = (uint64_t)cus * team_work[t];
+    n_wg[t] = (uint32_t)std::min<uint64_t>(team_rows[t], std::max<uint64_t>(1, share / total));
+    rem[t] = share % total;
+    given += n_wg[t];
+  }
+  while (given < (uint64_t)cus) {
+    int best = -1;
+    for (int t = 0; t < n_teams; t++)
+      if (n_wg[t] < team_rows[t] && (best < 0 || rem[t] > rem[best])) best = t;
+    if (best < 0) break;
+    n_wg[best]++;
+    rem[best] = 0;
+    given++;
+  }
+  uint32_t wg = 0;
+  for (int t = 0; t < n_teams; t++) {
+    L.wg_begin[t] = wg;
+    wg += n_wg[t];
+  }
+  L.wg_begin[n_teams] = wg;
   L.n_rows = (uint32_t)rows;
   L.n_groups = n_groups;
   L.y_bf16 = y_dtype == LBF_BF16;
   L.h = nullptr;
   used = true;
+  if (n_teams > 1) {
+    switch (batch) {
+      case 1: return run_ring_kernel<1, false, true>(L, s);
+      case 2: return run_ring_kernel<2, false, true>(L, s);
+      case 3: return run_ring_kernel<3, false, true>(L, s);
+      case 4: return run_ring_kernel<4, false, true>(L, s);
+      case 5: return run_ring_kernel<5, false, true>(L, s);
+      case 6: return run_ring_kernel<6, false, true>(L, s);
+      case 7: return run_ring_kernel<7, false, true>(L, s);
+      default: return run_ring_kernel<8, false, true>(L, s);
+    }
+  }
+  // one team: every workgroup deals every row (the kernel without teams)
+  L.n_teams = 0;
   switch (batch) {
     case 1: return run_ring_kernel<1>(L, s);
     case 2: return run_ring_kernel<2>(L, s);

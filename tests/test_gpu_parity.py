@@ -295,6 +295,32 @@ def test_gemv_tiny_groups_share_x(env, batch):
     check_product(ys[31], y_ref, a_ref, False)
 
 
+@pytest.mark.parametrize("batch", [3, 8])
+def test_gemv_teams_x_over_lds(env, batch):
+    """Tensors whose x arrays together pass the 128 KiB LDS x area, so the
+    call is split into teams of CUs that each stage only their tensors' x:
+    mixed widths and row counts (one-row tensors: teams with fewer rows than
+    CUs), one x array shared by tensors that land in different teams, an
+    escape-dense all-patterns tensor.  Every output matches the oracle."""
+    torch, lbf = env
+    rng = np.random.default_rng([31, batch])
+    shapes = [(200, 8192), (1, 8192), (150, 4096), (37, 8192), (1, 1024), (90, 6144), (64, 8192), (3, 2048),
+              (120, 8192), (45, 5120)]
+    Ws, xs = [], []
+    shared = synth.activations(rng, batch, 8192)
+    for i, (rows, cols) in enumerate(shapes):
+        Ws.append(synth.all_patterns(rows, cols) if i == 6 else synth.gaussian(rng, rows, cols, 0.02, 0.003, 100.0))
+        xs.append(shared if cols == 8192 and i % 3 == 0 else synth.activations(rng, batch, cols))
+    say("gemv teams, B=%d, %d KiB of x" % (batch, sum(x.nbytes for x in xs) // 1024))
+    blobs = [lbf.from_host_blob(O.encode(W)) for W in Ws]
+    xd = {}
+    ys = lbf.gemv(blobs, [xd.setdefault(id(x), dev(torch, x)) for x in xs], lbf.LBF_F32)
+    torch.cuda.synchronize()
+    for W, x, y in zip(Ws, xs, ys):
+        y_ref, a_ref = O.matvec(W, x)
+        check_product(y, y_ref, a_ref, False)
+
+
 @pytest.mark.parametrize("batch", [1, 3, 8])
 def test_gemv_same_x_pointer_different_widths(env, batch):
     """Two groups given the same x pointer with different column counts read
