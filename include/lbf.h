@@ -188,6 +188,9 @@ int lbf_decode(const lbf_desc* desc, const void* d_blob, void* d_w_out, hipStrea
  * table from the blob's own header copy, so the device header must equal
  * descs[g] (as lbf_encode writes it; lbf_verify checks it).  A device header
  * that differs can give wrong outputs but no access outside the buffers.
+ * A batch-8 call whose escapes are at most 1 % of its weights runs on the
+ * MFMA kernel of lbf_gemm (faster there); its fp32 sums then add in that
+ * kernel's fixed order, a different one from the other batches'.
  */
 int lbf_gemv(const lbf_desc* descs, const void* const* d_blobs, int n_groups, const void* const* d_x,
              int batch, void* const* d_y, int y_dtype, hipStream_t s);
