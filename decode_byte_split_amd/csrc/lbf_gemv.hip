@@ -681,11 +681,21 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
     row_hi = g_hi >= (uint32_t)L.n_groups ? L.n_rows : L.gtab[g_hi] >> 6;
     q0 = (L.gtab[g_lo] >> 6) + blockIdx.x - wg0;
   }
-  // x first: it depends on nothing but the launch record, and every wave
-  // waits for it before its first product
-  stage_x<B, W>(L, smem, g_lo, g_hi, wave, lane);
-  __builtin_amdgcn_sched_barrier(0);
-  const uint32_t GR = GATED ? 0u : group_regs(L, lane);  // the gated launch has one row space
+  // Start-up order.  Batch 1 (kChunkFirst): the group table, then the first
+  // chunk's index words and planes, then x, all before any wait, so the
+  // planes stream while x is staged (8B layer: 55.2 -> 54.6 us; a single
+  // tensor needs no table load).  Larger batches: x first, the group table
+  // load after it and waited for with it (the first order costs gate_proj
+  // at batch 4 half a microsecond, and the single-tensor shortcut pushes
+  // those kernels past their registers).
+  constexpr bool kChunkFirst = B == 1;
+  if constexpr (!kChunkFirst) {
+    stage_x<B, W>(L, smem, g_lo, g_hi, wave, lane);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const uint32_t GR = GATED ? 0u  // the gated launch has one row space
+                      : (kChunkFirst && L.n_groups == 1) ? (lane == 0 ? group_entry(0u, L.g[0].tiles) : ~0u)
+                                                         : group_regs(L, lane);
 
   // rows of this CU: the team's row_lo + b + k * n_wg (b: the workgroup
   // within the team); the wave's first two come from k = wave, wave + 16,
@@ -745,14 +755,25 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
   // in.  At batch 1 two chunks per wave are filled; larger batches have no
   // registers for a second one, which comes with the first step.
   constexpr int F = B == 1 ? 2 : 1;  // chunks filled at start-up
-  pp[0] = next_row();  // the group table load is waited for here; x has had the same time
+  pp[0] = next_row();  // the group table load is waited for here
   pp[1] = advance(pp[0]);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's x is in LDS
-  __builtin_amdgcn_sched_barrier(0);
-  load_idx(sl[0], L, pp[0], lane);
-  load_idx(sl[1], L, pp[1], lane);
-  load_planes(sl[0], L, pp[0], lane);
-  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (kChunkFirst) {
+    __builtin_amdgcn_sched_barrier(0);
+    load_idx(sl[0], L, pp[0], lane);
+    load_idx(sl[1], L, pp[1], lane);
+    load_planes(sl[0], L, pp[0], lane);
+    __builtin_amdgcn_sched_barrier(0);
+    stage_x<B, W>(L, smem, g_lo, g_hi, wave, lane);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's x (and the first chunk) is in
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's x is in LDS
+    __builtin_amdgcn_sched_barrier(0);
+    load_idx(sl[0], L, pp[0], lane);
+    load_idx(sl[1], L, pp[1], lane);
+    load_planes(sl[0], L, pp[0], lane);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   if (threadIdx.x == 0) *lctr = 2u * W;
   __syncthreads();
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * C));  // the index words are in
