@@ -35,7 +35,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 METRIC = "fused decode-GEMV BF16-equiv weight GB/s + % HBM roofline, 8B-shaped layer"
 COUNTERS = os.path.join(ROOT, "profiles", "gemv_ring_layer_b1_counters.json")
-KERNEL = "lbf::k_gemv_ring<1, 16, false, 4, 3>"
+KERNEL = "lbf::k_gemv_ring<1, 16, false, 4, 3, false>"
 KERNEL_SOURCES = ("decode_byte_split_amd/csrc/lbf_gemv.hip", "decode_byte_split_amd/csrc/lbf_device.h")
 
 
