@@ -60,6 +60,14 @@ def algorithmic_bytes(blob, batch: int, y_bytes: int) -> int:
     return n + (n + 1) // 2 + 4 * (n_tiles + 1) + blob.n_esc + 2 * batch * blob.cols + y_bytes * batch * blob.rows
 
 
+def product_path(blob, batch: int) -> str:
+    """Which kernel lbf_gemv / lbf_gemm run for one tensor: the fused GEMV up
+    to batch 8, the MFMA GEMM above, and at batch 8 when escapes are at most
+    1 % of the weights."""
+    mfma = batch > 8 or (batch == 8 and 100 * blob.n_esc <= blob.rows * blob.cols)
+    return "gemm_mfma_16x16x32_bf16" if mfma else "gemv"
+
+
 def dev(torch, a):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
 
@@ -511,7 +519,7 @@ def _timed(torch, calls, alg, steps=50):
 def config_keys(torch, lbf, synth, Ws, blobs, rot, copies):
     """The other workloads beside the headline, each with its own roofline
     fraction (algorithmic bytes / time against 8 TB/s): gate_proj (14336 x
-    4096) alone at batch 1, 8 (fused GEMV) and 16, 64 (fused GEMM on MFMA),
+    4096) alone at batch 1 (fused GEMV), 8, 16 and 64 (fused GEMM on MFMA),
     bf16 output, with torch's F.linear on the uncompressed tensor beside it;
     and the 64 expert tensors (1536 x 4096, escape-rate stress) in one grouped
     call at batch 4, fp32 output.  Rotation copies keep the working set past
@@ -524,7 +532,7 @@ def config_keys(torch, lbf, synth, Ws, blobs, rot, copies):
         y = torch.empty((batch, blobs[g].rows), dtype=torch.bfloat16, device="cuda")
         calls = [lbf.prepare(r[g], x, lbf.LBF_BF16, outs=y) for r in rot]
         r = _timed(torch, calls, algorithmic_bytes(blobs[g], batch, 2))
-        r["path"] = "gemv" if batch <= 8 else "gemm_mfma_16x16x32_bf16"
+        r["path"] = product_path(blobs[g], batch)
         r["raw_bf16_linear_us"] = round(time_region(torch, lambda i: torch.nn.functional.linear(x, wraw[i % 4]), 30, 5)
                                         * 1e3, 2)
         res["gate_proj_b%d" % batch] = r
@@ -628,9 +636,9 @@ def extras(torch, lbf, synth, Ws, blobs, rot, copies, args):
         alg = algorithmic_bytes(blobs[g], batch, 2)
         flops = 2.0 * batch * Ws[g].size
         ms_raw = time_region(torch, lambda i: torch.nn.functional.linear(x, wg[i % 4]), 30, 5)
-        # batch 8 runs on the MFMA kernel when escapes are at most 1 % of the weights
-        mfma = batch > 8 or (batch == 8 and 100 * blobs[g].n_esc <= Ws[g].size)
-        sweep[str(batch)] = {"path": "gemm_mfma" if mfma else "gemv", "us": round(ms * 1e3, 2),
+        path = product_path(blobs[g], batch)
+        mfma = path != "gemv"
+        sweep[str(batch)] = {"path": path, "us": round(ms * 1e3, 2),
                              "bf16_equiv_GBs": round(2 * Ws[g].size / (ms * 1e-3) / 1e9, 1),
                              "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                              "mfma_frac_of_2.5PF": round(flops / (ms * 1e-3) / 2.5e15, 4) if mfma else None,
@@ -842,7 +850,7 @@ def gate_batch(args):
            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
            "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": "gate_proj_14336x4096", "batch": B, "y_dtype": "bf16",
-                      "path": "gemv" if B <= 8 else "gemm_mfma_16x16x32_bf16", "rotation_copies": copies},
+                      "path": product_path(blob, B), "rotation_copies": copies},
            "roofline": {"bound": "hbm", "achieved": round(alg / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
                         "unit": "GB/s", "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                         "algorithmic_bytes_per_launch": alg},
