@@ -419,6 +419,22 @@ hipError_t launch_gemm(const GroupArg* groups, int n_groups, int batch, int y_dt
     L.g[g] = groups[g];
   }
   gemm_rows_per_wg(L.g, n_groups, cus);
+  // workgroups of the costliest groups first (blocks are dispatched in
+  // order, so the longest ones do not start last); cost of one workgroup:
+  // its coded bytes, escapes weighted for the ranked path
+  int perm[LBF_MAX_GROUPS];
+  uint64_t wcost[LBF_MAX_GROUPS];
+  for (int g = 0; g < n_groups; g++) {
+    perm[g] = g;
+    const uint64_t rpw = L.g[g].aux >> kAuxRowsShift, rows = std::max<uint64_t>(1, L.g[g].rows);
+    wcost[g] = rpw * L.g[g].tiles * (kTile + kTile / 2) + 64ull * L.g[g].n_esc * rpw / rows;
+  }
+  std::stable_sort(perm, perm + n_groups, [&](int a, int b) { return wcost[a] > wcost[b]; });
+  {
+    GroupArg tmp[LBF_MAX_GROUPS];
+    for (int g = 0; g < n_groups; g++) tmp[g] = L.g[perm[g]];
+    for (int g = 0; g < n_groups; g++) L.g[g] = tmp[g];
+  }
   uint64_t wg = 0;
   for (int g = 0; g < n_groups; g++) {
     const uint32_t rpw = L.g[g].aux >> kAuxRowsShift;
@@ -432,8 +448,9 @@ hipError_t launch_gemm(const GroupArg* groups, int n_groups, int batch, int y_dt
     const int nb = std::min(kGemmBatch, batch - b0);
     L.batch = nb;
     for (int g = 0; g < n_groups; g++) {
-      L.g[g].x = groups[g].x + (size_t)b0 * groups[g].tiles * kTile;
-      L.g[g].y = static_cast<uint8_t*>(groups[g].y) + (size_t)b0 * groups[g].rows * eb;
+      const GroupArg& o = groups[perm[g]];
+      L.g[g].x = o.x + (size_t)b0 * o.tiles * kTile;
+      L.g[g].y = static_cast<uint8_t*>(o.y) + (size_t)b0 * o.rows * eb;
     }
     hipError_t e;
     switch ((nb + 15) / 16) {
