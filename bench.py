@@ -72,14 +72,45 @@ def dev(torch, a):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
 
 
-def time_region(torch, fn, steps: int, warmup: int) -> float:
-    """Run fn(i) warmup times untimed, then steps times back to back between
-    two HIP events on the launch stream; returns ms per call.  One call is one
-    kernel launch here, so this is the mean launch duration (the gaps between
-    back-to-back launches are included, host marshalling is not: each call is
-    a single prepared ctypes call)."""
+def warm_gpu(torch, fn, min_ms: float, start: int = 0) -> int:
+    """Run fn back to back, in batches of 10 calls between HIP events, until
+    the GPU has spent at least min_ms on them; returns the number of calls.
+    The GPU needs tens of milliseconds of sustained load before its clocks
+    settle: a launch timed after a short warm-up reads several per cent
+    slow."""
+    n, spent = 0, 0.0
+    while spent < min_ms:
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(10):
+            fn(start + n)
+            n += 1
+        b.record()
+        b.synchronize()
+        spent += a.elapsed_time(b)
+    return n
+
+
+def time_torch_linear(torch, pairs_per_copy, steps: int = 30) -> float:
+    """torch's F.linear on uncompressed BF16 weights, the comparison lane:
+    the calls of rotation copy i % copies per step, back to back (ms per
+    step).  Replaying the same calls from HIP graphs measured slower, not
+    faster, so the host's dispatch is not what bounds them."""
+    F = torch.nn.functional
+    return time_region(torch, lambda i: [F.linear(x, w) for x, w in pairs_per_copy[i % len(pairs_per_copy)]], steps, 3)
+
+
+def time_region(torch, fn, steps: int, warmup: int, warm_ms: float = 30.0) -> float:
+    """Run fn(i) warmup times untimed (then on until the GPU has been busy
+    warm_ms with them), then steps times back to back between two HIP events
+    on the launch stream; returns ms per call.  One call is one kernel launch
+    here, so this is the mean launch duration (the gaps between back-to-back
+    launches are included, host marshalling is not: each call is a single
+    prepared ctypes call)."""
     for i in range(warmup):
         fn(i)
+    warmup += warm_gpu(torch, fn, warm_ms, warmup) if warm_ms > 0 else 0
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
@@ -350,7 +381,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--cpu-seconds", type=float, default=6.0)
     ap.add_argument("--no-configs", action="store_true", help="only the headline layer line (no gate_proj / expert "
                     "keys and no per-config CPU oracle legs)")
@@ -422,7 +453,9 @@ def main():
         copy_calibration(torch)
     calls = [lbf.prepare(r, xd, lbf.LBF_F32, outs=ys) for r in rot]
     step = lambda i: calls[i % copies]()
-    ms_step = time_region(torch, step, args.steps, args.warmup)
+    # exactly the requested warm-up here (500 launches by default: about
+    # 28 ms, enough for the clocks to settle)
+    ms_step = time_region(torch, step, args.steps, args.warmup, warm_ms=0)
     batch_ms = time_batches(torch, step, max(args.steps // 10, 5), 10, 3)
     ms_single, _ = time_each(torch, step, max(args.steps // 2, 10), 3)
     alg = sum(algorithmic_bytes(b, 1, 4) for b in blobs)
@@ -438,8 +471,7 @@ def main():
     # only streams them, with its own launch, ramp-up and tail
     same_us = alg / (read_ceiling(torch, 40, alg) * 1e9) * 1e6
     wrot = [[dev(torch, W) for W in Ws] for _ in range(4)]
-    raw_ms = time_region(torch, lambda i: [torch.nn.functional.linear(x, w) for x, w in zip(xd, wrot[i % 4])],
-                         20, 3)
+    raw_ms = time_torch_linear(torch, [list(zip(xd, wr)) for wr in wrot], 20)
     del wrot
     torch.cuda.empty_cache()
     log("read-stream ceiling %.1f GB/s; the same read over the launch's %d bytes %.2f us; raw BF16 F.linear layer "
@@ -533,8 +565,7 @@ def config_keys(torch, lbf, synth, Ws, blobs, rot, copies):
         calls = [lbf.prepare(r[g], x, lbf.LBF_BF16, outs=y) for r in rot]
         r = _timed(torch, calls, algorithmic_bytes(blobs[g], batch, 2))
         r["path"] = product_path(blobs[g], batch)
-        r["raw_bf16_linear_us"] = round(time_region(torch, lambda i: torch.nn.functional.linear(x, wraw[i % 4]), 30, 5)
-                                        * 1e3, 2)
+        r["raw_bf16_linear_us"] = round(time_torch_linear(torch, [[(x, w)] for w in wraw]) * 1e3, 2)
         res["gate_proj_b%d" % batch] = r
         log("gate_proj batch %d: %.2f us (%.3f of 8 TB/s), raw BF16 F.linear %.2f us"
             % (batch, r["us"], r["frac"], r["raw_bf16_linear_us"]))
@@ -616,11 +647,7 @@ def extras(torch, lbf, synth, Ws, blobs, rot, copies, args):
     xd = [dev(torch, synth.layer_x(m)) for m in range(len(Ws))]
     wrot = [wd] + [[w.clone() for w in wd] for _ in range(3)]
 
-    def raw(i):
-        for w, x in zip(wrot[i % 4], xd):
-            torch.nn.functional.linear(x, w)
-
-    ms = time_region(torch, raw, 20, 3)
+    ms = time_torch_linear(torch, [list(zip(xd, wr)) for wr in wrot], 20)
     res["raw_bf16_linear_layer"] = {"us": round(ms * 1e3, 2), "GBs": round(2 * n / (ms * 1e-3) / 1e9, 1),
                                     "hbm_frac": round(2 * n / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     del wd, wrot
@@ -635,7 +662,7 @@ def extras(torch, lbf, synth, Ws, blobs, rot, copies, args):
         ms = time_region(torch, lambda i: calls[i % copies](), 30, 5)
         alg = algorithmic_bytes(blobs[g], batch, 2)
         flops = 2.0 * batch * Ws[g].size
-        ms_raw = time_region(torch, lambda i: torch.nn.functional.linear(x, wg[i % 4]), 30, 5)
+        ms_raw = time_torch_linear(torch, [[(x, w)] for w in wg])
         path = product_path(blobs[g], batch)
         mfma = path != "gemv"
         sweep[str(batch)] = {"path": path, "us": round(ms * 1e3, 2),
