@@ -682,8 +682,10 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
     q0 = (L.gtab[g_lo] >> 6) + blockIdx.x - wg0;
   }
   // Start-up order.  Batch 1 (kChunkFirst): the group table, then the first
-  // chunk's index words and planes, then x, all before any wait, so the
-  // planes stream while x is staged (8B layer: 55.2 -> 54.6 us; a single
+  // chunk's index words and planes, the first two escape slices as soon as
+  // the index words are in, then x, so the planes stream while x is staged
+  // and the first decode waits for nothing else (8B layer: 55.2 -> 54.6 us,
+  // escape slices before x another 0.1 us, gate_proj 0.2 us; a single
   // tensor needs no table load).  Larger batches: x first, the group table
   // load after it and waited for with it (the first order costs gate_proj
   // at batch 4 half a microsecond, and the single-tensor shortcut pushes
@@ -763,8 +765,17 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
     load_idx(sl[1], L, pp[1], lane);
     load_planes(sl[0], L, pp[0], lane);
     __builtin_amdgcn_sched_barrier(0);
+    // the escape slices go out as soon as the index words are in (loads
+    // complete in order: they were issued first) and before x, so that the
+    // wait for x covers them: requested after x, they would queue behind
+    // the whole chip's plane traffic and hold up the first decode
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * C));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < F; i++) load_esc(sl[i], L, pp[i], ef[i], en[i], lane);
+    __builtin_amdgcn_sched_barrier(0);
     stage_x<B, W>(L, smem, g_lo, g_hi, wave, lane);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's x (and the first chunk) is in
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's x, the first chunk and the escapes are in
     __builtin_amdgcn_sched_barrier(0);
   } else {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's x is in LDS
@@ -776,12 +787,14 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
   }
   if (threadIdx.x == 0) *lctr = 2u * W;
   __syncthreads();
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * C));  // the index words are in
-  __builtin_amdgcn_sched_barrier(0);
-  // escapes before the second chunk's planes: loads complete in order, and
-  // the first step needs only chunk 0
+  if constexpr (!kChunkFirst) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * C));  // the index words are in
+    __builtin_amdgcn_sched_barrier(0);
+    // escapes before the second chunk's planes: loads complete in order, and
+    // the first step needs only chunk 0
 #pragma unroll
-  for (int i = 0; i < F; i++) load_esc(sl[i], L, pp[i], ef[i], en[i], lane);
+    for (int i = 0; i < F; i++) load_esc(sl[i], L, pp[i], ef[i], en[i], lane);
+  }
   if constexpr (F == 2) load_planes(sl[1], L, pp[1], lane);
 
   float acc[B][2];
