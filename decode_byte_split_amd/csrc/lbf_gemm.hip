@@ -206,6 +206,10 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void k_gemm(GemmLaunch L) {
     cur_first = e_first;
     cur_cnt = e_cnt;
     cur_e = e_byte[0] | e_byte[1] << 8 | e_byte[2] << 16 | e_byte[3] << 24;
+    // from here on these are plain register values: their loads are waited
+    // for once, here, and no later use (in loops, at joins) waits for the
+    // memory pipeline again
+    asm volatile("" : "+v"(cur_first), "+v"(cur_cnt), "+v"(cur_e));
     const uint32_t e0 = cur_e & 0xFFu;
     const uint32_t mask = cur_cnt >= 4 ? ~0u : (1u << (8 * cur_cnt)) - 1u;
     const bool fast = cur_cnt == 0 || (cur_cnt <= 4 && ((cur_e ^ (e0 * 0x01010101u)) & mask) == 0);
@@ -295,9 +299,14 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void k_gemm(GemmLaunch L) {
           for (int i = 0; i < 4; i++) {
             while (m[i]) {
               const uint32_t wi = 8u * (i & 1) + ((uint32_t)__builtin_ctzll(m[i]) >> 3);
-              const uint32_t e = pos < min(cnt, 4u) ? (e4 >> (8 * pos)) & 0xFFu
-                                                    : (pos < cnt ? (uint32_t)P.esc[first + pos] : 0u);
-              patch_exponent(i < 2 ? E0 : E1, wi, e);
+              // the first four escapes of the tile are in registers; only
+              // past them is the stream read (and only that path waits)
+              if (pos < min(cnt, 4u)) {
+                patch_exponent(i < 2 ? E0 : E1, wi, (e4 >> (8 * pos)) & 0xFFu);
+              } else {
+                const uint32_t e = pos < cnt ? (uint32_t)P.esc[first + pos] : 0u;
+                patch_exponent(i < 2 ? E0 : E1, wi, e);
+              }
               m[i] &= m[i] - 1;
               pos++;
             }
