@@ -14,7 +14,11 @@
 //  - a workgroup covers up to 64 rows (four MFMA row blocks of 16) of one
 //    tensor with 8 waves; the host sizes the row share so that a
 //    single-tensor launch has one workgroup per compute unit where it can
-//    (14336 rows: 256 workgroups of 56).  Wave w owns the half-tiles w,
+//    (14336 rows: 256 workgroups of 56).  With one block of 16 batch
+//    columns the registers allow four waves a SIMD: a workgroup then covers
+//    up to 32 rows (two row blocks) and each compute unit holds two
+//    (14336 rows: 512 workgroups of 28); more waves a SIMD hide more of the
+//    memory latency (gate_proj at batch 8: 25.5 -> 23.2 us).  Wave w owns the half-tiles w,
 //    w + 8, ... of K (columns [512 h, 512 h + 512) of every row), so the
 //    waves share nothing until the end, where their partial sums are added
 //    through LDS in wave order (a fixed order: bitwise reproducible);
@@ -64,9 +68,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 constexpr int kGemmWaves = 8;                       // waves per workgroup, one share of the half-tiles each
-constexpr int kGemmRB = 4;                          // MFMA row blocks of 16 per workgroup
-constexpr uint32_t kGemmMaxRows = 16 * kGemmRB;     // rows per workgroup at most
-constexpr uint32_t kGemmMinRows = 16;               // and at least (unless the tensor is smaller)
+constexpr uint32_t kGemmMinRows = 16;               // rows per workgroup at least (unless the tensor is smaller)
 constexpr int kGemmBatch = 64;                      // batch columns per launch
 constexpr uint32_t kGemmStep = 128;                 // columns per step
 constexpr uint32_t kHalfSteps = kTile / 2 / kGemmStep;  // steps per half-tile (4)
@@ -82,8 +84,9 @@ static_assert(sizeof(GemmLaunch) <= 3072, "kernel arguments stay well inside the
 
 // One step's coded chunks for one lane: per row block, weights 0..15 and
 // 16..31 of its 32 columns (raw) and their 32 codes (nibbles).
+template <int RB>
 struct Coded {
-  u32x4 raw0[kGemmRB], raw1[kGemmRB], nib[kGemmRB];
+  u32x4 raw0[RB], raw1[RB], nib[RB];
 };
 
 // 16 bytes a lane from a buffer straight into LDS: lane l's bytes land at
@@ -94,8 +97,14 @@ __device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t
                                            soffset, 0, 0);
 }
 
-template <int NB, int D>
-__global__ __launch_bounds__(kGemmWaves * kWave) void k_gemm(GemmLaunch L) {
+// RB row blocks of 16 a wave: RB = 4 with two waves a SIMD (one workgroup
+// a compute unit), RB = 2 with four (two workgroups a compute unit, more
+// waves to cover memory latency; used for one block of batch columns, where
+// the registers allow it).
+template <int NB, int D, int RB>
+__global__ __launch_bounds__(kGemmWaves * kWave) __attribute__((amdgpu_waves_per_eu(RB == 2 ? 4 : 1)))
+void k_gemm(GemmLaunch L) {
+  constexpr int kGemmRB = RB;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // the waves' partial sums
   const uint32_t wave = uniform(threadIdx.x >> 6);
   const int lane = lane_id();
@@ -141,7 +150,7 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void k_gemm(GemmLaunch L) {
     const uint32_t half = ht & 1u;
     return (ht >> 1) * kTile + half * (kTile / 2) + (half ? kHalfSteps - 1 - s : s) * kGemmStep;
   };
-  auto load_block = [&](Coded& C, int rb, uint32_t k) {
+  auto load_block = [&](Coded<RB>& C, int rb, uint32_t k) {
     const bool ok = k < n_steps;  // uniform
     const uint32_t c0 = ok ? col0_of(k) : 0u;
     const uint32_t vr = ok ? vo_raw : kOOB, vn = ok ? vo_nib : kOOB;
@@ -236,7 +245,7 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void k_gemm(GemmLaunch L) {
   // One step: the escape facts ahead, this step's x into registers (the
   // slot then takes the next step's x at once), then per row block: decode,
   // reload the block's registers for step k + D, multiply.
-  auto step = [&](Coded& C, uint32_t k) {
+  auto step = [&](Coded<RB>& C, uint32_t k) {
     const bool backward = ((wave + kGemmWaves * (k / kHalfSteps)) & 1u) != 0;
     if (k % kHalfSteps == 0) meta_take();  // a new half-tile: its escape facts
     // only the 3 * kGemmRB coded loads of the last step were issued after
@@ -335,17 +344,25 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void k_gemm(GemmLaunch L) {
 
   if (n_steps) {
     // x of step 0 goes before the coded loads, so that at least 3 * kGemmRB
-    // loads follow it before step 0 waits for it; every coded load of the
-    // ring goes out before the escape facts wait for their index words
+    // loads follow it before step 0 waits for it.  With four row blocks
+    // every coded load of the ring goes out before the escape facts wait for
+    // their index words; with two (four waves a SIMD, whose loads queue
+    // longer) only step 0's do, so that the escape facts and the next index
+    // words queue behind one step instead of the whole ring
+    constexpr int kFirst = RB == 2 ? 1 : D;
     meta_idx(0);
     dma_x(0);
-    Coded C[D];
+    Coded<RB> C[D];
 #pragma unroll
-    for (int d = 0; d < D; d++)
+    for (int d = 0; d < kFirst; d++)
 #pragma unroll
       for (int rb = 0; rb < kGemmRB; rb++) load_block(C[d], rb, d);
     meta_esc();
     meta_idx(1);
+#pragma unroll
+    for (int d = kFirst; d < D; d++)
+#pragma unroll
+      for (int rb = 0; rb < kGemmRB; rb++) load_block(C[d], rb, d);
     // n_steps is a multiple of 4, and D divides 4
     for (uint32_t k = 0; k < n_steps; k += D) {
 #pragma unroll
@@ -389,84 +406,104 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void k_gemm(GemmLaunch L) {
   }
 }
 
-template <int NB, int D>
+template <int NB, int D, int RB>
 static hipError_t run_gemm(const GemmLaunch& L, uint32_t grid, hipStream_t s) {
   constexpr int lds = kGemmWaves * NB * 4 * 1040;
-  const hipError_t e = open_dynamic_lds(reinterpret_cast<const void*>(&k_gemm<NB, D>), lds);
+  const hipError_t e = open_dynamic_lds(reinterpret_cast<const void*>(&k_gemm<NB, D, RB>), lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_gemm<NB, D>), dim3(grid), dim3(kGemmWaves * kWave), lds, s, L);
+  hipLaunchKernelGGL((k_gemm<NB, D, RB>), dim3(grid), dim3(kGemmWaves * kWave), lds, s, L);
   return hipGetLastError();
 }
 
 // Rows per workgroup of each group: a single tensor gets one workgroup per
-// compute unit where 16..64 rows a workgroup allow it; in a grouped launch
-// each tensor gets its share of the compute units by coded size.
-static void gemm_rows_per_wg(GroupArg* g, int n_groups, int cus) {
+// slot (slots = workgroups the compute units hold at once) where 16 ..
+// max_rows rows a workgroup allow it; in a grouped launch each tensor gets
+// its share of the slots by coded size.
+static void gemm_rows_per_wg(GroupArg* g, int n_groups, uint64_t slots, uint32_t max_rows) {
   uint64_t total = 0;
   for (int i = 0; i < n_groups; i++) total += (uint64_t)g[i].rows * g[i].tiles;
   for (int i = 0; i < n_groups; i++) {
     const uint64_t rows = g[i].rows;
-    const uint64_t lo = (rows + kGemmMaxRows - 1) / kGemmMaxRows, hi = (rows + kGemmMinRows - 1) / kGemmMinRows;
-    const uint64_t want = total ? ((uint64_t)cus * rows * g[i].tiles + total - 1) / total : 1;
+    const uint64_t lo = (rows + max_rows - 1) / max_rows, hi = (rows + kGemmMinRows - 1) / kGemmMinRows;
+    const uint64_t want = total ? (slots * rows * g[i].tiles + total - 1) / total : 1;
     const uint64_t n_wg = std::max<uint64_t>(1, std::min(std::max(want, lo), hi));
     const uint32_t rpw = (uint32_t)((rows + n_wg - 1) / n_wg);
     g[i].aux = (g[i].aux & ((1u << kAuxRowsShift) - 1)) | (rpw << kAuxRowsShift);
   }
 }
 
-// Batch columns go in slabs of up to 64 (each slab reads the coded weights
-// again); a slab of m columns runs ceil(m / 16) MFMA column blocks.
-hipError_t launch_gemm(const GroupArg* groups, int n_groups, int batch, int y_dtype, hipStream_t s) {
-  int cus = 0;
-  if (const hipError_t e = device_cus(&cus); e != hipSuccess) return e;
-  const uint32_t eb = y_dtype == LBF_BF16 ? 2u : 4u;
+// One launch layout: rows per workgroup for waves of RB row blocks, the
+// groups reordered so that the workgroups of the costliest come first
+// (blocks are dispatched in order, so the longest ones do not start last;
+// cost of one workgroup: its coded bytes, escapes weighted for the ranked
+// path), and each group's first workgroup.  perm[g] is the caller's index
+// of launch group g.
+struct GemmLayout {
   GemmLaunch L;
-  L.n_groups = n_groups;
-  L.y_bf16 = y_dtype == LBF_BF16;
-  for (int g = 0; g < n_groups; g++) {
-    if (groups[g].tiles > kGemmMaxTiles) return hipErrorNotSupported;
-    L.g[g] = groups[g];
-  }
-  gemm_rows_per_wg(L.g, n_groups, cus);
-  // workgroups of the costliest groups first (blocks are dispatched in
-  // order, so the longest ones do not start last); cost of one workgroup:
-  // its coded bytes, escapes weighted for the ranked path
   int perm[LBF_MAX_GROUPS];
+  uint64_t wg;
+};
+
+static void gemm_layout(GemmLayout& Y, const GroupArg* groups, int n_groups, int cus, int rb, int y_bf16) {
+  GemmLaunch& L = Y.L;
+  L.n_groups = n_groups;
+  L.y_bf16 = y_bf16;
+  for (int g = 0; g < n_groups; g++) L.g[g] = groups[g];
+  gemm_rows_per_wg(L.g, n_groups, (uint64_t)cus * (rb == 2 ? 2 : 1), 16u * rb);
   uint64_t wcost[LBF_MAX_GROUPS];
   for (int g = 0; g < n_groups; g++) {
-    perm[g] = g;
+    Y.perm[g] = g;
     const uint64_t rpw = L.g[g].aux >> kAuxRowsShift, rows = std::max<uint64_t>(1, L.g[g].rows);
     wcost[g] = rpw * L.g[g].tiles * (kTile + kTile / 2) + 64ull * L.g[g].n_esc * rpw / rows;
   }
-  std::stable_sort(perm, perm + n_groups, [&](int a, int b) { return wcost[a] > wcost[b]; });
-  {
-    GroupArg tmp[LBF_MAX_GROUPS];
-    for (int g = 0; g < n_groups; g++) tmp[g] = L.g[perm[g]];
-    for (int g = 0; g < n_groups; g++) L.g[g] = tmp[g];
-  }
+  std::stable_sort(Y.perm, Y.perm + n_groups, [&](int a, int b) { return wcost[a] > wcost[b]; });
+  GroupArg tmp[LBF_MAX_GROUPS];
+  for (int g = 0; g < n_groups; g++) tmp[g] = L.g[Y.perm[g]];
+  for (int g = 0; g < n_groups; g++) L.g[g] = tmp[g];
   uint64_t wg = 0;
   for (int g = 0; g < n_groups; g++) {
     const uint32_t rpw = L.g[g].aux >> kAuxRowsShift;
     L.wg_begin[g] = (uint32_t)wg;
     wg += L.g[g].rows ? (L.g[g].rows + rpw - 1) / rpw : 0;
   }
-  L.wg_begin[n_groups] = (uint32_t)wg;
-  if (wg == 0) return hipSuccess;
-  if (wg > 0x7FFFFFFFu) return hipErrorNotSupported;
+  L.wg_begin[n_groups] = (uint32_t)std::min<uint64_t>(wg, 0xFFFFFFFFu);
+  Y.wg = wg;
+}
+
+// Batch columns go in slabs of up to 64 (each slab reads the coded weights
+// again); a slab of m columns runs ceil(m / 16) MFMA column blocks, a slab
+// of one block with waves of two row blocks.
+hipError_t launch_gemm(const GroupArg* groups, int n_groups, int batch, int y_dtype, hipStream_t s) {
+  int cus = 0;
+  if (const hipError_t e = device_cus(&cus); e != hipSuccess) return e;
+  const uint32_t eb = y_dtype == LBF_BF16 ? 2u : 4u;
+  for (int g = 0; g < n_groups; g++)
+    if (groups[g].tiles > kGemmMaxTiles) return hipErrorNotSupported;
+  GemmLayout Y[2];  // [0]: four row blocks a wave, [1]: two
+  bool made[2] = {false, false};
   for (int b0 = 0; b0 < batch; b0 += kGemmBatch) {
     const int nb = std::min(kGemmBatch, batch - b0);
+    const int nblk = (nb + 15) / 16, which = nblk == 1 ? 1 : 0;
+    GemmLayout& y = Y[which];
+    if (!made[which]) {
+      gemm_layout(y, groups, n_groups, cus, which ? 2 : 4, y_dtype == LBF_BF16);
+      made[which] = true;
+    }
+    if (y.wg == 0) return hipSuccess;
+    if (y.wg > 0x7FFFFFFFu) return hipErrorNotSupported;
+    GemmLaunch& L = y.L;
     L.batch = nb;
     for (int g = 0; g < n_groups; g++) {
-      const GroupArg& o = groups[perm[g]];
+      const GroupArg& o = groups[y.perm[g]];
       L.g[g].x = o.x + (size_t)b0 * o.tiles * kTile;
       L.g[g].y = static_cast<uint8_t*>(o.y) + (size_t)b0 * o.rows * eb;
     }
     hipError_t e;
-    switch ((nb + 15) / 16) {
-      case 1: e = run_gemm<1, 2>(L, (uint32_t)wg, s); break;
-      case 2: e = run_gemm<2, 2>(L, (uint32_t)wg, s); break;
-      case 3: e = run_gemm<3, 2>(L, (uint32_t)wg, s); break;
-      default: e = run_gemm<4, 1>(L, (uint32_t)wg, s); break;
+    switch (nblk) {
+      case 1: e = run_gemm<1, 2, 2>(L, (uint32_t)y.wg, s); break;
+      case 2: e = run_gemm<2, 2, 4>(L, (uint32_t)y.wg, s); break;
+      case 3: e = run_gemm<3, 2, 4>(L, (uint32_t)y.wg, s); break;
+      default: e = run_gemm<4, 1, 4>(L, (uint32_t)y.wg, s); break;
     }
     if (e != hipSuccess) return e;
   }
