@@ -978,8 +978,10 @@ hipError_t launch_gemv_gated(const GroupArg& gate, const GroupArg& up, int batch
 // when all of them do; as few as possible otherwise: a team's time is set
 // by its workgroup count, and one workgroup more or less matters less the
 // more a team has).  Each team gets workgroups in proportion to its cost
-// (coded bytes, escapes counted twice: they are read and placed), at least
-// one and at most one a row; one workgroup per CU in all.
+// (coded bytes, each escape counted as four: it is read, staged, ranked and
+// placed; weights of 2 / 3 / 4 / 6 put the 64 escape-stress experts at
+// batch 4 at 131 / 126 / 126 / 131 us and at batch 1 at 114 / 111 / 110 /
+// 108 us), at least one and at most one a row; one workgroup per CU in all.
 static hipError_t launch_ring(const GroupArg* groups, int n_groups, int batch, int y_dtype, bool& used,
                               hipStream_t s) {
   used = false;
@@ -1018,7 +1020,7 @@ static hipError_t launch_ring(const GroupArg* groups, int n_groups, int batch, i
     if (rows + G.rows >= kRingMaxRows) return hipSuccess;
     L.gtab[g] = group_entry((uint32_t)rows, G.tiles);
     rows += G.rows;
-    team_work[n_teams - 1] += (uint64_t)G.rows * G.tiles * (kTile + kTile / 2) + 2ull * G.n_esc;
+    team_work[n_teams - 1] += (uint64_t)G.rows * G.tiles * (kTile + kTile / 2) + 4ull * G.n_esc;
     team_rows[n_teams - 1] += G.rows;
   }
   if (rows >= kRingMaxRows || rows == 0) return hipSuccess;
