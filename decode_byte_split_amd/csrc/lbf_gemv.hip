@@ -466,6 +466,7 @@ constexpr int kRingWaves = 16;  // waves per workgroup (4 per SIMD), every batch
 // the per-chunk scalar work grows faster than the extra loads in flight help.
 constexpr int kRingTiles = 4;
 constexpr int kRingSlots = 3;
+constexpr uint32_t kTailRows = 4;  // batch-1 tail: rows per wave rank a SIMD left to the earlier waves
 constexpr uint32_t kRingXMax = 131072;  // x area; with the wave slots 144 KiB of the 160 KiB LDS
 
 // Ring launch: the group records, rows dealt in record order (the launcher
@@ -703,10 +704,35 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
   // within the team); the wave's first two come from k = wave, wave + 16,
   // the rest from the LDS counter (starts at 32)
   uint32_t k_static = 0;
+  // Tail (batch 1, one team, plain products).  The four waves of a SIMD are
+  // served by the memory pipeline in the order they issue: the first wave
+  // of each SIMD gets its chunks back soonest and the fourth last (on the 8B
+  // layer they decode about 17 against 10 chunks a launch, and the fourth
+  // ends 2-3 us after the first).  So the waves after the first of their
+  // SIMD stop taking rows kTailRows rows per rank before this CU's last row
+  // (a soft limit: a row taken from the counter is always decoded), and the
+  // last rows go to the waves that return them soonest (8B layer 54.4 ->
+  // 53.9 us, gate_proj 18.9 -> 18.7 us).  Not with teams, whose last rows
+  // can be the costliest (escape-dense tensors; 64 experts at batch 1: 110
+  // -> 116 us), and not above batch 1, where the extra registers spill.
+  constexpr bool kTail = B == 1 && !TEAMS && !GATED;
+  uint32_t kcap = ~0u;
+  if constexpr (kTail) {
+    const uint32_t b = blockIdx.x, per = gridDim.x >> 3;
+    const uint32_t cu = (gridDim.x & 7u) ? b : (b & 7u) * per + (b >> 3);
+    const uint32_t n_k = row_hi > cu ? (row_hi - cu + gridDim.x - 1) / gridDim.x : 0u;  // rows k of this CU: k < n_k
+    kcap = n_k - min(n_k, kTailRows * (wave >> 2));
+  }
   auto next_row = [&]() -> Pos {
     uint32_t k;
     if (k_static < 2) {
       k = wave + W * k_static++;
+    } else if constexpr (kTail) {
+      uint32_t v = ~0u;
+      if (lane == 0 && __hip_atomic_load(lctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < kcap)
+        v = atomicAdd(lctr, 1u);
+      k = uniform(v);
+      if (k == ~0u) return row_pos<GATED, C>(L, GR, L.n_rows);  // past this wave's limit: it stops
     } else {
       uint32_t v = 0;
       if (lane == 0) v = atomicAdd(lctr, 1u);
