@@ -705,18 +705,19 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
   // within the team); the wave's first two come from k = wave, wave + 16,
   // the rest from the LDS counter (starts at 32)
   uint32_t k_static = 0;
-  // Tail (batch 1, one team, plain products).  The four waves of a SIMD are
-  // served by the memory pipeline in the order they issue: the first wave
-  // of each SIMD gets its chunks back soonest and the fourth last (on the 8B
-  // layer they decode about 17 against 10 chunks a launch, and the fourth
-  // ends 2-3 us after the first).  So the waves after the first of their
-  // SIMD stop taking rows kTailRows rows per rank before this CU's last row
-  // (a soft limit: a row taken from the counter is always decoded), and the
-  // last rows go to the waves that return them soonest (8B layer 54.4 ->
-  // 53.9 us, gate_proj 18.9 -> 18.7 us).  Not with teams, whose last rows
-  // can be the costliest (escape-dense tensors; 64 experts at batch 1: 110
-  // -> 116 us), and not above batch 1, where the extra registers spill.
-  constexpr bool kTail = B == 1 && !TEAMS && !GATED;
+  // Tail (batch 1, one team).  The four waves of a SIMD are served by the
+  // memory pipeline in the order they issue: the first wave of each SIMD
+  // gets its chunks back soonest and the fourth last (on the 8B layer they
+  // decode about 17 against 10 chunks a launch, and the fourth ends 2-3 us
+  // after the first).  So the waves after the first of their SIMD stop
+  // taking rows kTailRows rows per rank before this CU's last row (a soft
+  // limit: a row taken from the counter is always decoded), and the last
+  // rows go to the waves that return them soonest (8B layer 54.4 -> 53.9 us,
+  // gate_proj 18.9 -> 18.7 us, fused SwiGLU 32.5 -> 31.7 us).  Not with
+  // teams, whose last rows can be the costliest (escape-dense tensors; 64
+  // experts at batch 1: 110 -> 116 us), and not above batch 1, where the
+  // extra registers spill.
+  constexpr bool kTail = B == 1 && !TEAMS;
   uint32_t kcap = ~0u;
   if constexpr (kTail) {
     const uint32_t b = blockIdx.x, per = gridDim.x >> 3;
