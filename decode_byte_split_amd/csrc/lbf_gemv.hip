@@ -723,7 +723,9 @@ __global__ __launch_bounds__(W * kWave) void k_gemv_ring(RingLaunch L) {
     const uint32_t b = blockIdx.x, per = gridDim.x >> 3;
     const uint32_t cu = (gridDim.x & 7u) ? b : (b & 7u) * per + (b >> 3);
     const uint32_t n_k = row_hi > cu ? (row_hi - cu + gridDim.x - 1) / gridDim.x : 0u;  // rows k of this CU: k < n_k
-    kcap = n_k - min(n_k, kTailRows * (wave >> 2));
+    // the first wave of each SIMD takes rows until the counter runs out, so
+    // every row is taken whatever the limits of the others
+    kcap = (wave >> 2) == 0 ? ~0u : n_k - min(n_k, kTailRows * (wave >> 2));
   }
   auto next_row = [&]() -> Pos {
     uint32_t k;
