@@ -42,6 +42,16 @@ def tensors():
     flat[1023::1024] = 0x0001  # smallest denormal, exponent 0
     flat[4096:5120] = (np.arange(1024) % 65536).astype(np.uint16) | 0x7000
     g["edge_escapes_4x4096"] = W
+    # escapes of different exponents around each tile's half boundary (the
+    # decoder gives lane l the weights 8l..8l+7 of each half) and in the
+    # partial second half of the last tile (3000 weights: 952 in tile 2)
+    W = synth.gaussian(rng, 3, 1000, 0.02, 0.0, 1.0)
+    flat = W.reshape(-1)
+    for t0 in (0, 1024, 2048):
+        flat[t0 + np.array([7, 8, 504, 511, 512, 513, 519, 520, 900])] = [
+            0x7F80, 0x0001, 0xFF81, 0x0001, 0x7F80, 0x0002, 0xFF80, 0x0001, 0x7F80]
+    flat[-1] = 0x0003
+    g["half_edges_3x1000"] = W
     return g
 
 
@@ -82,19 +92,20 @@ def test_encode_decode_empty(env):
     assert lbf.decode(b).shape == (0, 1024)
 
 
-def test_decode_leaves_neighbours_untouched(env):
+@pytest.mark.parametrize("name", ["ragged_7x333", "half_edges_3x1000"])
+def test_decode_leaves_neighbours_untouched(env, name):
     torch, lbf = env
-    W = TENSORS["ragged_7x333"]
+    W = TENSORS[name]
     blob = lbf.from_host_blob(O.encode(W))
     n = W.size
     guard = 4096
     buf = torch.full((guard + n + guard,), -12345, dtype=torch.int16, device="cuda")
-    out = buf[guard:guard + n].view(torch.bfloat16).view(7, 333)
+    out = buf[guard:guard + n].view(torch.bfloat16).view(*W.shape)
     lbf.decode(blob, out=out)
     torch.cuda.synchronize()
     h = buf.cpu().numpy()
     assert (h[:guard] == -12345).all() and (h[guard + n:] == -12345).all()
-    assert np.array_equal(h[guard:guard + n].view(np.uint16).reshape(7, 333), W)
+    assert np.array_equal(h[guard:guard + n].view(np.uint16).reshape(W.shape), W)
 
 
 @pytest.mark.parametrize("batch", [1, 2, 3, 4, 5, 8])
